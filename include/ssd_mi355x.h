@@ -1,0 +1,198 @@
+/*
+ * ssd_mi355x.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * The library evaluates the selective state space model with one scalar decay
+ * per head (the Mamba-2 "state space duality" layer):
+ *
+ *     a_t        = exp(dt[b,t,h] * A[h])
+ *     h_t[p][n]  = a_t * h_{t-1}[p][n] + dt[b,t,h] * x[b,t,h,p] * B[b,t,g,n]
+ *     y[b,t,h,p] = sum_n C[b,t,g,n] * h_t[p][n] + D[h] * x[b,t,h,p]
+ *
+ * with g = h / (H / G) the B/C group of head h and h_{-1} the initial state.
+ *
+ * Sources (page title, section):
+ *  - discrete recurrence with zero-order-hold decay exp(Delta A) and input
+ *    scaled by Delta B: "State Space Model" (book.paithon.it), "Un sistema che
+ *    riassume il passato"; "State Space Models (SSM)" (ultralytics.com),
+ *    "Come funzionano gli SSM";
+ *  - scalar transition a_t I, equal to masked linear attention without
+ *    softmax: "State Space Model", "Due strade, una meta" and "Da ricordare";
+ *  - y = C h + D x: "Puntata 205 -- State Space Models e Mamba"
+ *    (aiperbabbani.it), "Cos'e' un SSM, in 30 secondi";
+ *  - per-token Delta, B, C (selectivity): same page, "Mamba (Gu & Dao,
+ *    dicembre 2023): selective scan";
+ *  - the block algorithm evaluated by ssd_forward -- quadratic masked form
+ *    inside each chunk, only the summary state carried between chunks --
+ *    "Mamba-2 (2024): SSM e attention sono la stessa cosa" (paithon.it),
+ *    "Il trucco a blocchi"; "Architektury Mamba-2, State Space Models i
+ *    liniowa atencja..." (tech.tersel.eu), "Rewolucja Mamba-2 i teoria State
+ *    Space Duality SSD";
+ *  - two ways to run one model: all tokens at once to train / prefill, one
+ *    token at a time with a fixed-size state to generate: "State Space
+ *    Model", "Un sistema che riassume il passato" (end of the water-tank
+ *    passage); tech.tersel.eu, "Porownanie zlozonosci obliczeniowej i
+ *    zachowania pamieci" (constant memory while generating).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major
+ *    array; the caller allocates and owns all memory, including the
+ *    workspace.  The library allocates nothing and keeps no pointer after a
+ *    call returns; it has no mutable global state, so calls are reentrant.
+ *  - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *    returns at once.  SSD_OK means every kernel was launched; results are
+ *    valid once the stream has completed.  No call synchronises.
+ *  - All arguments are checked before any launch.  An error is reported as a
+ *    status code; no exception crosses the ABI and nothing is written.
+ *  - Alignment: x, B, C, y, states and workspace must be 16-byte aligned;
+ *    dt, A and D 4-byte aligned (SSD_ERR_ALIGN otherwise).
+ *  - dtype (ssd_dtype) is the storage type of x, B, C and y.  dt, A, D and
+ *    every state are fp32.  Arithmetic is fp32 (bf16 operands of the matrix
+ *    instructions, fp32 accumulation and fp32 states).
+ *  - Preconditions that are documented, not checked on the device:
+ *    dt >= 0, A <= 0, finite inputs.  NaN/Inf propagate.
+ *  - Layouts (B = batch, L = seqlen, H = nheads, P = headdim, N = dstate,
+ *    G = ngroups, Q = chunk, nc = ceil(L / Q)):
+ *        x, y      [B][L][H][P]        dt        [B][L][H]
+ *        Bm, Cm    [B][L][G][N]        A, D      [H]
+ *        init, final, state            [B][H][P][N]
+ *  - H must be a multiple of G.  L may be any length >= 1; the last chunk may
+ *    be partial.
+ *  - Supported shapes (ssd_forward and the stage calls): either dtype with
+ *    1 <= P <= 128, 1 <= N <= 128, 1 <= Q <= 256; bf16 with P = 64, N = 128
+ *    and Q in {64, 128, 256} runs on the matrix cores, everything else on the
+ *    vector units.  Anything else returns SSD_ERR_UNSUPPORTED.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    SSD_ERR_SHAPE = 2,       /* a size is < 1, H % G != 0, or sizes overflow         */
+    SSD_ERR_UNSUPPORTED = 3, /* (dtype, P, N, chunk) not compiled in                 */
+    SSD_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required              */
+    SSD_ERR_ALIGN = 5,       /* a pointer is not aligned as stated above             */
+    SSD_ERR_HIP = 6,         /* a kernel launch failed (hipGetLastError)             */
+    SSD_ERR_ALIAS = 7        /* an output overlaps an input it must not overlap      */
+} ssd_status;
+
+/* Version of this ABI (SSD_ABI_VERSION). */
+int32_t ssd_abi_version(void);
+
+/* Static, NUL-terminated description of a status code.  Never NULL. */
+const char* ssd_status_str(int32_t status);
+
+/*
+ * Bytes of device workspace ssd_forward needs for these sizes, or 0 if the
+ * sizes are invalid or unsupported.  The workspace holds, each region
+ * 256-byte aligned and in this order:
+ *     cs   fp32 [B][H][nc][Q]  log2(e) * inclusive prefix of dt*A in the chunk
+ *     dtc  fp32 [B][H][nc][Q]  dt rearranged head-major (0 past the end)
+ *     S    fp32 [B][H][nc][P][N]  each chunk's end state, starting from zero
+ *     Hin  [B][H][nc][P][N]    state entering each chunk, in the storage type
+ *                              (bf16 for bf16, fp32 for fp32)
+ */
+size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int64_t ngroups,
+                                   int64_t chunk, int32_t dtype);
+
+/*
+ * Whole-sequence forward (training / prefill): y and the final state from x,
+ * dt, A, B, C, D and an optional initial state, by the block algorithm with
+ * chunk length `chunk` (see the block-algorithm sources above).  Runs, in
+ * order on `stream`: ssd_chunk_cumsum, ssd_chunk_state, ssd_state_passing,
+ * ssd_chunk_scan.
+ *   D           may be NULL: no skip term.
+ *   init_state  may be NULL: zero initial state.  When given it is decayed by
+ *               exp(dt_0 A) at the first token, like any carried state.
+ *   final_state may be NULL: not written.  It may alias init_state (the
+ *               state is read before it is overwritten).
+ *   y           must not overlap any input or the workspace (SSD_ERR_ALIAS).
+ *   workspace   at least ssd_forward_workspace_bytes(...) bytes.
+ */
+int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                    int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                    const void* x, const float* dt, const float* A, const void* B,
+                    const void* C, const float* D, const float* init_state, void* y,
+                    float* final_state, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * One decode step for every (batch, head) -- one token of generation with a
+ * fixed-size state ("State Space Model", "Un sistema che riassume il
+ * passato"; tech.tersel.eu, constant memory while generating):
+ *     a = exp(dt_t[b,h] A[h]);  state = a state + dt_t x_t (outer) B_t;
+ *     y_t = C_t . state + D x_t
+ *   state  fp32 [B][H][P][N], read and written in place.
+ *   x_t, y_t [B][H][P] (dtype)   dt_t fp32 [B][H]   B_t, C_t [B][G][N] (dtype)
+ *   A, D   fp32 [H]; D may be NULL.
+ * The signature adds A, D and y_t to (state, x_t, dt_t, B_t, C_t): the
+ * recurrence needs the decay and the skip term, and the step's output.
+ * Supported: any P <= 1024, N <= 1024 (fast path when N is a multiple of 4
+ * and N / 4 divides 64).
+ */
+int32_t ssm_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int64_t ngroups, int32_t dtype, float* state, const void* x_t,
+                 const float* dt_t, const float* A, const void* B_t, const void* C_t,
+                 const float* D, void* y_t, hipStream_t stream);
+
+/*
+ * The four stages of ssd_forward, callable one by one (per-stage checks and
+ * timing).  Arrays named after the workspace regions have the layouts given
+ * at ssd_forward_workspace_bytes.
+ */
+
+/* cs, dtc from dt and A: the per-chunk inclusive prefix of dt * A, scaled by
+ * log2(e), and dt rearranged head-major.  Past the end of the sequence cs
+ * repeats its last value and dtc is 0.  (Decay weights multiply along the
+ * sequence -- the fading weights 1, 1/2, 1/4 ... of the water-tank example,
+ * "State Space Model", "Un sistema che riassume il passato" -- so their
+ * logarithms add up.) */
+int32_t ssd_chunk_cumsum(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
+                         const float* dt, const float* A, float* cs, float* dtc,
+                         hipStream_t stream);
+
+/* S [B][H][nc][P][N]: each chunk's end state from a zero start,
+ * S_c[p][n] = sum_j exp(Acs_last - Acs_j) dt_j x_j[p] B_j[n]
+ * ("Il trucco a blocchi": only a summary state leaves a block). */
+int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                        const void* x, const void* B, const float* cs, const float* dtc,
+                        float* S, hipStream_t stream);
+
+/* Hin (storage type of `dtype`) and final_state from S: the linear recurrence
+ * between chunks, H_0 = init (or 0), Hin_c = H_c, H_{c+1} = exp(Acs_last) H_c
+ * + S_c, final = H_nc.  init_state / final_state may be NULL and may alias. */
+int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                          int64_t dstate, int64_t chunk, int32_t dtype, const float* S,
+                          const float* cs, const float* init_state, void* Hin,
+                          float* final_state, hipStream_t stream);
+
+/* y from the chunk's own tokens (masked C.B^T weighted by exp(Acs_i - Acs_j)
+ * dt_j, the attention-like quadratic form), the carried state
+ * (exp(Acs_i) Hin_c C_i) and D x. */
+int32_t ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                       const void* x, const void* B, const void* C, const float* cs,
+                       const float* dtc, const void* Hin, const float* D, void* y,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

@@ -1,0 +1,31 @@
+"""MI355X-native (gfx950) selective scan with a scalar decay per head.
+
+``ssd_forward`` runs the block algorithm over whole sequences and ``ssm_step``
+one decode step, both in hand-written HIP kernels behind the C ABI of
+``include/ssd_mi355x.h`` (``libssd_mi355x.so``).  This package only marshals
+torch tensors into that ABI.
+"""
+from .ssd import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    SSDError,
+    abi_version,
+    chunk_cumsum,
+    chunk_scan,
+    chunk_state,
+    library_path,
+    load,
+    n_chunks,
+    ssd_forward,
+    ssm_step,
+    state_passing,
+    status_str,
+    workspace_bytes,
+    workspace_regions,
+)
+
+__all__ = [
+    "ssd_forward", "ssm_step", "workspace_bytes", "workspace_regions", "chunk_cumsum",
+    "chunk_state", "state_passing", "chunk_scan", "load", "library_path", "abi_version",
+    "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16",
+]

@@ -1,0 +1,66 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Storage types.  bf16 is carried as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Two fp32 -> one word holding (lo, hi) bf16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+
+template <>
+struct Elem<bf16_t> {
+    __device__ __forceinline__ static float load(const bf16_t* p, int64_t i) {
+        return bf16_bits_to_f32(p[i].bits);
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, int64_t i, float v) {
+        p[i].bits = (uint16_t)f32_to_bf16_bits(v);
+    }
+};
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Map a linear workgroup id to a logical work item so that the 8 XCDs each
+// receive one contiguous range of the logical order (workgroups are handed to
+// XCDs round-robin).  Identity when the count is not a multiple of 8.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t wg, uint32_t count) {
+    if ((count & 7u) != 0u) return wg;
+    return (wg & 7u) * (count >> 3) + (wg >> 3);
+}
+
+}  // namespace ssd

@@ -1,0 +1,142 @@
+// state_passing.hip -- the linear recurrence between chunks.
+//
+// Only the summary state travels from one block to the next (page "Mamba-2
+// (2024): SSM e attention sono la stessa cosa", section "Il trucco a blocchi"),
+// and the update has the general linear form h_t = A_t h_{t-1} + b_t of page
+// "State Space Model", section "Due strade, una meta", here applied once per
+// chunk:  Hin_c = H_c,  H_{c+1} = exp(Acs_c[last]) H_c + S_c.
+//
+// Pure streaming: every state element is independent, one thread owns VW
+// consecutive elements of one (batch, head) and walks the chunks in order.
+// The loads of S for the next PF chunks do not depend on the carried state, so
+// they are kept in flight in a register ring while the chain advances.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace ssd {
+
+template <int VW>
+struct Vec {
+    float v[VW];
+};
+
+template <int VW>
+__device__ __forceinline__ Vec<VW> load_vec(const float* p, int64_t i) {
+    Vec<VW> r;
+    if constexpr (VW == 4) {
+        const float4 t = reinterpret_cast<const float4*>(p)[i];
+        r.v[0] = t.x; r.v[1] = t.y; r.v[2] = t.z; r.v[3] = t.w;
+    } else {
+        r.v[0] = p[i];
+    }
+    return r;
+}
+
+template <int VW>
+__device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r) {
+    if constexpr (VW == 4) {
+        reinterpret_cast<float4*>(p)[i] = make_float4(r.v[0], r.v[1], r.v[2], r.v[3]);
+    } else {
+        p[i] = r.v[0];
+    }
+}
+
+template <int VW>
+__device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r) {
+    if constexpr (VW == 4) {
+        uint2 w;
+        w.x = pack_bf16x2(r.v[0], r.v[1]);
+        w.y = pack_bf16x2(r.v[2], r.v[3]);
+        reinterpret_cast<uint2*>(p)[i] = w;
+    } else {
+        p[i].bits = (uint16_t)f32_to_bf16_bits(r.v[0]);
+    }
+}
+
+// Element indices below are in units of VW floats.
+template <typename HT, int PF, int VW>
+__global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ S,
+                                                            const float* __restrict__ cs,
+                                                            const float* init, HT* __restrict__ Hin,
+                                                            float* fin, int64_t total, int pnv,
+                                                            int nc, int Q) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int64_t bh = idx / pnv;
+    const int off = (int)(idx - bh * pnv);
+
+    Vec<VW> h;
+    if (init) {
+        h = load_vec<VW>(init, idx);
+    } else {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) h.v[e] = 0.0f;
+    }
+    const int64_t base = bh * nc * (int64_t)pnv + off;
+    const float* dec = cs + bh * nc * (int64_t)Q + (Q - 1);
+
+    Vec<VW> buf[PF];
+    float lg[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        if (k < nc) {
+            buf[k] = load_vec<VW>(S, base + (int64_t)k * pnv);
+            lg[k] = dec[(int64_t)k * Q];
+        }
+    }
+    for (int c0 = 0; c0 < nc; c0 += PF) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int c = c0 + k;
+            if (c < nc) {
+                const Vec<VW> s = buf[k];
+                const float a = fast_exp2(lg[k]);
+                if (c + PF < nc) {
+                    buf[k] = load_vec<VW>(S, base + (int64_t)(c + PF) * pnv);
+                    lg[k] = dec[(int64_t)(c + PF) * Q];
+                }
+                store_vec<VW>(Hin, base + (int64_t)c * pnv, h);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + s.v[e];
+            }
+        }
+    }
+    if (fin) store_vec<VW>(fin, idx, h);
+}
+
+template <typename HT, int VW>
+static void launch_sp_vw(const Dims& d, const float* S, const float* cs, const float* init,
+                         void* Hin, float* fin, hipStream_t stream) {
+    const int pnv = (int)(d.headdim * d.dstate / VW);
+    const int64_t total = d.batch * d.nheads * (int64_t)pnv;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    HT* hin = reinterpret_cast<HT*>(Hin);
+    if (d.nchunks >= 64) {
+        state_passing_kernel<HT, 16, VW><<<blocks, 256, 0, stream>>>(
+            S, cs, init, hin, fin, total, pnv, (int)d.nchunks, (int)d.chunk);
+    } else {
+        state_passing_kernel<HT, 8, VW><<<blocks, 256, 0, stream>>>(
+            S, cs, init, hin, fin, total, pnv, (int)d.nchunks, (int)d.chunk);
+    }
+}
+
+template <typename HT>
+static void launch_sp(const Dims& d, const float* S, const float* cs, const float* init,
+                      void* Hin, float* fin, hipStream_t stream) {
+    if ((d.headdim * d.dstate) % 4 == 0)
+        launch_sp_vw<HT, 4>(d, S, cs, init, Hin, fin, stream);
+    else
+        launch_sp_vw<HT, 1>(d, S, cs, init, Hin, fin, stream);
+}
+
+hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, const float* cs,
+                                const float* init, void* Hin, float* final_state,
+                                hipStream_t stream) {
+    if (dtype == 1)
+        launch_sp<bf16_t>(d, S, cs, init, Hin, final_state, stream);
+    else
+        launch_sp<float>(d, S, cs, init, Hin, final_state, stream);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,128 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before any HIP call (no GPU needed: no compute call is made)."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ssd_mi355x.h"
+
+OK, NULL, SHAPE, UNSUP, WS, ALIGN, HIP, ALIAS = range(8)
+
+
+def _declared():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+|ssm_step)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mamba_ssd_scan_02_amd as ssd
+    return ssd.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("ssd_forward", "ssm_step", "ssd_forward_workspace_bytes", "ssd_status_str",
+              "ssd_abi_version", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
+              "ssd_chunk_scan"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import mamba_ssd_scan_02_amd as ssd
+    out = subprocess.run(["nm", "-D", "--defined-only", str(ssd.library_path())],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssd_abi_version() == 1
+    for s in range(8):
+        assert lib.ssd_status_str(s)
+    assert lib.ssd_status_str(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    import mamba_ssd_scan_02_amd as ssd
+    n = lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 1, 256, 1)
+    regions = ssd.workspace_regions(4, 8192, 80, 64, 128, 256, __import__("torch").bfloat16)
+    assert n == regions["total"]
+    nc = 32
+    assert n >= 4 * 80 * nc * 256 * 4 * 2 + 4 * 80 * nc * 64 * 128 * (4 + 2)
+    assert lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 3, 256, 1) == 0   # H % G
+    assert lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 1, 512, 1) == 0   # chunk
+    assert lib.ssd_forward_workspace_bytes(1, 8, 1, 256, 16, 1, 8, 0) == 0         # P too big
+    assert lib.ssd_forward_workspace_bytes(1, 8, 1, 16, 16, 1, 8, 7) == 0          # dtype
+    assert lib.ssd_forward_workspace_bytes(0, 8, 1, 16, 16, 1, 8, 0) == 0
+
+
+def _fwd(lib, **over):
+    a = dict(batch=1, seqlen=64, nheads=2, headdim=16, dstate=16, ngroups=1, chunk=64, dtype=0,
+             x=0x1000, dt=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, init=None, y=0x100000,
+             final=None, ws=0x200000, wsb=1 << 30, stream=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    return lib.ssd_forward(a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["dstate"],
+                           a["ngroups"], a["chunk"], a["dtype"], P(a["x"]), P(a["dt"]), P(a["A"]),
+                           P(a["B"]), P(a["C"]), P(a["D"]), P(a["init"]), P(a["y"]), P(a["final"]),
+                           P(a["ws"]), a["wsb"], P(a["stream"]))
+
+
+def test_forward_argument_errors(lib):
+    assert _fwd(lib, batch=0) == SHAPE
+    assert _fwd(lib, seqlen=-1) == SHAPE
+    assert _fwd(lib, nheads=3, ngroups=2) == SHAPE
+    assert _fwd(lib, chunk=0) == SHAPE
+    assert _fwd(lib, chunk=300) == UNSUP
+    assert _fwd(lib, headdim=129) == UNSUP
+    assert _fwd(lib, dtype=5) == UNSUP
+    assert _fwd(lib, x=None) == NULL
+    assert _fwd(lib, y=None) == NULL
+    assert _fwd(lib, ws=None) == WS
+    assert _fwd(lib, wsb=16) == WS
+    assert _fwd(lib, x=0x1008) == ALIGN
+    assert _fwd(lib, dt=0x2002) == ALIGN
+    assert _fwd(lib, y=0x1000) == ALIAS            # y on top of x
+    assert _fwd(lib, ws=0x1000) == ALIAS           # workspace on top of x
+
+
+def test_step_argument_errors(lib):
+    P = ctypes.c_void_p
+
+    def step(**over):
+        a = dict(batch=1, nheads=2, headdim=16, dstate=16, ngroups=1, dtype=0, state=0x100000,
+                 x=0x1000, dt=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, y=0x6000)
+        a.update(over)
+        return lib.ssm_step(a["batch"], a["nheads"], a["headdim"], a["dstate"], a["ngroups"],
+                            a["dtype"], P(a["state"]), P(a["x"]), P(a["dt"]), P(a["A"]),
+                            P(a["B"]), P(a["C"]), P(a["D"]), P(a["y"]), None)
+
+    assert step(batch=0) == SHAPE
+    assert step(nheads=3, ngroups=2) == SHAPE
+    assert step(dstate=2048) == UNSUP
+    assert step(dtype=9) == UNSUP
+    assert step(state=None) == NULL
+    assert step(state=0x100004) == ALIGN
+    assert step(y=0x100000) == ALIAS
+
+
+def test_stage_argument_errors(lib):
+    P = ctypes.c_void_p
+    assert lib.ssd_chunk_cumsum(1, 64, 2, 0, P(0x1000), P(0x2000), P(0x3000), P(0x4000), None) == SHAPE
+    assert lib.ssd_chunk_cumsum(1, 64, 2, 512, P(0x1000), P(0x2000), P(0x3000), P(0x4000), None) == UNSUP
+    assert lib.ssd_chunk_cumsum(1, 64, 2, 64, None, P(0x2000), P(0x3000), P(0x4000), None) == NULL
+    assert lib.ssd_chunk_state(1, 64, 2, 64, 128, 1, 64, 1, P(0x1000), None, P(0x10), P(0x20),
+                               P(0x4000), None) == NULL
+    assert lib.ssd_state_passing(1, 64, 2, 64, 128, 64, 1, P(0x1000), P(0x2000), None, P(0x3008),
+                                 None, None) == ALIGN
+    assert lib.ssd_chunk_scan(1, 64, 2, 64, 128, 1, 64, 1, P(0x1000), P(0x2000), P(0x3000),
+                              P(0x10), P(0x20), P(0x8000), None, P(0x1000), None) == ALIAS

@@ -1,0 +1,213 @@
+"""End-to-end parity of ssd_forward (GPU, through the C ABI) with the fp64
+oracle, on the five workloads and on the edge cases the method has.
+
+Gate: max |gpu - oracle| / max |oracle| per output tensor, <= 1e-4 for fp32
+storage and <= 2e-2 for bf16 storage (fp32 accumulation and state).
+At full size the oracle runs on a sample of (batch, head) pairs over the
+whole sequence (first and last pair always included)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.helpers import (TOL, all_pairs, gpu_forward, oracle_forward, sample_pairs, say,
+                           select_state, select_y, to_gpu)
+from tests.metrics import max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, chunk, dtype, bh=None, t_range=None, label=""):
+    y, fin = gpu_forward(inp, chunk)
+    batch, L, H, P = inp["x"].shape
+    if bh is None:
+        bh = all_pairs(batch, H)
+    y_ref, f_ref = oracle_forward(inp, bh=bh, t_range=t_range)
+    e_y = max_rel_err(select_y(y, bh, t_range), y_ref)
+    e_f = max_rel_err(select_state(fin, bh), f_ref)
+    say(f"[forward] {label} chunk={chunk}: y {e_y:.3e} final {e_f:.3e}")
+    assert e_y <= TOL[dtype], e_y
+    assert e_f <= TOL[dtype], e_f
+    return y, fin
+
+
+def _spec_inputs(spec):
+    from mamba_ssd_scan_02_amd.workloads import make_forward_inputs
+    return make_forward_inputs(spec)
+
+
+# ----------------------------------------------------------------- workloads
+def test_tiny_f32():
+    from mamba_ssd_scan_02_amd.workloads import TINY_F32
+    _check(_spec_inputs(TINY_F32), TINY_F32.chunk, "f32", label=TINY_F32.name)
+
+
+def test_mamba2_130m_shape():
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M as s
+    inp = _spec_inputs(s)
+    _check(inp, s.chunk, s.dtype, bh=sample_pairs(s.batch, s.nheads, 24, seed=2), label=s.name)
+
+
+def test_mamba2_2p7b_shape():
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as s
+    inp = _spec_inputs(s)
+    _check(inp, s.chunk, s.dtype, bh=sample_pairs(s.batch, s.nheads, 12, seed=3), label=s.name)
+
+
+def test_long_context_1m():
+    from mamba_ssd_scan_02_amd.workloads import LONG_1M as s
+    inp = _spec_inputs(s)
+    say(f"[forward] {s.name}: inputs ready")
+    # heads 0 and 31 (groups 0 and 7) plus two in between, over all 1M tokens
+    _check(inp, s.chunk, s.dtype, bh=[(0, 0), (0, 5), (0, 18), (0, 31)], label=s.name)
+
+
+# ---------------------------------------------------------------- edge cases
+def test_water_tank_in_tiny_shape():
+    """Inflow 2 on channel 0 with half kept per step: 2, 3, 3.5, 3.75, 3.875,
+    3.9375 on channel 0 and 0 everywhere else (page "State Space Model",
+    section "Un sistema che riassume il passato")."""
+    import mamba_ssd_scan_02_amd as ssd
+    L, P, N = 6, 16, 16
+    x = torch.zeros(1, L, 1, P)
+    x[..., 0] = 2.0
+    dt = torch.ones(1, L, 1)
+    A = torch.tensor([-math.log(2.0)])
+    B = torch.zeros(1, L, 1, N)
+    B[..., 0] = 1.0
+    y, fin = ssd.ssd_forward(x.cuda(), dt.cuda(), A.cuda(), B.cuda(), B.clone().cuda(), None, 64)
+    y = y.cpu()
+    np.testing.assert_allclose(y[0, :, 0, 0].numpy(), [2, 3, 3.5, 3.75, 3.875, 3.9375], atol=2e-6)
+    assert torch.all(y[0, :, 0, 1:] == 0)
+    # resume: half of 3.875 plus two new litres
+    init = torch.zeros(1, 1, P, N)
+    init[0, 0, 0, 0] = 3.875
+    y2, _ = ssd.ssd_forward(x[:, :1].cuda(), dt[:, :1].cuda(), A.cuda(), B[:, :1].cuda(),
+                            B[:, :1].clone().cuda(), None, 64, init.cuda())
+    assert abs(float(y2[0, 0, 0, 0]) - 3.9375) < 2e-6
+
+
+def test_long_memory_bf16():
+    """Tiny |A|: chunks barely decay, so every carried state matters."""
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=2048, nheads=8, init_var=0.1))
+    r = np.random.default_rng(5)
+    inp["A"] = torch.from_numpy((-1e-4 * np.exp(r.uniform(0, 1, 8))).astype(np.float32))
+    _check(inp, 256, "bf16", label="long_memory")
+
+
+def test_long_memory_f32():
+    from mamba_ssd_scan_02_amd.workloads import TINY_F32
+    inp = _spec_inputs(TINY_F32.with_(batch=2, seqlen=1000, nheads=3, init_var=0.5))
+    inp["A"] = torch.tensor([-1e-3, -1e-4, -1e-2], dtype=torch.float32)
+    _check(inp, 64, "f32", label="long_memory_f32")
+
+
+@pytest.mark.parametrize("L", [1, 63, 255, 257, 1000])
+def test_ragged_lengths_bf16(L):
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=L, nheads=4, init_var=0.1, seed=77))
+    _check(inp, 256, "bf16", label=f"ragged L={L}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_chunk_sweep_bf16(chunk):
+    """Same inputs, three chunk sizes: all match the oracle."""
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=1024, nheads=4, init_var=0.1, seed=78))
+    _check(inp, chunk, "bf16", label="chunk sweep")
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 200, 256])
+def test_chunk_sweep_f32(chunk):
+    from mamba_ssd_scan_02_amd.workloads import TINY_F32
+    inp = _spec_inputs(TINY_F32.with_(batch=2, seqlen=300, nheads=2, init_var=0.3, seed=79))
+    _check(inp, chunk, "f32", label="chunk sweep f32")
+
+
+def test_groups_and_permutation():
+    """G = 8 groups of 4 heads; permuting groups together with their heads
+    permutes the outputs exactly."""
+    from mamba_ssd_scan_02_amd.workloads import LONG_1M
+    inp = _spec_inputs(LONG_1M.with_(seqlen=1024, init_var=0.1, seed=80))
+    y, fin = _check(inp, 256, "bf16", label="groups G=8")
+    gperm = np.array([3, 0, 7, 1, 6, 2, 5, 4])
+    hperm = np.concatenate([np.arange(4 * g, 4 * g + 4) for g in gperm])
+    p = dict(inp)
+    p["B"], p["C"] = inp["B"][:, :, gperm].contiguous(), inp["C"][:, :, gperm].contiguous()
+    p["x"], p["dt"] = inp["x"][:, :, hperm].contiguous(), inp["dt"][:, :, hperm].contiguous()
+    p["A"], p["D"] = inp["A"][hperm].contiguous(), inp["D"][hperm].contiguous()
+    p["init"] = inp["init"][:, hperm].contiguous()
+    y2, fin2 = gpu_forward(p, 256)
+    assert torch.equal(y2.cpu(), y.cpu()[:, :, hperm])
+    assert torch.equal(fin2.cpu(), fin.cpu()[:, hperm])
+
+
+def test_split_sequence_handoff():
+    """forward(x[:m]) then forward(x[m:], init=final) equals forward(x): the
+    single-device form of carrying boundary states between sequence shards."""
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=1536, nheads=4, init_var=0.1, seed=81))
+    m = 512 + 100
+    first = {k: (v[:, :m].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    second = {k: (v[:, m:].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    y1, f1 = gpu_forward(first, 256)
+    second["init"] = f1.cpu()
+    y2, f2 = gpu_forward(second, 256)
+    y_ref, f_ref = oracle_forward(inp)
+    bh = all_pairs(2, 4)
+    y_cat = torch.cat([y1.cpu(), y2.cpu()], dim=1)
+    e_y = max_rel_err(select_y(y_cat, bh), y_ref)
+    e_f = max_rel_err(select_state(f2, bh), f_ref)
+    say(f"[forward] handoff y {e_y:.3e} final {e_f:.3e}")
+    assert e_y <= TOL["bf16"] and e_f <= TOL["bf16"]
+
+
+def test_zero_step_keeps_state():
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=1, seqlen=300, nheads=2, init_var=0.1, seed=82))
+    inp["dt"] = torch.zeros_like(inp["dt"])
+    y, fin = _check(inp, 256, "bf16", label="dt=0")
+    assert torch.equal(fin.cpu(), inp["init"])
+
+
+def test_huge_step_is_memoryless():
+    from mamba_ssd_scan_02_amd.workloads import TINY_F32
+    inp = _spec_inputs(TINY_F32.with_(batch=1, seqlen=128, nheads=2, init_var=0.3, seed=83))
+    inp["dt"] = torch.full_like(inp["dt"], 50.0)
+    _check(inp, 64, "f32", label="dt=50")
+
+
+def test_no_skip_no_init_no_final():
+    """D = None, init = None, final_state not requested."""
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=1, seqlen=512, nheads=2, seed=84))
+    g = to_gpu(inp)
+    y, fin = ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], None, 256, None,
+                             return_final_state=False)
+    assert fin is None
+    ref = dict(inp, D=None, init=None)
+    y_ref, _ = oracle_forward(ref)
+    assert max_rel_err(select_y(y, all_pairs(1, 2)), y_ref) <= TOL["bf16"]
+
+
+def test_final_state_may_alias_init():
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=1, seqlen=512, nheads=2, init_var=0.1, seed=85))
+    g = to_gpu(inp)
+    y_a, f_a = ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 256, g["init"])
+    st = g["init"].clone()
+    y_b, f_b = ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 256, st,
+                               final_state=st)
+    assert torch.equal(y_a, y_b) and torch.equal(f_a, st)
+
+
+def test_bitwise_deterministic():
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
+    inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=1024, nheads=8, init_var=0.1, seed=86))
+    y1, f1 = gpu_forward(inp, 256)
+    y2, f2 = gpu_forward(inp, 256)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)

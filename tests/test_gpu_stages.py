@@ -1,0 +1,96 @@
+"""Each GPU stage against the fp64 stage definitions of oracle/stages.py,
+feeding every stage the GPU's own upstream intermediates so that a mismatch
+names one kernel.  Shapes span several chunks and a ragged last chunk."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.helpers import TOL, say, to_gpu
+from tests.metrics import max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def _inputs(seed, batch, L, H, P, N, G, dtype, init=True):
+    from mamba_ssd_scan_02_amd.workloads import ForwardSpec, make_forward_inputs
+    spec = ForwardSpec("stage", batch, L, H, P, N, G, 64, dtype, init_var=0.1 if init else 0.0,
+                       seed=seed)
+    return make_forward_inputs(spec)
+
+
+CASES = [
+    # (name, batch, L, H, P, N, G, chunk, dtype)
+    ("mfma_q256_ragged", 2, 700, 4, 64, 128, 2, 256, "bf16"),
+    ("mfma_q128", 1, 512, 2, 64, 128, 1, 128, "bf16"),
+    ("mfma_q64_ragged", 1, 333, 2, 64, 128, 2, 64, "bf16"),
+    ("generic_f32", 2, 300, 3, 16, 16, 1, 64, "f32"),
+    ("generic_f32_odd", 1, 77, 2, 3, 5, 1, 16, "f32"),
+    ("generic_bf16", 1, 260, 2, 32, 64, 2, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_stages(case):
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    name, batch, L, H, P, N, G, Q, dtype = case
+    say(f"[stages] {name}")
+    inp = _inputs(11, batch, L, H, P, N, G, dtype)
+    g = to_gpu(inp)
+    tol = TOL[dtype]
+
+    # cumsum
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    err_cs = np.max(np.abs(cs.cpu().double().numpy() - Acs * LOG2E)) / max(1.0, np.abs(Acs * LOG2E).max())
+    assert err_cs < 2e-6, err_cs
+    nc = Acs.shape[2]
+    dt_ref = np.zeros((batch, nc * Q, H), np.float32)
+    dt_ref[:, :L] = inp["dt"].numpy()
+    assert np.array_equal(dtc.cpu().numpy(), dt_ref.reshape(batch, nc, Q, H).transpose(0, 3, 1, 2))
+
+    # chunk state, from the GPU's cs/dtc
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
+    S_ref = stages.chunk_state(inp["x"], inp["dt"], inp["B"], Acs, Q)
+    e = max_rel_err(S, S_ref)
+    say(f"  chunk_state max rel err {e:.3e}")
+    assert e < (tol if dtype == "bf16" else 1e-5)
+
+    # state passing, from the GPU's S
+    sd = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Hin, fin = ssd.state_passing(S, cs, L, Q, sd, g["init"])
+    S_gpu = S.cpu().double().numpy()
+    Hin_ref, fin_ref = stages.state_passing(S_gpu, Acs, inp["init"])
+    e_h = max_rel_err(Hin, Hin_ref)
+    e_f = max_rel_err(fin, fin_ref)
+    say(f"  state_passing Hin {e_h:.3e} final {e_f:.3e}")
+    assert e_h < (8e-3 if dtype == "bf16" else 1e-6)
+    assert e_f < 1e-5
+
+    # chunk scan, from the GPU's cs/dtc/Hin
+    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], Q)
+    y_ref = stages.chunk_scan(inp["x"], inp["dt"], inp["B"], inp["C"], Acs,
+                              Hin.cpu().double().numpy(), inp["D"], Q)
+    e_y = max_rel_err(y, y_ref)
+    say(f"  chunk_scan max rel err {e_y:.3e}")
+    assert e_y < tol
+
+
+def test_stage_intermediates_deterministic():
+    import mamba_ssd_scan_02_amd as ssd
+    inp = _inputs(12, 1, 512, 4, 64, 128, 1, "bf16")
+    g = to_gpu(inp)
+    outs = []
+    for _ in range(2):
+        cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], 256)
+        S = ssd.chunk_state(g["x"], g["B"], cs, dtc, 256)
+        Hin, fin = ssd.state_passing(S, cs, 512, 256, torch.bfloat16, g["init"])
+        y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], 256)
+        outs.append([t.clone() for t in (cs, S, Hin, fin, y)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
