@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Throughput of the SSD forward scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+A step is one ssd_forward call (chunk cumsum, chunk state, state passing and
+chunk scan) over the Mamba-2-2.7B-shaped workload: batch 4, seqlen 8192, 80
+heads, P = 64, N = 128, one B/C group, chunk 256, bf16 x/B/C, fp32 dt/A/D and
+state, random initial state.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (its
+algorithmic bytes per launch over its average launch time, measured here with
+HIP events on the stream it runs on), per-kernel figures, the decode step
+(batch 256, 64 steps) and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = "SSD fwd tokens/s at B=4,L=8K,H=80,P=64,N=128 bf16; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+KERNEL_SOURCES = {
+    "chunk_cumsum": "chunk_cumsum.hip",
+    "chunk_state": "chunk_state.hip",
+    "state_passing": "state_passing.hip",
+    "chunk_scan": "chunk_scan.hip",
+    "ssm_step": "ssm_step.hip",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------- byte models
+def forward_model(b, L, H, P, N, G, Q):
+    """Algorithmic HBM bytes and flops of each kernel of the four-kernel
+    pipeline: every input read once, every output written once (workspace
+    intermediates included, Hin in bf16)."""
+    nc = -(-L // Q)
+    tok = b * L
+    x = tok * H * P * 2
+    bc = tok * G * N * 2
+    dt = tok * H * 4
+    rows = b * H * nc * Q * 4               # one of cs / dtc
+    st = b * H * P * N * 4                  # init or final
+    S = b * H * nc * P * N * 4
+    Hin = b * H * nc * P * N * 2
+    bytes_ = {
+        "chunk_cumsum": dt + 2 * rows,
+        "chunk_state": x + bc + 2 * rows + S,
+        "state_passing": S + b * H * nc * 4 + st + Hin + st,
+        "chunk_scan": x + 2 * bc + 2 * rows + Hin + x,
+    }
+    th = tok * H
+    flops = {
+        "chunk_cumsum": 2 * th,
+        "chunk_state": 2 * P * N * th,                               # sum_j w_j x_j B_j^T
+        "state_passing": 2 * b * H * nc * P * N,
+        "chunk_scan": ((Q + 1) * P + 2 * N * P) * th + (Q + 1) * N * tok * G,  # causal-exact
+    }
+    return bytes_, flops
+
+
+def compulsory_bytes(b, L, H, P, N, G):
+    tok = b * L
+    return tok * H * P * 2 * 2 + tok * G * N * 2 * 2 + tok * H * 4 + 2 * b * H * P * N * 4
+
+
+def source_hash(kernel: str) -> str:
+    p = ROOT / "mamba_ssd_scan_02_amd" / "csrc" / KERNEL_SOURCES[kernel]
+    h = hashlib.sha256(p.read_bytes())
+    h.update((ROOT / "mamba_ssd_scan_02_amd" / "csrc" / "device_common.h").read_bytes())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per dispatch from the committed rocprofv3 counter summary for
+    this kernel and workload, or None if there is none or the kernel source
+    changed since the counters were taken."""
+    path = ROOT / "profiles" / f"{kernel}_{workload}_counters.txt"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    m_hash = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel):
+        return None
+    return float(m_bytes.group(1))
+
+
+# -------------------------------------------------------------------- timing
+def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk, g["init"], y=y,
+                        final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk, g["init"], y=y,
+                        final_state=fin, workspace=ws)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def time_stages(ssd, g, y, fin, ws, dims, steps):
+    """Average duration of each kernel, from HIP events recorded on the
+    stream the stage calls are launched on (torch's current stream)."""
+    import ctypes
+    import torch
+    lib = ssd.load()
+    b, L, H, P, N, G, Q = dims
+    reg = ssd.workspace_regions(b, L, H, P, N, Q, torch.bfloat16)
+    base = ws.data_ptr()
+    cs, dtc, S, Hin = (ctypes.c_void_p(base + reg[k][0]) for k in ("cs", "dtc", "S", "Hin"))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+    calls = [
+        lambda: lib.ssd_chunk_cumsum(b, L, H, Q, p(g["dt"]), p(g["A"]), cs, dtc, stream),
+        lambda: lib.ssd_chunk_state(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), cs, dtc, S, stream),
+        lambda: lib.ssd_state_passing(b, L, H, P, N, Q, 1, S, cs, p(g["init"]), Hin, p(fin), stream),
+        lambda: lib.ssd_chunk_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["C"]), cs, dtc,
+                                   Hin, p(g["D"]), p(y), stream),
+    ]
+    for f in calls:            # warm
+        assert f() == 0
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record()
+        for i, f in enumerate(calls):
+            if f() != 0:
+                raise RuntimeError(f"{names[i]} failed")
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    return {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps * 1e3
+            for i, n in enumerate(names)}   # microseconds
+
+
+def bench_decode(ssd, steps_warm=3):
+    import torch
+    from mamba_ssd_scan_02_amd.workloads import DECODE_B256 as spec
+    from mamba_ssd_scan_02_amd.workloads import make_decode_static, make_decode_step
+    st = make_decode_static(spec)
+    state = st["state"].cuda()
+    A, D = st["A"].cuda(), st["D"].cuda()
+    ins = [{k: v.cuda() for k, v in make_decode_step(spec, t).items()} for t in range(spec.steps)]
+    ys = [torch.empty_like(i["x"]) for i in ins]
+    for t in range(steps_warm):
+        ssd.ssm_step(state, ins[t]["x"], ins[t]["dt"], A, ins[t]["B"], ins[t]["C"], D, y_t=ys[t])
+    torch.cuda.synchronize()
+    state.copy_(st["state"].cuda())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(spec.steps):
+        ssd.ssm_step(state, ins[t]["x"], ins[t]["dt"], A, ins[t]["B"], ins[t]["C"], D, y_t=ys[t])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / spec.steps
+    b, H, P, N, G = spec.batch, spec.nheads, spec.headdim, spec.dstate, spec.ngroups
+    byts = b * H * P * N * 4 * 2 + b * H * P * 2 * 2 + b * H * 4 + 2 * b * G * N * 2 + 2 * H * 4
+    gbs = byts / (us * 1e-6) / 1e9
+    return {
+        "workload": spec.name, "tokens_per_s": b / (us * 1e-6), "us_per_step": us,
+        "bytes_per_step": byts, "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+        "traffic": counter_traffic("ssm_step", spec.name),
+    }
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the same workload: whole
+    sequences of (batch, head) pairs, in batches of one pair per core, until
+    the time budget is spent."""
+    import oracle
+    b, L, H = inp["x"].shape[0], inp["x"].shape[1], inp["x"].shape[2]
+    cores = oracle.threads()
+    pairs = [(i, h) for i in range(b) for h in range(H)]
+    done, t_total = 0, 0.0
+    while done < len(pairs) and t_total < budget_s:
+        chunk = pairs[done:done + cores]
+        t0 = time.perf_counter()
+        oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"],
+                       bh=chunk)
+        t_total += time.perf_counter() - t0
+        done += len(chunk)
+    tokens_equiv = done * L / H
+    return {"value": tokens_equiv / t_total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (batch, head) pairs x {L} tokens of the same "
+                      f"workload (= {tokens_equiv:.0f} full-width tokens) in {t_total:.1f} s"}
+
+
+# ---------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as spec
+    from mamba_ssd_scan_02_amd.workloads import make_forward_inputs
+
+    ssd.load()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dims = (spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups,
+            spec.chunk)
+    b, L, H, P, N, G, Q = dims
+    log(f"[bench] generating {spec.name}")
+    inp = make_forward_inputs(spec)
+    g = {k: v.cuda() for k, v in inp.items()}
+    y = torch.empty_like(g["x"])
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ssd.workspace_bytes(b, L, H, P, N, G, Q, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    log(f"[bench] forward: {args.warmup} warmup + {args.steps} timed steps")
+    ms, wall = time_forward(ssd, g, y, fin, ws, Q, args.steps, args.warmup)
+    tokens_per_s = b * L / (ms * 1e-3)
+    log(f"[bench] forward {ms * 1e3:.1f} us/step, {tokens_per_s:.4g} tokens/s")
+
+    log("[bench] per-kernel event timing")
+    k_us = time_stages(ssd, g, y, fin, ws, dims, max(args.steps, 10))
+    kbytes, kflops = forward_model(*dims)
+    kernels = {}
+    for n, us in k_us.items():
+        gbs = kbytes[n] / (us * 1e-6) / 1e9
+        tf = kflops[n] / (us * 1e-6) / 1e12
+        kernels[n] = {"us": round(us, 2), "alg_bytes": kbytes[n], "GBps": round(gbs, 1),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "alg_flops": kflops[n],
+                      "TFLOPs": round(tf, 2), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    dom = max(k_us, key=k_us.get)
+    d_us = k_us[dom]
+    achieved = kbytes[dom] / (d_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(dom, spec.name), "kernel": dom,
+                "alg_bytes_per_launch": kbytes[dom], "avg_launch_us": round(d_us, 2)}
+    comp = compulsory_bytes(b, L, H, P, N, G)
+    flops_total = sum(kflops.values())
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; x,dt,B,C,D,A,init drawn from the workload's distributions)",
+        "config": {"workload": spec.name, "batch": b, "seqlen": L, "nheads": H, "headdim": P,
+                   "dstate": N, "ngroups": G, "chunk": Q},
+        "roofline": roofline,
+        "path": {"hbm_frac_of_compulsory_bytes": round(comp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac_algorithmic_flops": round(flops_total / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "compulsory_bytes": comp, "four_kernel_bytes": sum(kbytes.values()),
+                 "algorithmic_flops": flops_total, "wall_s_timed_region": round(wall, 4)},
+        "kernels": kernels,
+    }
+    if not args.no_decode:
+        log("[bench] decode")
+        out["decode"] = bench_decode(ssd)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,8 +24,10 @@
 //     permutation that makes accumulator register r of lane half hf hold token
 //     16*(r/8) + 8*hf + r%8, i.e. the 8 K-slots of each following product
 //     are 8 consecutive tokens.
-//   * G~ = G * exp2(cs_i - cs_j) * dt_j for j <= i, 0 above the diagonal, + D
-//     on the diagonal (term iii), rounded to bf16.
+//   * G~ = G * exp2(cs_i - cs_j) * dt_j below the diagonal (factorised as
+//     exp2(cs_i - c0) * [exp2(c0 - cs_j) dt_j] with c0 the block's first
+//     token, the bracket precomputed once per token), masked on the diagonal
+//     block with D added on its diagonal (term iii); rounded to bf16.
 //   * Y^T += X^T G~^T (M = P rows in two 32-row tiles, K = 32 tokens).  A-row m
 //     reads channel sigma(m) so that a lane ends with 16 consecutive channels
 //     of its token: two 16-byte stores per tile.
@@ -33,34 +35,17 @@
 //     exp2(cs_i).
 // Wave w owns i tiles {w, 2W-1-w} so that every wave has the same number of
 // causal (j <= i) tiles.  C fragments of the wave's own tokens stay in
-// registers for the whole kernel; the j blocks of B (32 rows) and X^T (64 x 32)
-// stream through a 12 KB LDS window.
+// registers for the whole kernel; the carried state and the j blocks of B
+// (32 rows) and x (32 rows) are copied straight into LDS (lds_pipe.h) through
+// a 3-buffer ring, two blocks ahead, and x is read back transposed with tr16.
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
 #include "device_common.h"
 #include "launchers.h"
+#include "lds_pipe.h"
 
 namespace ssd {
-
-__device__ __forceinline__ void transpose8x8_bf16_scan(const uint4 (&in)[8], uint4 (&out)[8]) {
-    uint32_t w[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        w[i][0] = in[i].x; w[i][1] = in[i].y; w[i][2] = in[i].z; w[i][3] = in[i].w;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int m = q >> 1;
-        uint32_t o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = w[2 * k][m], hi = w[2 * k + 1][m];
-            o[k] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        out[q] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
 
 // Row m = 8a + 4hf + b of a 32-row MFMA tile.
 __device__ __forceinline__ int perm_pi(int m) {
@@ -72,54 +57,71 @@ __device__ __forceinline__ int perm_sigma(int m) {
     return 16 * hf + 4 * a + b;
 }
 
-template <int Q>
-__global__ __launch_bounds__(Q) void chunk_scan_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
-    const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
-    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc) {
-    constexpr int P = 64, N = 128, W = Q / 64, NT = Q / 32;
-    __shared__ float cs_s[Q];
-    __shared__ float dt_s[Q];
-    __shared__ uint4 win[1024];          // 16 KB: Hin [64][16] or B block [32][16] + X^T [64][4]
-    uint4* hs = win;
-    uint4* bsm = win;
-    uint4* xsm = win + 512;
+// ---------------------------------------------------------------------------
+// Pieces shared by the two matrix-core kernels.  A workgroup has 4 waves (or
+// Q/64 for short chunks); wave w owns i tiles it_[0] = w and it_[1] = 2W-1-w.
 
-    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int h = (int)(wg % (uint32_t)H);
-    const int bc = (int)(wg / (uint32_t)H);
-    const int c = bc % nc, b = bc / nc;
-    const int g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hf = lane >> 5, l32 = lane & 31;
-    const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-    const int tok0 = c * Q;
-    const float Dh = D ? D[h] : 0.0f;
+// Per-lane tr16 addressing of the X^T operand (see lds_pipe.h): lane r of
+// 16-lane group grp supplies token row 8*(grp/2) + r/4 and channel quad qb,
+// so lane i receives channel 32*mt + sigma(16*(grp%2) + i).
+struct XtAddr {
+    int qb, trow0;
+};
+__device__ __forceinline__ XtAddr xt_addr(int lane) {
+    const int grp = lane >> 4, rr = lane & 15;
+    XtAddr a;
+    a.qb = ((rr & 1) ? 16 : 0) + ((rr & 2) ? 4 : 0) + ((grp & 1) ? 8 : 0);
+    a.trow0 = 8 * (grp >> 1) + (rr >> 2);
+    return a;
+}
 
-    for (int e = tid; e < Q; e += Q) {
-        cs_s[e] = cs[row + e];
-        dt_s[e] = dtc[row + e];
-    }
-    const uint4* hsrc = reinterpret_cast<const uint4*>(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N));
-    for (int e = tid; e < 1024; e += Q) {
-        const int r = e >> 4, ch = e & 15;
-        hs[r * 16 + (ch ^ (r & 7))] = hsrc[e];
-    }
+// Largest decay inside one 32-token block (log2 units) for which the
+// factorised weights are used; beyond it the row factor exp2(c0 - cs_j)
+// could overflow, and the direct form is taken.
+constexpr float kMaxBlockDecayLog2 = 64.0f;
 
-    const int it_[2] = {wave, 2 * W - 1 - wave};
-    uint4 cf[2][8];
+__device__ __forceinline__ float uniform_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// Causal keep bits of the diagonal block for this lane.  Accumulator
+// register r of lane (l32, hf) holds token j = 16*(r/8) + 8*hf + r%8 of the
+// block and column i = l32: with t = l32 - 8*hf, registers r < 8 are kept
+// iff r <= t and registers r >= 8 iff r - 8 <= t - 16.
+__device__ __forceinline__ uint32_t diag_keep_bits(int l32, int hf) {
+    const int t = l32 - 8 * hf;
+    const int n0 = min(max(t + 1, 0), 8), n1 = min(max(t - 15, 0), 8);
+    return ((1u << n0) - 1u) | (((1u << n1) - 1u) << 8);
+}
+
+// Bit r set iff accumulator register r of this lane is the diagonal entry
+// j == i of the diagonal block (at most one per lane).
+__device__ __forceinline__ uint32_t diag_eq_bits(int l32, int hf) {
+    const int t = l32 - 8 * hf;
+    if (t >= 0 && t < 8) return 1u << t;
+    if (t >= 16 && t < 24) return 1u << (t - 8);
+    return 0u;
+}
+
+// C fragments of the wave's own tokens (B operand of both C products).
+__device__ __forceinline__ void load_c_frags(uint4 (&cf)[2][8], const bf16_t* Cm, int64_t b, int L,
+                                             int G, int g, int tok0, const int (&it_)[2], int hf,
+                                             int l32) {
+    constexpr int N = 128;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int tok = tok0 + 32 * it_[t] + l32;
-        const bf16_t* crow = Cm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
+        const bf16_t* crow = Cm + ((b * L + tok) * G + g) * N + 8 * hf;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
             cf[t][kk] = (tok < L) ? *reinterpret_cast<const uint4*>(crow + 16 * kk) : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+}
 
-    // (ii) carried state: Y^T[p][i] = sum_n Hin[p][n] C[i][n], scaled by exp2(cs_i)
-    f32x16 acc[2][2];
+// (ii) carried state: acc[t][mt] = exp2(cs_i) * sum_n Hin[p][n] C[i][n].
+__device__ __forceinline__ void scan_state_term(f32x16 (&acc)[2][2], const uint4* hs,
+                                                const uint4 (&cf)[2][8], const float (&csi)[2],
+                                                int hf, int l32) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -130,113 +132,114 @@ __global__ __launch_bounds__(Q) void chunk_scan_mfma_kernel(
         for (int mt = 0; mt < 2; ++mt) {
             const int pr = 32 * mt + perm_sigma(l32);
             const int ch = 2 * kk + hf;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, hs[pr * 16 + (ch ^ (pr & 7))]);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, hs[pr * 16 + (ch ^ swz_h(pr))]);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 acc[t][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, cf[t][kk]), acc[t][mt], 0, 0, 0);
         }
     }
-    float csi[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        csi[t] = cs_s[32 * it_[t] + l32];
         const float s = fast_exp2(csi[t]);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[t][mt][r] *= s;
     }
+}
 
-    // (i) + (iii): stream the j blocks
-    for (int jt = 0; jt < NT; ++jt) {
-        __syncthreads();
-        for (int e = tid; e < 512; e += Q) {
-            const int r = e >> 4, ch = e & 15;
-            const int tok = tok0 + 32 * jt + r;
-            bsm[r * 16 + (ch ^ (r & 7))] =
-                (tok < L) ? *reinterpret_cast<const uint4*>(Bm + (((int64_t)b * L + tok) * G + g) * N + 8 * ch)
-                          : make_uint4(0, 0, 0, 0);
+// (i) + (iii) for j block jt: G^T tiles from the B block, masked decay
+// weights (+ D on the diagonal), then Y^T += X^T G~^T.
+__device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const uint4* bst,
+                                           const uint4* xst, const float* cs_s, const float* dt_s,
+                                           const float* rf_s, const uint4 (&cf)[2][8],
+                                           const float (&csi)[2], const int (&it_)[2], float Dh,
+                                           XtAddr xa, int hf, int l32, uint32_t diag_keep,
+                                           uint32_t diag_eq) {
+    if (it_[1] < jt) return;   // it_[1] >= it_[0]: nothing left for this wave
+    const bool act0 = it_[0] >= jt;
+    f32x16 gacc[2] = {f32x16{}, f32x16{}};
+    {
+        const int jr = perm_pi(l32);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int ch = 2 * kk + hf;
+            const bf16x8 bq = __builtin_bit_cast(bf16x8, bst[jr * 16 + (ch ^ swz_b(jr))]);
+            if (act0)
+                gacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq, __builtin_bit_cast(bf16x8, cf[0][kk]), gacc[0], 0, 0, 0);
+            gacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq, __builtin_bit_cast(bf16x8, cf[1][kk]), gacc[1], 0, 0, 0);
         }
-        if (tid < 32) {
-            const int tg = tid >> 3, pb = tid & 7;
-            uint4 rr[8];
+    }
+    const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
+    const float* csb = cs_s + 32 * jt + 8 * hf;
+    const float* dtb = dt_s + 32 * jt + 8 * hf;
+    const float* rfb = rf_s + 32 * jt + 8 * hf;
+    // factorised weights exp2(cs_i - c0) * [exp2(c0 - cs_j) dt_j] for blocks
+    // below the diagonal whose own decay stays under 2^64 (c0 = cs of the
+    // block's first token; the row factors rf_s are precomputed per block)
+    const float c0 = cs_s[32 * jt];
+    const bool fact = uniform_f(c0 - cs_s[32 * jt + 31]) <= kMaxBlockDecayLog2;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int tok = tok0 + 32 * jt + 8 * tg + i;
-                rr[i] = (tok < L) ? *reinterpret_cast<const uint4*>(x + (((int64_t)b * L + tok) * H + h) * P + 8 * pb)
-                                  : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < 2; ++t) {
+        if (t == 0 && !act0) continue;
+        uint32_t pk[8];
+        const bool dgb = it_[t] == jt;
+        if (!dgb && fact) {
+            const float colf = fast_exp2(csi[t] - c0);
+#pragma unroll
+            for (int r2 = 0; r2 < 8; ++r2) {
+                const int r = 2 * r2;
+                const int jl = 16 * (r >> 3) + (r & 7);
+                pk[r2] = pack_bf16x2(gacc[t][r] * (rfb[jl] * colf), gacc[t][r + 1] * (rfb[jl + 1] * colf));
             }
-            uint4 o[8];
-            transpose8x8_bf16_scan(rr, o);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int p = 8 * pb + q;
-                xsm[p * 4 + (tg ^ ((p >> 1) & 3))] = o[q];
-            }
-        }
-        __syncthreads();
-
-        // B operand rows of this j block, shared by the wave's two i tiles
-        bf16x8 bfr[8];
-        {
-            const int jr = perm_pi(l32);
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int ch = 2 * kk + hf;
-                bfr[kk] = __builtin_bit_cast(bf16x8, bsm[jr * 16 + (ch ^ (jr & 7))]);
-            }
-        }
-        bf16x8 xfr[2][2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int pr = 32 * mt + perm_sigma(l32);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int blk = 2 * u + hf;
-                xfr[mt][u] = __builtin_bit_cast(bf16x8, xsm[pr * 4 + (blk ^ ((pr >> 1) & 3))]);
-            }
-        }
-
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int it = it_[t];
-            if (it < jt) continue;
-            f32x16 gacc = {};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-                gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk], __builtin_bit_cast(bf16x8, cf[t][kk]), gacc, 0, 0, 0);
-            const int i = 32 * it + l32;
-            uint32_t pk[8];
+        } else {
+            // diagonal block (causal keep bits, D on the diagonal) or a block
+            // with too much decay for the factorisation: direct weights
+            const uint32_t keep = dgb ? diag_keep : 0xffffu;
+            const uint32_t deq = dgb ? diag_eq : 0u;
 #pragma unroll
             for (int r2 = 0; r2 < 8; ++r2) {
                 float v2[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int r = 2 * r2 + e;
-                    const int j = 32 * jt + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    float v = 0.0f;
-                    if (j <= i) v = gacc[r] * fast_exp2(csi[t] - cs_s[j]) * dt_s[j];
-                    if (j == i) v += Dh;
-                    v2[e] = v;
+                    const int jl = 16 * (r >> 3) + (r & 7);
+                    const float kf = (float)((keep >> r) & 1u);
+                    const float df = (float)((deq >> r) & 1u);
+                    v2[e] = gacc[t][r] * (fast_exp2(fminf(csi[t] - csb[jl], 0.0f)) * dtb[jl] * kf) + Dh * df;
                 }
                 pk[r2] = pack_bf16x2(v2[0], v2[1]);
             }
-            const bf16x8 g0 = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            const bf16x8 g1 = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+        }
+        const bf16x8 gq[2] = {__builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3])),
+                              __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]))};
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                acc[t][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xfr[mt][0], g0, acc[t][mt], 0, 0, 0);
-                acc[t][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xfr[mt][1], g1, acc[t][mt], 0, 0, 0);
+        for (int mt = 0; mt < 2; ++mt) {
+            const int pc = 32 * mt + xa.qb;          // multiple of 4
+            const int chk = pc >> 3, sub = (pc & 7) * 2;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r0 = 16 * u + xa.trow0, r1 = r0 + 4;
+                const uint2 lo = tr16(xb + r0 * 128 + ((chk ^ swz_x(r0)) << 4) + sub);
+                const uint2 hi = tr16(xb + r1 * 128 + ((chk ^ swz_x(r1)) << 4) + sub);
+                const bf16x8 xq = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc[t][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, gq[u], acc[t][mt], 0, 0, 0);
             }
         }
     }
+}
 
-    // write y: lane owns token i, channels 32*mt + 16*hf + 0..15
+// y rows of the wave's own tokens: lane owns token i, channels
+// 32*mt + 16*hf + 0..15 (two 16-byte stores per tile).
+__device__ __forceinline__ void scan_store_y(const f32x16 (&acc)[2][2], bf16_t* y, int64_t b, int L,
+                                             int H, int h, int tok0, const int (&it_)[2], int hf,
+                                             int l32, bool guard) {
+    constexpr int P = 64;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int tok = tok0 + 32 * it_[t] + l32;
-        if (tok >= L) continue;
-        bf16_t* yrow = y + (((int64_t)b * L + tok) * H + h) * P;
+        if (guard && tok >= L) continue;
+        bf16_t* yrow = y + ((b * L + tok) * H + h) * P;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             uint32_t w8[8];
@@ -247,6 +250,93 @@ __global__ __launch_bounds__(Q) void chunk_scan_mfma_kernel(
             dst[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (batch, chunk, head).
+template <int Q>
+__global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
+    const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
+    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc) {
+    constexpr int P = 64, N = 128, W = Q / 64, NT = Q / 32;
+    constexpr int DPS = 12 / W;   // LDS-copy instructions per wave per stage
+    __shared__ uint4 hs[1024];                         // Hin, 64 rows x 256 B
+    __shared__ uint4 bs0[512], bs1[512], bs2[512];     // B stages, 32 rows x 256 B
+    __shared__ uint4 xs0[256], xs1[256], xs2[256];     // x stages, 32 rows x 128 B
+    __shared__ float cs_s[Q];
+    __shared__ float dt_s[Q];
+    __shared__ float rf_s[Q];
+
+    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int h = (int)(wg % (uint32_t)H);
+    const int bc = (int)(wg / (uint32_t)H);
+    const int c = bc % nc, b = bc / nc;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int64_t bh = (int64_t)b * H + h;
+    const int64_t row = (bh * nc + c) * Q;
+    const int tok0 = c * Q;
+    const float Dh = D ? D[h] : 0.0f;
+    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+    const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
+    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
+
+    // Ordinary loads are written to LDS / consumed before any LDS copy is
+    // issued: the compiler waits for vmcnt(0) on such uses once a copy is in
+    // flight.
+    {
+        const float cv = cs[row + tid], dv = dtc[row + tid];
+        cs_s[tid] = cv;
+        dt_s[tid] = dv;
+        // row factor of token tid within its 32-token block (see scan_block)
+        rf_s[tid] = fast_exp2(fminf(cs[row + (tid & ~31)] - cv, kMaxBlockDecayLog2)) * dv;
+    }
+    const int it_[2] = {wave, 2 * W - 1 - wave};
+    uint4 cf[2][8];
+    load_c_frags(cf, Cm, b, L, G, g, tok0, it_, hf, l32);
+    float csi[2];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    {
+        const bf16_t* hsrc = Hin + (bh * nc + c) * (int64_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < 16 / W; ++i) {
+            const int k = wave + i * W;
+            const int r = 4 * k + (lane >> 4);
+            const int cc = (lane & 15) ^ swz_h(r);
+            dma16(hsrc + r * N + 8 * cc, lds(hs) + k * 64);
+        }
+    }
+    issue_bx_stage<W>(wave, lane, tok0, L, xbase, xstride, bbase, bstride, bs0, xs0);
+    if (NT > 1) issue_bx_stage<W>(wave, lane, tok0 + 32, L, xbase, xstride, bbase, bstride, bs1, xs1);
+
+    if (NT > 1) wait_vmcnt<2 * DPS>(); else wait_vmcnt<DPS>();
+    barrier_lds();
+    csi[0] = cs_s[32 * it_[0] + l32];
+    csi[1] = cs_s[32 * it_[1] + l32];
+    f32x16 acc[2][2];
+    scan_state_term(acc, hs, cf, csi, hf, l32);
+    const XtAddr xa = xt_addr(lane);
+    const uint32_t dkeep = diag_keep_bits(l32, hf);
+    const uint32_t deq = diag_eq_bits(l32, hf);
+
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+        uint4* bst = (jt % 3 == 0) ? bs0 : ((jt % 3 == 1) ? bs1 : bs2);
+        uint4* xst = (jt % 3 == 0) ? xs0 : ((jt % 3 == 1) ? xs1 : xs2);
+        if (jt + 1 < NT) wait_vmcnt<DPS>(); else wait_vmcnt<0>();
+        barrier_lds();
+        if (jt + 2 < NT) {
+            uint4* nb = ((jt + 2) % 3 == 0) ? bs0 : (((jt + 2) % 3 == 1) ? bs1 : bs2);
+            uint4* nx = ((jt + 2) % 3 == 0) ? xs0 : (((jt + 2) % 3 == 1) ? xs1 : xs2);
+            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + 2), L, xbase, xstride, bbase, bstride, nb, nx);
+        }
+        scan_block(acc, jt, bst, xst, cs_s, dt_s, rf_s, cf, csi, it_, Dh, xa, hf, l32, dkeep, deq);
+    }
+    scan_store_y(acc, y, b, L, H, h, tok0, it_, hf, l32, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -381,17 +471,19 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream) {
     if (mfma_path(dtype, d)) {
-        const unsigned blocks = (unsigned)(d.batch * d.nchunks * d.nheads);
         const bf16_t* xb = static_cast<const bf16_t*>(x);
         const bf16_t* bb = static_cast<const bf16_t*>(B);
         const bf16_t* cb = static_cast<const bf16_t*>(C);
         const bf16_t* hb = static_cast<const bf16_t*>(Hin);
         bf16_t* yb = static_cast<bf16_t*>(y);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
-        switch (d.chunk) {
-            case 64: chunk_scan_mfma_kernel<64><<<blocks, 64, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
-            case 128: chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
-            default: chunk_scan_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
+        {
+            const unsigned blocks = (unsigned)(d.batch * nc * d.nheads);
+            switch (d.chunk) {
+                case 64: chunk_scan_mfma_kernel<64><<<blocks, 64, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
+                case 128: chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
+                default: chunk_scan_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
+            }
         }
     } else if (dtype == 1) {
         launch_generic_t<bf16_t>(d, x, B, C, cs, dtc, Hin, D, y, stream);

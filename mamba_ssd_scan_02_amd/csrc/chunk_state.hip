@@ -22,136 +22,119 @@
 // LDS, fp32 FMA on the vector units.
 #include "device_common.h"
 #include "launchers.h"
+#include "lds_pipe.h"
 
 namespace ssd {
 
-// ---------------------------------------------------------------------------
-// Register transpose of an 8 x 8 block of bf16.
-// in[i]  : 8 values of row i (token i), word m holds columns 2m (lo), 2m+1 (hi)
-// out[q] : 8 values of column q, word k holds tokens 2k (lo), 2k+1 (hi)
-__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&out)[8]) {
-    uint32_t w[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        w[i][0] = in[i].x; w[i][1] = in[i].y; w[i][2] = in[i].z; w[i][3] = in[i].w;
-    }
-    uint32_t o[8][4];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int m = q >> 1;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = w[2 * k][m], hi = w[2 * k + 1][m];
-            o[q][k] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) out[q] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
-}
-
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
-
-// Scale the 8 bf16 of one word-quad by w in fp32 and round back to bf16.
-__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
-    uint32_t in[4] = {v.x, v.y, v.z, v.w};
+// Multiply the 8 bf16 of a fragment by 8 fp32 weights and round back to bf16.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, const float (&w)[8]) {
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const float lo = bf16_bits_to_f32(in[m] & 0xffffu) * w;
-        const float hi = bf16_bits_to_f32(in[m] >> 16) * w;
+        const float lo = bf16_bits_to_f32(in[m] & 0xffffu) * w[2 * m];
+        const float hi = bf16_bits_to_f32(in[m] >> 16) * w[2 * m + 1];
         out[m] = pack_bf16x2(lo, hi);
     }
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// One workgroup (4 waves) per (batch, chunk, head).  Wave w owns state
+// columns n in [32w, 32w+32) for both 32-row tiles of p.  The chunk's tokens
+// stream through a 3-buffer ring of 32-token blocks of B and x copied
+// straight into LDS; both operands are read token-contiguous with tr16, and
+// the decay-and-step weight w_j is applied to the B fragment in fp32 before
+// the single rounding to bf16.
 template <int Q>
-__global__ __launch_bounds__(256) void chunk_state_mfma_kernel(const bf16_t* __restrict__ x,
-                                                               const bf16_t* __restrict__ Bm,
-                                                               const float* __restrict__ cs,
-                                                               const float* __restrict__ dtc,
-                                                               float* __restrict__ S, int L, int H,
-                                                               int G, int nc) {
-    constexpr int P = 64, N = 128, KB = 64;
-    __shared__ uint4 xs[P * (KB / 8)];   // [p][token block], 8 KB
-    __shared__ uint4 bs[N * (KB / 8)];   // [n][token block], 16 KB
-    __shared__ float wv[KB];
+__global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* __restrict__ x,
+                                                                  const bf16_t* __restrict__ Bm,
+                                                                  const float* __restrict__ cs,
+                                                                  const float* __restrict__ dtc,
+                                                                  float* __restrict__ S, int L, int H,
+                                                                  int G, int nc) {
+    constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
+    constexpr int DPS = 12 / W;
+    __shared__ uint4 bs0[512], bs1[512], bs2[512];
+    __shared__ uint4 xs0[256], xs1[256], xs2[256];
+    __shared__ float wv[Q];
 
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
     const int h = (int)(wg % (uint32_t)H);
     const int bc = (int)(wg / (uint32_t)H);
     const int c = bc % nc, b = bc / nc;
     const int g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hf = lane >> 5, l32 = lane & 31;
     const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-    const float cl = cs[row + Q - 1];
+    const int tok0 = c * Q;
+    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+    const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
+    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
 
-    f32x16 acc0 = {}, acc1 = {};
+    // ordinary loads first (see chunk_scan): w_j = exp2(cs_last - cs_j) dt_j
+    float w_v = 0.0f;
+    if (tid < Q) w_v = fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid];
+    asm volatile("" ::: "memory");
+    issue_bx_stage<W>(wave, lane, tok0, L, xbase, xstride, bbase, bstride, bs0, xs0);
+    if (NT > 1) issue_bx_stage<W>(wave, lane, tok0 + 32, L, xbase, xstride, bbase, bstride, bs1, xs1);
+    if (tid < Q) wv[tid] = w_v;
 
-    for (int kb = 0; kb < Q / KB; ++kb) {
-        const int tb = c * Q + kb * KB;
-        if (tid < KB) {
-            const int j = kb * KB + tid;
-            wv[tid] = fast_exp2(cl - cs[row + j]) * dtc[row + j];
+    // tr16 addressing: lane r of group grp supplies token row 8*(grp/2) + r/4
+    // (+ 16u + 4*half) and column quad 16*(grp%2) + 4*(r%4) (identity order).
+    const int grp = lane >> 4, rr = lane & 15;
+    const int trow0 = 8 * (grp >> 1) + (rr >> 2);
+    const int qcol = 16 * (grp & 1) + 4 * (rr & 3);
+
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+        uint4* bst = (jt % 3 == 0) ? bs0 : ((jt % 3 == 1) ? bs1 : bs2);
+        uint4* xst = (jt % 3 == 0) ? xs0 : ((jt % 3 == 1) ? xs1 : xs2);
+        if (jt + 1 < NT) wait_vmcnt<DPS>(); else wait_vmcnt<0>();
+        barrier_lds();
+        if (jt + 2 < NT) {
+            uint4* nb = ((jt + 2) % 3 == 0) ? bs0 : (((jt + 2) % 3 == 1) ? bs1 : bs2);
+            uint4* nx = ((jt + 2) % 3 == 0) ? xs0 : (((jt + 2) % 3 == 1) ? xs1 : xs2);
+            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + 2), L, xbase, xstride, bbase, bstride, nb, nx);
         }
-        __syncthreads();
-        if (tid < 64) {
-            // x task: tokens 8*tg .. +7, columns 8*pb .. +7
-            const int tg = tid >> 3, pb = tid & 7;
-            uint4 r[8];
+        const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
+        const SSD_LDS char* bb = (const SSD_LDS char*)lds(bst);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = tb + 8 * tg + i;
-                r[i] = (t < L) ? *reinterpret_cast<const uint4*>(x + (((int64_t)b * L + t) * H + h) * P + 8 * pb)
-                               : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+            const int r0 = 16 * u + trow0, r1 = r0 + 4;
+            // B^T fragment: columns n = 32*wave + 16*(grp%2) + i, 8 tokens
+            uint4 bq;
+            {
+                const int nc4 = 32 * wave + qcol;
+                const int chk = nc4 >> 3, sub = (nc4 & 7) * 2;
+                const uint2 lo = tr16(bb + r0 * 256 + ((chk ^ swz_b(r0)) << 4) + sub);
+                const uint2 hi = tr16(bb + r1 * 256 + ((chk ^ swz_b(r1)) << 4) + sub);
+                bq = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
+            float wj[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) r[i] = scale_bf16x8(r[i], wv[8 * tg + i]);
-            uint4 o[8];
-            transpose8x8_bf16(r, o);
+            for (int sidx = 0; sidx < 8; ++sidx) wj[sidx] = wv[32 * jt + 16 * u + 8 * hf + sidx];
+            const bf16x8 bw = __builtin_bit_cast(bf16x8, scale_bf16x8(bq, wj));
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int p = 8 * pb + q;
-                xs[p * 8 + (tg ^ swz8(p))] = o[q];
+            for (int mt = 0; mt < 2; ++mt) {
+                const int pc = 32 * mt + qcol;
+                const int chk = pc >> 3, sub = (pc & 7) * 2;
+                const uint2 lo = tr16(xb + r0 * 128 + ((chk ^ swz_x(r0)) << 4) + sub);
+                const uint2 hi = tr16(xb + r1 * 128 + ((chk ^ swz_x(r1)) << 4) + sub);
+                const bf16x8 xq = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, bw, acc[mt], 0, 0, 0);
             }
-        } else if (tid < 192) {
-            // B task: tokens 8*tg .. +7, columns 8*nb .. +7
-            const int u = tid - 64;
-            const int nb = u & 15, tg = u >> 4;
-            uint4 r[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = tb + 8 * tg + i;
-                r[i] = (t < L) ? *reinterpret_cast<const uint4*>(Bm + (((int64_t)b * L + t) * G + g) * N + 8 * nb)
-                               : make_uint4(0, 0, 0, 0);
-            }
-            uint4 o[8];
-            transpose8x8_bf16(r, o);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int n = 8 * nb + q;
-                bs[n * 8 + (tg ^ swz8(n))] = o[q];
-            }
-        }
-        __syncthreads();
-        const int pr0 = lane & 31, pr1 = 32 + (lane & 31), nr = 32 * wave + (lane & 31);
-#pragma unroll
-        for (int kk = 0; kk < KB / 16; ++kk) {
-            const int blk = 2 * kk + (lane >> 5);
-            const bf16x8 a0 = __builtin_bit_cast(bf16x8, xs[pr0 * 8 + (blk ^ swz8(pr0))]);
-            const bf16x8 a1 = __builtin_bit_cast(bf16x8, xs[pr1 * 8 + (blk ^ swz8(pr1))]);
-            const bf16x8 bb = __builtin_bit_cast(bf16x8, bs[nr * 8 + (blk ^ swz8(nr))]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bb, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bb, acc1, 0, 0, 0);
         }
     }
 
     float* Sp = S + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N);
-    const int n = 32 * wave + (lane & 31);
+    const int n = 32 * wave + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int p = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        Sp[p * N + n] = acc0[r];
-        Sp[(32 + p) * N + n] = acc1[r];
+        const int p = 8 * (r >> 2) + 4 * hf + (r & 3);
+        Sp[p * N + n] = acc[0][r];
+        Sp[(32 + p) * N + n] = acc[1][r];
     }
 }
 

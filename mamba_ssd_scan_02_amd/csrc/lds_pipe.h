@@ -1,0 +1,105 @@
+// lds_pipe.h -- gfx950 helpers for staging tiles into LDS without registers
+// and reading MFMA operands out of them.
+//
+//  * dma16(): global_load_lds_dwordx4 -- each lane copies 16 bytes from its
+//    own global address into LDS at (wave-uniform base) + 16 * lane.  The
+//    copies count in vmcnt like loads; they are waited for with an explicit
+//    s_waitcnt vmcnt(n) and made visible to the workgroup with s_barrier.
+//    Pipeline buffers are distinct __shared__ arrays selected with
+//    compile-time indices, so the compiler can tell an outstanding copy into
+//    one buffer from a read of another and does not force vmcnt(0).
+//  * tr16(): ds_read_b64_tr_b16 -- within each group of 16 lanes, lane i
+//    receives element (i % 4) of the 4-element (8-byte) rows addressed by
+//    lanes 4k + i/4, k = 0..3.  If lane r of a group addresses row (token)
+//    t0 + r/4 at column quad q(r % 4), lane i gets 4 consecutive tokens of
+//    column q(i/4) + i%4: the K-contiguous operand fragment of a token-major
+//    tile.
+//  * Row swizzles: the 16-byte chunk index inside an LDS row is XORed with a
+//    function of the row so that the operand reads hit distinct banks.  The
+//    copy side realises the swizzle by choosing, for LDS slot c', the global
+//    chunk c = c' ^ f(row).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+#define SSD_LDS __attribute__((address_space(3)))
+
+namespace ssd {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16(const void* gsrc, SSD_LDS void* ldst) {
+    __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n): at most n of this wave's vector-memory operations
+// (loads, stores and LDS copies, which retire in order) still outstanding.
+// Written with the builtin so that the compiler's own wait insertion knows
+// about it (it cannot see inside asm, and would otherwise drain every copy
+// in flight before each LDS read).  The builtin is modelled as touching no
+// memory, so it is always followed by barrier_lds() or a compiler fence.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Finish this wave's LDS accesses, then meet the rest of the workgroup.  As
+// asm with a "memory" clobber (the s_barrier builtin is modelled as touching
+// no memory) so that no LDS access moves across it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint2 tr16(const SSD_LDS void* p) {
+    v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSD_LDS v4s*)p);
+    return __builtin_bit_cast(uint2, v);
+}
+
+template <typename T>
+__device__ __forceinline__ SSD_LDS T* lds(T* p) {
+    return (SSD_LDS T*)(p);
+}
+
+// Chunk swizzles (16-byte chunk index XOR f(row)).
+// x tiles: 128-byte rows of 64 channels, read only through tr16.
+__device__ __forceinline__ int swz_x(int r) { return (r & 8) >> 1; }
+// B tiles: 256-byte rows of 128 state entries, read as rows (ds_read_b128)
+// by the C.B^T product and through tr16 by the chunk-state product.
+__device__ __forceinline__ int swz_b(int r) { return (r & 3) | ((r & 8) >> 1); }
+// Hin tiles: 256-byte rows, read as rows in the permuted order of the
+// carried-state product.
+__device__ __forceinline__ int swz_h(int r) { return (r & 3) | ((r & 16) >> 2); }
+
+// Copy a block of 32 tokens of B (32 rows x 256 B) and x (32 rows x
+// 128 B) into one pipeline buffer: 8 + 4 LDS-copy instructions per
+// workgroup, spread over its W waves.  Tokens past the end of the sequence
+// re-read the last token (finite values whose weights are zero).
+template <int W>
+__device__ __forceinline__ void issue_bx_stage(int wave, int lane, int tokbase, int L,
+                                                 const bf16_t* xbase, int64_t xstride,
+                                                 const bf16_t* bbase, int64_t bstride,
+                                                 uint4* bst, uint4* xst) {
+#pragma unroll
+    for (int i = 0; i < 8 / W; ++i) {
+        const int k = wave + i * W;
+        const int r = 4 * k + (lane >> 4);
+        const int cc = (lane & 15) ^ swz_b(r);
+        const int tok = min(tokbase + r, L - 1);
+        dma16(bbase + tok * bstride + 8 * cc, lds(bst) + k * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 / W; ++i) {
+        const int k = wave + i * W;
+        const int r = 8 * k + (lane >> 3);
+        const int cc = (lane & 7) ^ swz_x(r);
+        const int tok = min(tokbase + r, L - 1);
+        dma16(xbase + tok * xstride + 8 * cc, lds(xst) + k * 64);
+    }
+}
+
+}  // namespace ssd
