@@ -3,6 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 
+Profiling helpers (see profiles/):
+    python bench.py --profile-loop K      run each kernel K times, plus a
+                                          1 GiB device copy for calibration
+    python bench.py --summarize-trace DIR --out FILE
+    python bench.py --summarize-counters DIR_FETCH DIR_WRITE --out-dir profiles
+
 A step is one ssd_forward call (chunk cumsum, chunk state, state passing and
 chunk scan) over the Mamba-2-2.7B-shaped workload: batch 4, seqlen 8192, 80
 heads, P = 64, N = 128, one B/C group, chunk 256, bf16 x/B/C, fp32 dt/A/D and
@@ -208,6 +214,142 @@ def cpu_baseline(inp, budget_s=12.0):
                       f"workload (= {tokens_equiv:.0f} full-width tokens) in {t_total:.1f} s"}
 
 
+# ----------------------------------------------------------------- profiling
+COPY_BYTES = 1 << 30
+
+
+def profile_loop(k: int):
+    """Each kernel of the forward and decode paths k times, then a plain
+    device-to-device copy of COPY_BYTES (the counter calibration)."""
+    import torch
+
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as spec
+    from mamba_ssd_scan_02_amd.workloads import make_forward_inputs
+    dims = (spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups,
+            spec.chunk)
+    b, L, H, P, N, G, Q = dims
+    inp = make_forward_inputs(spec)
+    g = {kk: v.cuda() for kk, v in inp.items()}
+    y = torch.empty_like(g["x"])
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ssd.workspace_bytes(b, L, H, P, N, G, Q, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    time_stages(ssd, g, y, fin, ws, dims, k)
+    from mamba_ssd_scan_02_amd.workloads import DECODE_B256 as dspec
+    from mamba_ssd_scan_02_amd.workloads import make_decode_static, make_decode_step
+    st = make_decode_static(dspec)
+    state = st["state"].cuda()
+    A, D = st["A"].cuda(), st["D"].cuda()
+    s0 = {kk: v.cuda() for kk, v in make_decode_step(dspec, 0).items()}
+    for _ in range(k):
+        ssd.ssm_step(state, s0["x"], s0["dt"], A, s0["B"], s0["C"], D)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(k):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[profile-loop] done ({k} iterations)")
+
+
+def _short_kernel(name: str) -> str:
+    for k in KERNEL_SOURCES:
+        if k in name:
+            return k
+    if "copyBuffer" in name or "copy" in name.lower():
+        return "copy"
+    return name.split("(")[0][-40:]
+
+
+def summarize_trace(d: str, out: str, cmd: str):
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not f:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    lines = ["# rocprofv3 kernel trace summary (per-kernel dispatch durations)",
+             f"command: {cmd}", "",
+             f"{'kernel':24s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_%':>8s}"]
+    for r in rows:
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"{_short_kernel(r['Name']):24s} {int(r['Calls']):6d} {avg:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):8.2f}")
+    lines.append("")
+    lines.append("full kernel names:")
+    for r in rows:
+        lines.append(f"  {_short_kernel(r['Name'])}: {r['Name'][:160]}")
+    Path(out).write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str, cmd_write: str):
+    """Per-kernel HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled by the ratio known bytes / counter value of the
+    calibration copy (COPY_BYTES read and written)."""
+    import csv
+    import glob
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B, DECODE_B256
+
+    def load(dd, counter):
+        f = sorted(glob.glob(os.path.join(dd, "**", "*counter_collection.csv"), recursive=True))
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {dd}")
+        acc = {}
+        copies = []
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            if k == "copy":
+                copies.append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+            else:
+                acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        if copies:   # the calibration copy is the largest one
+            gmax = max(gs for gs, _ in copies)
+            acc["copy"] = [v for gs, v in copies if gs == gmax]
+        return acc
+
+    fetch = load(d_fetch, "FETCH_SIZE")
+    write = load(d_write, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("calibration copy missing from the counters")
+    cf = COPY_BYTES / (sum(fetch["copy"]) / len(fetch["copy"]) * 1024)
+    cw = COPY_BYTES / (sum(write["copy"]) / len(write["copy"]) * 1024)
+    b, L, H, P, N, G, Q = (MAMBA2_2P7B.batch, MAMBA2_2P7B.seqlen, MAMBA2_2P7B.nheads,
+                           MAMBA2_2P7B.headdim, MAMBA2_2P7B.dstate, MAMBA2_2P7B.ngroups,
+                           MAMBA2_2P7B.chunk)
+    alg, _ = forward_model(b, L, H, P, N, G, Q)
+    db = DECODE_B256
+    alg["ssm_step"] = (db.batch * db.nheads * db.headdim * db.dstate * 4 * 2 +
+                       db.batch * db.nheads * db.headdim * 2 * 2 + db.batch * db.nheads * 4 +
+                       2 * db.batch * db.ngroups * db.dstate * 2 + 2 * db.nheads * 4)
+    for k in KERNEL_SOURCES:
+        if k not in fetch or k not in write:
+            continue
+        fk = sum(fetch[k]) / len(fetch[k]) * 1024 * cf
+        wk = sum(write[k]) / len(write[k]) * 1024 * cw
+        wl = DECODE_B256.name if k == "ssm_step" else MAMBA2_2P7B.name
+        text = "\n".join([
+            f"# HBM traffic of {k} on {wl} (rocprofv3 counters, calibrated)",
+            f"command_fetch: {cmd_fetch}",
+            f"command_write: {cmd_write}",
+            f"calibration: a {COPY_BYTES}-byte device copy reads FETCH_SIZE x {cf:.4f} and writes "
+            f"WRITE_SIZE x {cw:.4f} of its counter values (KiB per dispatch)",
+            f"dispatches: {len(fetch[k])}",
+            f"fetch_bytes_per_dispatch: {fk:.6g}",
+            f"write_bytes_per_dispatch: {wk:.6g}",
+            f"hbm_bytes_per_dispatch: {fk + wk:.6g}",
+            f"algorithmic_bytes_per_dispatch: {alg[k]}",
+            f"traffic_over_algorithmic: {(fk + wk) / alg[k]:.4f}",
+            f"source_sha256_16: {source_hash(k)}",
+        ]) + "\n"
+        outp = Path(out_dir) / f"{k}_{wl}_counters.txt"
+        outp.write_text(text)
+        print(text)
+
+
 # ---------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -216,7 +358,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-loop", type=int, default=0)
+    ap.add_argument("--summarize-trace", default=None)
+    ap.add_argument("--summarize-counters", nargs=2, default=None)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--out-dir", default="profiles")
+    ap.add_argument("--cmd", default="", help="command recorded in a summary")
+    ap.add_argument("--cmd2", default="", help="second command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.cmd)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.out_dir,
+                           args.cmd, args.cmd2)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -232,6 +388,9 @@ def main():
     ssd.load()
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
+    if args.profile_loop:
+        profile_loop(args.profile_loop)
+        return
     dims = (spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups,
             spec.chunk)
     b, L, H, P, N, G, Q = dims
