@@ -7,66 +7,74 @@
 // inside a chunk every such product is exp of a difference of this prefix.
 // Storing log2(e) * prefix lets consumers use the hardware exp2 directly.
 //
-// One workgroup (4 waves) per (batch, chunk, 32-head slice).  The [Q x 32]
-// slab of dt is read coalesced along heads into LDS; each wave then scans
-// one head's Q values (up to 4 per lane, wave-level prefix by shuffles) with
-// fp64 accumulation, rounding once to fp32 on the store.
+// One workgroup (256 threads) per (batch, chunk, 32-head slice).  The
+// [Q x 32] slab of dt is read coalesced along heads into LDS.  Thread
+// (segment s, head hh) then sums its Q/8 consecutive tokens in fp64, the 8
+// segment totals of a head are combined through LDS, and each thread writes
+// its segment's prefix (rounded once to fp32) back into LDS.  Both outputs
+// leave as whole head rows of Q contiguous floats.
 #include "device_common.h"
 #include "launchers.h"
 
 namespace ssd {
 
 constexpr int kCsHeads = 32;
+constexpr int kCsSegs = 8;
 
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ dt,
                                                            const float* __restrict__ A,
                                                            float* __restrict__ cs,
                                                            float* __restrict__ dtc, int L,
                                                            int H, int Q, int nc) {
-    __shared__ float tile[256][kCsHeads + 1];
+    __shared__ float dts[256][kCsHeads + 1];
+    __shared__ float css[256][kCsHeads + 1];
+    __shared__ double segsum[kCsSegs][kCsHeads];
     const int b = blockIdx.x / nc;
-    const int c = blockIdx.x % nc;
+    const int c = blockIdx.x - b * nc;
     const int h0 = blockIdx.y * kCsHeads;
     const int nh = min(kCsHeads, H - h0);
     const int t0 = c * Q;
     const int nt = min(Q, L - t0);
+    const int tid = threadIdx.x;
+    const int hh = tid & (kCsHeads - 1), seg = tid >> 5;
 
-    for (int e = threadIdx.x; e < Q * nh; e += blockDim.x) {
-        const int j = e / nh, hh = e % nh;
-        tile[j][hh] = (j < nt) ? dt[((int64_t)b * L + t0 + j) * H + h0 + hh] : 0.0f;
+    {
+        // all of a thread's loads in flight before the first LDS write
+        const float* src = dt + ((int64_t)b * L + t0) * H + h0 + hh;
+        float v[256 / kCsSegs];
+#pragma unroll
+        for (int k = 0; k < 256 / kCsSegs; ++k) {
+            const int j = seg + kCsSegs * k;
+            v[k] = (j < nt && hh < nh) ? src[(int64_t)j * H] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 256 / kCsSegs; ++k) {
+            const int j = seg + kCsSegs * k;
+            if (j < Q) dts[j][hh] = v[k];
+        }
     }
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int epl = (Q + 63) >> 6;  // values per lane, <= 4
-    for (int hh = wave; hh < nh; hh += 4) {
-        const int h = h0 + hh;
-        const double a = (double)A[h] * 1.4426950408889634074;
-        double pre[4];
-        double run = 0.0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int j = lane * epl + k;
-            const double v = (k < epl && j < Q) ? (double)tile[j][hh] * a : 0.0;
-            run += v;
-            pre[k] = run;
-        }
-        double incl = run;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        const double excl = incl - run;
-        float* csr = cs + (((int64_t)b * H + h) * nc + c) * Q;
-        float* dtr = dtc + (((int64_t)b * H + h) * nc + c) * Q;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int j = lane * epl + k;
-            if (k < epl && j < Q) {
-                csr[j] = (float)(excl + pre[k]);
-                dtr[j] = tile[j][hh];
-            }
+    const int sl = (Q + kCsSegs - 1) / kCsSegs;
+    const int j0 = min(seg * sl, Q), j1 = min(j0 + sl, Q);
+    const double a = (hh < nh) ? (double)A[h0 + hh] * 1.4426950408889634074 : 0.0;
+    double run = 0.0;
+    for (int j = j0; j < j1; ++j) run += (double)dts[j][hh] * a;
+    segsum[seg][hh] = run;
+    __syncthreads();
+    run = 0.0;
+    for (int s = 0; s < seg; ++s) run += segsum[s][hh];
+    for (int j = j0; j < j1; ++j) {
+        run += (double)dts[j][hh] * a;
+        css[j][hh] = (float)run;
+    }
+    __syncthreads();
+
+    for (int k = 0; k < nh; ++k) {
+        const int64_t off = (((int64_t)b * H + h0 + k) * nc + c) * Q;
+        for (int j = tid; j < Q; j += 256) {
+            cs[off + j] = css[j][k];
+            dtc[off + j] = dts[j][k];
         }
     }
 }

@@ -41,6 +41,8 @@
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
+#include <cmath>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "lds_pipe.h"
@@ -75,19 +77,20 @@ __device__ __forceinline__ XtAddr xt_addr(int lane) {
     return a;
 }
 
-// Largest decay inside one 32-token block (log2 units) for which the
-// factorised weights are used; beyond it the row factor exp2(c0 - cs_j)
-// could overflow, and the direct form is taken.
-constexpr float kMaxBlockDecayLog2 = 64.0f;
+// Largest decay across one 32-token output tile (log2 units) for which the
+// factorised weights are used; beyond it the per-token factors could
+// overflow, and the tile takes the direct form.
+constexpr float kMaxTileDecayLog2 = 64.0f;
 
 __device__ __forceinline__ float uniform_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
-// Causal keep bits of the diagonal block for this lane.  Accumulator
-// register r of lane (l32, hf) holds token j = 16*(r/8) + 8*hf + r%8 of the
-// block and column i = l32: with t = l32 - 8*hf, registers r < 8 are kept
-// iff r <= t and registers r >= 8 iff r - 8 <= t - 16.
+// Accumulator register r of lane (l32, hf) of a G^T tile holds block token
+// j = 16*(r/8) + 8*hf + r%8 and column (output token) i = l32.
+__host__ __device__ constexpr int gt_row(int r, int hf) { return 16 * (r >> 3) + 8 * hf + (r & 7); }
+
+// Causal keep bits of the diagonal block for this lane (direct form).
 __device__ __forceinline__ uint32_t diag_keep_bits(int l32, int hf) {
     const int t = l32 - 8 * hf;
     const int n0 = min(max(t + 1, 0), 8), n1 = min(max(t - 15, 0), 8);
@@ -95,7 +98,7 @@ __device__ __forceinline__ uint32_t diag_keep_bits(int l32, int hf) {
 }
 
 // Bit r set iff accumulator register r of this lane is the diagonal entry
-// j == i of the diagonal block (at most one per lane).
+// j == i of the diagonal block (at most one per lane; direct form).
 __device__ __forceinline__ uint32_t diag_eq_bits(int l32, int hf) {
     const int t = l32 - 8 * hf;
     if (t >= 0 && t < 8) return 1u << t;
@@ -104,23 +107,38 @@ __device__ __forceinline__ uint32_t diag_eq_bits(int l32, int hf) {
 }
 
 // C fragments of the wave's own tokens (B operand of both C products).
+// Tokens past the end of the sequence re-read the last token: C_i only
+// reaches output column i, which is not stored for those tokens.
 __device__ __forceinline__ void load_c_frags(uint4 (&cf)[2][8], const bf16_t* Cm, int64_t b, int L,
                                              int G, int g, int tok0, const int (&it_)[2], int hf,
                                              int l32) {
     constexpr int N = 128;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int tok = tok0 + 32 * it_[t] + l32;
+        const int tok = min(tok0 + 32 * it_[t] + l32, L - 1);
         const bf16_t* crow = Cm + ((b * L + tok) * G + g) * N + 8 * hf;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            cf[t][kk] = (tok < L) ? *reinterpret_cast<const uint4*>(crow + 16 * kk) : make_uint4(0, 0, 0, 0);
+        for (int kk = 0; kk < 8; ++kk) cf[t][kk] = *reinterpret_cast<const uint4*>(crow + 16 * kk);
     }
 }
 
-// (ii) carried state: acc[t][mt] = exp2(cs_i) * sum_n Hin[p][n] C[i][n].
+// Per-tile factors.  With the factorised form (fact), tile t's weights are
+// exp2(cs_i - cs_j) dt_j = colf_i * rf_j, colf_i = exp2(cs_i - cref) and
+// rf_j = exp2(cref - cs_j) dt_j with cref = cs of the tile's first token:
+// the accumulator gathers sum_j x_j G_ji rf_j (+ D x_i / colf_i on the
+// diagonal), starts from exp2(cref) * (Hin C_i) and is scaled by colf_i at
+// the end.  Otherwise (direct form) the weights are formed per element and
+// the state term is scaled by exp2(cs_i).
+struct TileF {
+    bool fact;
+    float colf;     // final column scale (1 for the direct form)
+    float sstate;   // scale of the state term
+    float dprime;   // D / colf_i, the diagonal addend of the factorised form
+};
+
+// (ii) carried state: acc[t][mt] = sstate_t * sum_n Hin[p][n] C[i][n].
 __device__ __forceinline__ void scan_state_term(f32x16 (&acc)[2][2], const uint4* hs,
-                                                const uint4 (&cf)[2][8], const float (&csi)[2],
+                                                const uint4 (&cf)[2][8], const TileF (&tf)[2],
                                                 int hf, int l32) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -139,23 +157,22 @@ __device__ __forceinline__ void scan_state_term(f32x16 (&acc)[2][2], const uint4
         }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const float s = fast_exp2(csi[t]);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][mt][r] *= s;
-    }
+            for (int r = 0; r < 16; ++r) acc[t][mt][r] *= tf[t].sstate;
 }
 
-// (i) + (iii) for j block jt: G^T tiles from the B block, masked decay
-// weights (+ D on the diagonal), then Y^T += X^T G~^T.
+// (i) + (iii) for j block jt: G^T tiles from the B block, decay weights
+// (+ D on the diagonal), then Y^T += X^T G~^T.
+template <int Q>
 __device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const uint4* bst,
                                            const uint4* xst, const float* cs_s, const float* dt_s,
-                                           const float* rf_s, const uint4 (&cf)[2][8],
-                                           const float (&csi)[2], const int (&it_)[2], float Dh,
-                                           XtAddr xa, int hf, int l32, uint32_t diag_keep,
-                                           uint32_t diag_eq) {
+                                           const float* rfT, const uint4 (&cf)[2][8],
+                                           const float (&csi)[2], const int (&it_)[2],
+                                           const TileF (&tf)[2], float Dh, XtAddr xa, int hf,
+                                           int l32, uint32_t diag_keep, uint32_t diag_eq) {
     if (it_[1] < jt) return;   // it_[1] >= it_[0]: nothing left for this wave
     const bool act0 = it_[0] >= jt;
     f32x16 gacc[2] = {f32x16{}, f32x16{}};
@@ -171,30 +188,43 @@ __device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const ui
         }
     }
     const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
-    const float* csb = cs_s + 32 * jt + 8 * hf;
-    const float* dtb = dt_s + 32 * jt + 8 * hf;
-    const float* rfb = rf_s + 32 * jt + 8 * hf;
-    // factorised weights exp2(cs_i - c0) * [exp2(c0 - cs_j) dt_j] for blocks
-    // below the diagonal whose own decay stays under 2^64 (c0 = cs of the
-    // block's first token; the row factors rf_s are precomputed per block)
-    const float c0 = cs_s[32 * jt];
-    const bool fact = uniform_f(c0 - cs_s[32 * jt + 31]) <= kMaxBlockDecayLog2;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (t == 0 && !act0) continue;
         uint32_t pk[8];
         const bool dgb = it_[t] == jt;
-        if (!dgb && fact) {
-            const float colf = fast_exp2(csi[t] - c0);
+        if (tf[t].fact) {
+            // rf_j of this tile's reference for the lane's 16 block tokens
+            const float* rfb = rfT + it_[t] * Q + 32 * jt + 8 * hf;
+            const float4 f0 = *reinterpret_cast<const float4*>(rfb);
+            const float4 f1 = *reinterpret_cast<const float4*>(rfb + 4);
+            const float4 f2 = *reinterpret_cast<const float4*>(rfb + 16);
+            const float4 f3 = *reinterpret_cast<const float4*>(rfb + 20);
+            const float rf[16] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w,
+                                  f2.x, f2.y, f2.z, f2.w, f3.x, f3.y, f3.z, f3.w};
+            if (!dgb) {
 #pragma unroll
-            for (int r2 = 0; r2 < 8; ++r2) {
-                const int r = 2 * r2;
-                const int jl = 16 * (r >> 3) + (r & 7);
-                pk[r2] = pack_bf16x2(gacc[t][r] * (rfb[jl] * colf), gacc[t][r + 1] * (rfb[jl + 1] * colf));
+                for (int r2 = 0; r2 < 8; ++r2)
+                    pk[r2] = pack_bf16x2(gacc[t][2 * r2] * rf[2 * r2], gacc[t][2 * r2 + 1] * rf[2 * r2 + 1]);
+            } else {
+                // causal mask j <= i and D on j == i; with t = l32 - 8 hf,
+                // register r holds j - 8 hf = 16 (r / 8) + r % 8
+                int tcol = l32 - 8 * hf;
+                asm volatile("" : "+v"(tcol));   // compares stay inside this block
+                float v[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jr = 16 * (r >> 3) + (r & 7);
+                    const float w = (tcol >= jr) ? gacc[t][r] * rf[r] : 0.0f;
+                    v[r] = (tcol == jr) ? w + tf[t].dprime : w;
+                }
+#pragma unroll
+                for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
             }
         } else {
-            // diagonal block (causal keep bits, D on the diagonal) or a block
-            // with too much decay for the factorisation: direct weights
+            // direct weights for a tile with too much decay to factorise
+            const float* csb = cs_s + 32 * jt + 8 * hf;
+            const float* dtb = dt_s + 32 * jt + 8 * hf;
             const uint32_t keep = dgb ? diag_keep : 0xffffu;
             const uint32_t deq = dgb ? diag_eq : 0u;
 #pragma unroll
@@ -230,113 +260,236 @@ __device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const ui
 }
 
 // y rows of the wave's own tokens: lane owns token i, channels
-// 32*mt + 16*hf + 0..15 (two 16-byte stores per tile).
-__device__ __forceinline__ void scan_store_y(const f32x16 (&acc)[2][2], bf16_t* y, int64_t b, int L,
-                                             int H, int h, int tok0, const int (&it_)[2], int hf,
-                                             int l32, bool guard) {
-    constexpr int P = 64;
+// 32*mt + 16*hf + 0..15 (two 16-byte stores per tile), after the final
+// column scale.  Buffer stores against a record bounded by the sequence end:
+// every wave always issues its 8 stores (fixed memory-counter arithmetic),
+// and the hardware drops those of tokens past the end.
+__device__ __forceinline__ void scan_store_y(const f32x16 (&acc)[2][2], const TileF (&tf)[2],
+                                             __amdgpu_buffer_rsrc_t yrs, int rowbytes,
+                                             const int (&it_)[2], int hf, int l32) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int tok = tok0 + 32 * it_[t] + l32;
-        if (guard && tok >= L) continue;
-        bf16_t* yrow = y + ((b * L + tok) * H + h) * P;
+        const int off = (32 * it_[t] + l32) * rowbytes + 32 * hf;
+        const float s = tf[t].colf;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             uint32_t w8[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) w8[k] = pack_bf16x2(acc[t][mt][2 * k], acc[t][mt][2 * k + 1]);
-            uint4* dst = reinterpret_cast<uint4*>(yrow + 32 * mt + 16 * hf);
-            dst[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
-            dst[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+            for (int k = 0; k < 8; ++k) w8[k] = pack_bf16x2(acc[t][mt][2 * k] * s, acc[t][mt][2 * k + 1] * s);
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v0 = {w8[0], w8[1], w8[2], w8[3]};
+            const u32x4 v1 = {w8[4], w8[5], w8[6], w8[7]};
+            __builtin_amdgcn_raw_buffer_store_b128(v0, yrs, off + 64 * mt, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v1, yrs, off + 64 * mt + 16, 0, 0);
         }
     }
 }
 
+// Pipeline buffer k of a 4-deep ring (compile-time k after unrolling).
+template <typename T>
+__device__ __forceinline__ T* ring4(int k, T* a0, T* a1, T* a2, T* a3) {
+    const int m = k & 3;
+    return m == 0 ? a0 : (m == 1 ? a1 : (m == 2 ? a2 : a3));
+}
+
+// s_waitcnt vmcnt(n) for an n that is a constant once the caller's loop is
+// unrolled (the switch folds to one case).
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+    switch (n) {
+#define SSD_WAIT_CASE(k) case k: wait_vmcnt<k>(); break;
+        SSD_WAIT_CASE(0) SSD_WAIT_CASE(1) SSD_WAIT_CASE(2) SSD_WAIT_CASE(3) SSD_WAIT_CASE(4)
+        SSD_WAIT_CASE(5) SSD_WAIT_CASE(6) SSD_WAIT_CASE(7) SSD_WAIT_CASE(8) SSD_WAIT_CASE(9)
+        SSD_WAIT_CASE(10) SSD_WAIT_CASE(11) SSD_WAIT_CASE(12) SSD_WAIT_CASE(13) SSD_WAIT_CASE(14)
+        SSD_WAIT_CASE(15) SSD_WAIT_CASE(16) SSD_WAIT_CASE(17) SSD_WAIT_CASE(18) SSD_WAIT_CASE(19)
+        SSD_WAIT_CASE(20) SSD_WAIT_CASE(21) SSD_WAIT_CASE(22) SSD_WAIT_CASE(23) SSD_WAIT_CASE(24)
+        SSD_WAIT_CASE(25) SSD_WAIT_CASE(26) SSD_WAIT_CASE(27) SSD_WAIT_CASE(28) SSD_WAIT_CASE(29)
+        SSD_WAIT_CASE(30) SSD_WAIT_CASE(31) SSD_WAIT_CASE(32) SSD_WAIT_CASE(33) SSD_WAIT_CASE(34)
+        SSD_WAIT_CASE(35) SSD_WAIT_CASE(36) SSD_WAIT_CASE(37) SSD_WAIT_CASE(38) SSD_WAIT_CASE(39)
+#undef SSD_WAIT_CASE
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
+// Memory operations a wave issues at loop step k of a head (stage k + 3 of
+// this head or of the next, and at k = 0 the next head's carried state and
+// cs/dt rows).
+__host__ __device__ constexpr int scan_issue_ops(int NT, int k, bool more, int DPS, int DH, int DC) {
+    return (k + 3 < NT ? DPS : (more ? DPS : 0)) + (k == 0 && more ? DH + DC : 0);
+}
+// Operations issued after stage jt of the current head and before the wait
+// at step jt: stages 0..2 came at the end of the previous head, followed by
+// its NY y stores.
+__host__ __device__ constexpr int scan_ops_after(int NT, int jt, bool more, int DPS, int DH, int DC,
+                                                 int NY) {
+    int n = 0;
+    if (jt <= 2) {
+        n = (2 - jt) * DPS + NY;
+        for (int k = 0; k < jt; ++k) n += scan_issue_ops(NT, k, more, DPS, DH, DC);
+    } else {
+        n = (jt == 3 && more) ? DH + DC : 0;   // issued right after stage 3
+        for (int k = jt - 2; k < jt; ++k) n += scan_issue_ops(NT, k, more, DPS, DH, DC);
+    }
+    return n;
+}
+
 // ---------------------------------------------------------------------------
-// One workgroup per (batch, chunk, head).
+// One workgroup per (batch, chunk, run of hg heads of one group).  The heads
+// share C, so the C fragments are loaded once; everything a head needs
+// besides (its carried state, cs/dt rows, x) streams in while the previous
+// head computes:
+//   per wave and head, in issue order (Q = 256: 4 waves, 3 copies a stage):
+//     jt = 0: stage 3, Hin(next) x4, cs/dt(next) x2
+//     jt = 1..4: stages 4..7;  jt = 5..7: stages 0..2 of the next head
+//     end: 8 y stores
+// and the wait before block jt leaves exactly the operations issued after
+// stage jt outstanding (fewer on the last head, which prefetches nothing).
 template <int Q>
 __global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
-    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc) {
+    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg) {
     constexpr int P = 64, N = 128, W = Q / 64, NT = Q / 32;
-    constexpr int DPS = 12 / W;   // LDS-copy instructions per wave per stage
-    __shared__ uint4 hs[1024];                         // Hin, 64 rows x 256 B
-    __shared__ uint4 bs0[512], bs1[512], bs2[512];     // B stages, 32 rows x 256 B
-    __shared__ uint4 xs0[256], xs1[256], xs2[256];     // x stages, 32 rows x 128 B
-    __shared__ float cs_s[Q];
+    static_assert(NT % 4 == 0, "the ring index must repeat every head");
+    constexpr int DPS = 12 / W;      // LDS-copy instructions per wave per stage
+    constexpr int DH = 16 / W;       // ... for the carried state
+    constexpr int DC = 2;            // ... for the cs and dt rows
+    constexpr int NY = 8;            // y stores per wave
+    // One array per copy target in flight (the compiler tracks a few LDS
+    // copy targets separately and waits for all copies beyond that).
+    __shared__ uint4 hs[1024];                              // Hin, 64 rows x 256 B
+    __shared__ uint4 st0[768], st1[768], st2[768], st3[768];   // stages: B 32 x 256 B, x 32 x 128 B
+    __shared__ float csdt_n[2 * Q];                         // next head's cs and dt rows
+    __shared__ float cs_s[Q];                               // current head's
     __shared__ float dt_s[Q];
-    __shared__ float rf_s[Q];
+    __shared__ __align__(16) float rfT[NT * Q];             // rf_j per output tile
 
+    const int ngr = H / hg;
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int h = (int)(wg % (uint32_t)H);
-    const int bc = (int)(wg / (uint32_t)H);
+    const int hgi = (int)(wg % (uint32_t)ngr);
+    const int bc = (int)(wg / (uint32_t)ngr);
     const int c = bc % nc, b = bc / nc;
-    const int g = h / (H / G);
+    const int h0 = hgi * hg;
+    const int g = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5, l32 = lane & 31;
-    const int64_t bh = (int64_t)b * H + h;
-    const int64_t row = (bh * nc + c) * Q;
     const int tok0 = c * Q;
-    const float Dh = D ? D[h] : 0.0f;
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
-    const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
     const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
+    const int rowbytes = H * P * 2;
+    const int yrecord = (L - 1 - tok0) * rowbytes + P * 2;   // end of the last valid row
 
-    // Ordinary loads are written to LDS / consumed before any LDS copy is
-    // issued: the compiler waits for vmcnt(0) on such uses once a copy is in
-    // flight.
-    {
-        const float cv = cs[row + tid], dv = dtc[row + tid];
-        cs_s[tid] = cv;
-        dt_s[tid] = dv;
-        // row factor of token tid within its 32-token block (see scan_block)
-        rf_s[tid] = fast_exp2(fminf(cs[row + (tid & ~31)] - cv, kMaxBlockDecayLog2)) * dv;
-    }
-    const int it_[2] = {wave, 2 * W - 1 - wave};
-    uint4 cf[2][8];
-    load_c_frags(cf, Cm, b, L, G, g, tok0, it_, hf, l32);
-    float csi[2];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    {
-        const bf16_t* hsrc = Hin + (bh * nc + c) * (int64_t)(P * N);
+    // Copies for head h0: cs/dt rows, the carried state, stages 0..2.
+    auto issue_csdt = [&](int h) {
+        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+        dma4(cs + row, 4u * (uint32_t)tid, lds(csdt_n) + 64 * wave);
+        dma4(dtc + row, 4u * (uint32_t)tid, lds(csdt_n) + Q + 64 * wave);
+    };
+    auto issue_hin = [&](int h) {
+        const bf16_t* hsrc = Hin + ((((int64_t)b * H + h) * nc + c) * (int64_t)(P * N));
 #pragma unroll
-        for (int i = 0; i < 16 / W; ++i) {
+        for (int i = 0; i < DH; ++i) {
             const int k = wave + i * W;
             const int r = 4 * k + (lane >> 4);
             const int cc = (lane & 15) ^ swz_h(r);
-            dma16(hsrc + r * N + 8 * cc, lds(hs) + k * 64);
+            dma16(hsrc, (uint32_t)(r * N + 8 * cc) * 2u, lds(hs) + k * 64);
         }
-    }
-    issue_bx_stage<W>(wave, lane, tok0, L, xbase, xstride, bbase, bstride, bs0, xs0);
-    if (NT > 1) issue_bx_stage<W>(wave, lane, tok0 + 32, L, xbase, xstride, bbase, bstride, bs1, xs1);
+    };
+    auto issue_stage = [&](int h, int s, uint4* bst, uint4* xst) {
+        const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
+        issue_bx_stage<W>(wave, lane, tok0 + 32 * s, L, xbase, xstride, bbase, bstride, bst, xst);
+    };
+    // rf table and current cs/dt rows from the copied next-head rows.
+    auto make_tables = [&]() {
+        const float cv = csdt_n[tid], dv = csdt_n[Q + tid];
+        cs_s[tid] = cv;
+        dt_s[tid] = dv;
+#pragma unroll
+        for (int k = 0; k < NT; ++k)
+            if (k >= (tid >> 5)) rfT[k * Q + tid] = fast_exp2(fminf(csdt_n[32 * k] - cv, kMaxTileDecayLog2)) * dv;
+    };
 
-    if (NT > 1) wait_vmcnt<2 * DPS>(); else wait_vmcnt<DPS>();
+    issue_csdt(h0);
+    issue_hin(h0);
+    issue_stage(h0, 0, st0, st0 + 512);
+    issue_stage(h0, 1, st1, st1 + 512);
+    issue_stage(h0, 2, st2, st2 + 512);
+    const int it_[2] = {wave, 2 * W - 1 - wave};
+    uint4 cf[2][8];
+    load_c_frags(cf, Cm, b, L, G, g, tok0, it_, hf, l32);
+    wait_vmcnt<0>();
     barrier_lds();
-    csi[0] = cs_s[32 * it_[0] + l32];
-    csi[1] = cs_s[32 * it_[1] + l32];
-    f32x16 acc[2][2];
-    scan_state_term(acc, hs, cf, csi, hf, l32);
-    const XtAddr xa = xt_addr(lane);
-    const uint32_t dkeep = diag_keep_bits(l32, hf);
-    const uint32_t deq = diag_eq_bits(l32, hf);
+    make_tables();
+    barrier_lds();
+
+    for (int hi = 0; hi < hg; ++hi) {
+        const int h = h0 + hi;
+        // Lane-dependent values are re-derived every head: laundering the
+        // lane index keeps the compiler from hoisting every LDS address of
+        // the unrolled block loop out of the head loop (which costs far more
+        // registers than recomputing them).
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int hf_o = lane_o >> 5, l32_o = lane_o & 31;
+        const XtAddr xa = xt_addr(lane_o);
+        const uint32_t dkeep = diag_keep_bits(l32_o, hf_o);
+        const uint32_t deq = diag_eq_bits(l32_o, hf_o);
+        const bool more = hi + 1 < hg;
+        const float Dh = D ? D[h] : 0.0f;
+        float csi[2];
+        TileF tf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int i0 = 32 * it_[t];
+            const float cref = cs_s[i0];
+            csi[t] = cs_s[i0 + l32_o];
+            tf[t].fact = uniform_f(cref - cs_s[i0 + 31]) <= kMaxTileDecayLog2;
+            if (tf[t].fact) {
+                tf[t].colf = fast_exp2(csi[t] - cref);
+                tf[t].sstate = fast_exp2(cref);
+                tf[t].dprime = Dh * fast_exp2(cref - csi[t]);
+            } else {
+                tf[t].colf = 1.0f;
+                tf[t].sstate = fast_exp2(csi[t]);
+                tf[t].dprime = 0.0f;
+            }
+        }
+        f32x16 acc[2][2];
+        scan_state_term(acc, hs, cf, tf, hf_o, l32_o);
 
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-        uint4* bst = (jt % 3 == 0) ? bs0 : ((jt % 3 == 1) ? bs1 : bs2);
-        uint4* xst = (jt % 3 == 0) ? xs0 : ((jt % 3 == 1) ? xs1 : xs2);
-        if (jt + 1 < NT) wait_vmcnt<DPS>(); else wait_vmcnt<0>();
-        barrier_lds();
-        if (jt + 2 < NT) {
-            uint4* nb = ((jt + 2) % 3 == 0) ? bs0 : (((jt + 2) % 3 == 1) ? bs1 : bs2);
-            uint4* nx = ((jt + 2) % 3 == 0) ? xs0 : (((jt + 2) % 3 == 1) ? xs1 : xs2);
-            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + 2), L, xbase, xstride, bbase, bstride, nb, nx);
+        for (int jt = 0; jt < NT; ++jt) {
+            // stage jt has landed once only the operations issued after it
+            // are outstanding (the first head's stages 0..2 were waited for
+            // in full before the loop)
+            if (more) wait_vmcnt_n(scan_ops_after(NT, jt, true, DPS, DH, DC, NY));
+            else wait_vmcnt_n(scan_ops_after(NT, jt, false, DPS, DH, DC, NY));
+            barrier_lds();
+            uint4* nst = ring4(jt + 3, st0, st1, st2, st3);
+            if (jt + 3 < NT) {
+                issue_stage(h, jt + 3, nst, nst + 512);
+            } else if (more) {
+                issue_stage(h + 1, jt + 3 - NT, nst, nst + 512);
+            }
+            if (jt == 0 && more) {
+                issue_hin(h + 1);
+                issue_csdt(h + 1);
+            }
+            uint4* cst = ring4(jt, st0, st1, st2, st3);
+            scan_block<Q>(acc, jt, cst, cst + 512, cs_s,
+                          dt_s, rfT, cf, csi, it_, tf, Dh, xa, hf_o, l32_o, dkeep, deq);
         }
-        scan_block(acc, jt, bst, xst, cs_s, dt_s, rf_s, cf, csi, it_, Dh, xa, hf, l32, dkeep, deq);
+        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+            y + (((int64_t)b * L + tok0) * H + h) * P, (short)0, yrecord, 0x00020000);
+        scan_store_y(acc, tf, yrs, rowbytes, it_, hf_o, l32_o);
+        if (more) {
+            // the next head's carried state and cs/dt rows (issued at step 0)
+            wait_vmcnt_n((NT - 1) * DPS + NY);
+            barrier_lds();
+            make_tables();
+            barrier_lds();
+        }
     }
-    scan_store_y(acc, y, b, L, H, h, tok0, it_, hf, l32, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -467,6 +620,30 @@ static void launch_generic_t(const Dims& d, const void* x, const void* B, const 
     else launch_generic<T, 32>(d, x, B, C, cs, dtc, Hin, D, y, stream);
 }
 
+// Heads per workgroup of the matrix-core kernel: a divisor of the heads per
+// group (they share C) chosen so that the grid fills whole rounds of the
+// machine (two workgroups per CU), with a small charge per workgroup for
+// its start-up copies.
+static int scan_heads_per_workgroup(const Dims& d) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const double slots = 2.0 * cus;
+    const int64_t hpg = d.nheads / d.ngroups;
+    const double items = (double)d.batch * (double)d.nchunks * (double)d.nheads;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int64_t hg = 1; hg <= hpg && hg <= 64; ++hg) {
+        if (hpg % hg) continue;
+        const double rounds = std::ceil(items / (double)hg / slots);
+        const double cost = rounds * ((double)hg + 0.5);
+        if (cost < best_cost - 1e-9) { best_cost = cost; best = (int)hg; }
+    }
+    return best;
+}
+
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream) {
@@ -477,13 +654,11 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         const bf16_t* hb = static_cast<const bf16_t*>(Hin);
         bf16_t* yb = static_cast<bf16_t*>(y);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
-        {
-            const unsigned blocks = (unsigned)(d.batch * nc * d.nheads);
-            switch (d.chunk) {
-                case 64: chunk_scan_mfma_kernel<64><<<blocks, 64, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
-                case 128: chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
-                default: chunk_scan_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc); break;
-            }
+        const int hg = scan_heads_per_workgroup(d);
+        const unsigned blocks = (unsigned)(d.batch * nc * (d.nheads / hg));
+        switch (d.chunk) {
+            case 128: chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg); break;
+            default: chunk_scan_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg); break;
         }
     } else if (dtype == 1) {
         launch_generic_t<bf16_t>(d, x, B, C, cs, dtc, Hin, D, y, stream);

@@ -11,12 +11,11 @@
 // Matrix-core kernel (bf16 storage, P = 64, N = 128): M = P, N = N, K = the
 // chunk's tokens, with v_mfma_f32_32x32x16_bf16 and fp32 accumulation.  Both
 // operands are token-major in memory while the instruction wants the K index
-// (tokens) contiguous per lane, so every 8 x 8 block of (tokens x columns) is
-// loaded as eight 16-byte rows, transposed in registers and written to LDS
-// with one 16-byte store per column.  LDS rows are 64 tokens (128 B); the
-// 16-byte block index is XOR-swizzled with (row ^ row/8) & 7 so that both
-// the transposing stores and the operand loads touch 8 distinct block
-// columns.  w_j x_j is formed in fp32 and rounded once to bf16.
+// (tokens) contiguous per lane: 32-token blocks of B and x are copied
+// straight into LDS (lds_pipe.h) and read back transposed with
+// ds_read_b64_tr_b16, which hands each lane 4 consecutive tokens of one
+// column.  w_j is applied to the B fragment in fp32 and the product rounded
+// once to bf16.
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): tiles of 32 tokens in
 // LDS, fp32 FMA on the vector units.
@@ -226,8 +225,10 @@ static void launch_generic_t(const Dims& d, const void* x, const void* B, const 
 }
 
 bool mfma_path(int32_t dtype, const Dims& d) {
+    // chunk-relative y offsets of the scan kernel's buffer stores fit 31 bits
     return dtype == 1 && d.headdim == 64 && d.dstate == 128 &&
-           (d.chunk == 64 || d.chunk == 128 || d.chunk == 256);
+           (d.chunk == 128 || d.chunk == 256) &&
+           (double)d.chunk * (double)d.nheads * (double)d.headdim * 2.0 < 2147483647.0;
 }
 
 bool generic_path(const Dims& d) {

@@ -1,13 +1,16 @@
 // lds_pipe.h -- gfx950 helpers for staging tiles into LDS without registers
 // and reading MFMA operands out of them.
 //
-//  * dma16(): global_load_lds_dwordx4 -- each lane copies 16 bytes from its
-//    own global address into LDS at (wave-uniform base) + 16 * lane.  The
-//    copies count in vmcnt like loads; they are waited for with an explicit
-//    s_waitcnt vmcnt(n) and made visible to the workgroup with s_barrier.
-//    Pipeline buffers are distinct __shared__ arrays selected with
-//    compile-time indices, so the compiler can tell an outstanding copy into
-//    one buffer from a read of another and does not force vmcnt(0).
+//  * dma16() / dma4(): global_load_lds_dwordx4 / _dword -- each lane copies
+//    16 (4) bytes from (wave-uniform global base) + (its 32-bit offset) into
+//    LDS at (wave-uniform LDS base) + 16 (4) * lane.  The copies count in
+//    vmcnt like loads; they are waited for with an explicit s_waitcnt
+//    vmcnt(n) and made visible to the workgroup with s_barrier.  They are
+//    issued from asm (no register results; the "memory" clobber keeps LDS
+//    accesses on their side of the issue): the compiler then never waits
+//    for them on its own -- it cannot tell every LDS read from a copy in
+//    flight and would otherwise drain all copies before such reads -- and
+//    the waits written here are the only ones that order them.
 //  * tr16(): ds_read_b64_tr_b16 -- within each group of 16 lanes, lane i
 //    receives element (i % 4) of the 4-element (8-byte) rows addressed by
 //    lanes 4k + i/4, k = 0..3.  If lane r of a group addresses row (token)
@@ -31,8 +34,22 @@ namespace ssd {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void dma16(const void* gsrc, SSD_LDS void* ldst) {
-    __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const SSD_LDS void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
+// base: wave-uniform global address; voff: per-lane byte offset; ldst:
+// wave-uniform LDS address of lane 0's 16 bytes.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, SSD_LDS void* ldst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr(ldst))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, SSD_LDS void* ldst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr(ldst))
+                 : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(n): at most n of this wave's vector-memory operations
@@ -65,40 +82,58 @@ __device__ __forceinline__ SSD_LDS T* lds(T* p) {
     return (SSD_LDS T*)(p);
 }
 
-// Chunk swizzles (16-byte chunk index XOR f(row)).
-// x tiles: 128-byte rows of 64 channels, read only through tr16.
-__device__ __forceinline__ int swz_x(int r) { return (r & 8) >> 1; }
-// B tiles: 256-byte rows of 128 state entries, read as rows (ds_read_b128)
-// by the C.B^T product and through tr16 by the chunk-state product.
-__device__ __forceinline__ int swz_b(int r) { return (r & 3) | ((r & 8) >> 1); }
+// Chunk swizzles (16-byte chunk index XOR f(row)).  LDS serves 256 bytes
+// per cycle (64 banks x 4 B): a ds_read_b128 takes 16 lanes per cycle and a
+// ds_read_b64_tr_b16 32 lanes, so each such lane group must touch 16
+// distinct 16-byte bank groups.
+// x tiles: 128-byte rows of 64 channels, read only through tr16; the lane
+// groups read 4 consecutive rows at 4 chunks each, and rows r and r + 2
+// share bank groups unless the second pair moves to the other half-row.
+__device__ __forceinline__ int swz_x(int r) { return ((r >> 1) & 1) << 2; }
+// B tiles: 256-byte rows of 128 state entries, read as rows (ds_read_b128,
+// 16 distinct rows per lane group) by the C.B^T product and through tr16
+// (4 consecutive rows at 4 adjacent chunks) by the chunk-state product: a
+// bijection of the row's low 4 bits whose upper two bits come from r & 3.
+__device__ __forceinline__ int swz_b(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 // Hin tiles: 256-byte rows, read as rows in the permuted order of the
-// carried-state product.
-__device__ __forceinline__ int swz_h(int r) { return (r & 3) | ((r & 16) >> 2); }
+// carried-state product (rows {0..7, 16..23} + 8k per lane group).
+__device__ __forceinline__ int swz_h(int r) { return (r & 7) | ((r & 16) >> 1); }
 
 // Copy a block of 32 tokens of B (32 rows x 256 B) and x (32 rows x
 // 128 B) into one pipeline buffer: 8 + 4 LDS-copy instructions per
 // workgroup, spread over its W waves.  Tokens past the end of the sequence
-// re-read the last token (finite values whose weights are zero).
+// re-read the last token (finite values whose weights are zero).  Addresses
+// are a wave-uniform base (the block's first token, clamped) plus a 32-bit
+// per-lane byte offset, so the copies use the scalar-base addressing form
+// and keep no 64-bit per-lane addresses alive.
 template <int W>
 __device__ __forceinline__ void issue_bx_stage(int wave, int lane, int tokbase, int L,
                                                  const bf16_t* xbase, int64_t xstride,
                                                  const bf16_t* bbase, int64_t bstride,
                                                  uint4* bst, uint4* xst) {
+    asm volatile("" : "+s"(tokbase));   // scalar bases likewise
+    const int tb = min(tokbase, L - 1);
+    const char* bb = reinterpret_cast<const char*>(bbase + (int64_t)tb * bstride);
+    const char* xb = reinterpret_cast<const char*>(xbase + (int64_t)tb * xstride);
+    // Per-lane offsets are formed where the copies are issued: hoisted, the
+    // offsets of every future stage would each hold a register.
+    asm volatile("" : "+v"(lane));
+    const uint32_t bs2 = (uint32_t)bstride * 2u, xs2 = (uint32_t)xstride * 2u;
 #pragma unroll
     for (int i = 0; i < 8 / W; ++i) {
         const int k = wave + i * W;
         const int r = 4 * k + (lane >> 4);
         const int cc = (lane & 15) ^ swz_b(r);
-        const int tok = min(tokbase + r, L - 1);
-        dma16(bbase + tok * bstride + 8 * cc, lds(bst) + k * 64);
+        const uint32_t dr = (uint32_t)(min(tokbase + r, L - 1) - tb);
+        dma16(bb, dr * bs2 + 16u * (uint32_t)cc, lds(bst) + k * 64);
     }
 #pragma unroll
     for (int i = 0; i < 4 / W; ++i) {
         const int k = wave + i * W;
         const int r = 8 * k + (lane >> 3);
         const int cc = (lane & 7) ^ swz_x(r);
-        const int tok = min(tokbase + r, L - 1);
-        dma16(xbase + tok * xstride + 8 * cc, lds(xst) + k * 64);
+        const uint32_t dr = (uint32_t)(min(tokbase + r, L - 1) - tb);
+        dma16(xb, dr * xs2 + 16u * (uint32_t)cc, lds(xst) + k * 64);
     }
 }
 
