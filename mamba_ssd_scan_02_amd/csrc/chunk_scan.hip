@@ -175,16 +175,34 @@ __device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const ui
                                            int l32, uint32_t diag_keep, uint32_t diag_eq) {
     if (it_[1] < jt) return;   // it_[1] >= it_[0]: nothing left for this wave
     const bool act0 = it_[0] >= jt;
-    f32x16 gacc[2] = {f32x16{}, f32x16{}};
+    // G^T tiles.  The branch sits outside the K loop, and the B-row reads
+    // run two steps ahead of the products (the scheduler, short of
+    // registers, would otherwise wait out each read's latency in turn).
+    f32x16 gacc[2];
     {
         const int jr = perm_pi(l32);
+        const uint4* brow = bst + jr * 16;
+        const int sw = swz_b(jr);
+        bf16x8 bq[2];
+        bq[0] = __builtin_bit_cast(bf16x8, brow[hf ^ sw]);
+        bq[1] = __builtin_bit_cast(bf16x8, brow[(2 + hf) ^ sw]);
+        if (act0) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int ch = 2 * kk + hf;
-            const bf16x8 bq = __builtin_bit_cast(bf16x8, bst[jr * 16 + (ch ^ swz_b(jr))]);
-            if (act0)
-                gacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq, __builtin_bit_cast(bf16x8, cf[0][kk]), gacc[0], 0, 0, 0);
-            gacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq, __builtin_bit_cast(bf16x8, cf[1][kk]), gacc[1], 0, 0, 0);
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 cur = bq[kk & 1];
+                if (kk + 2 < 8) bq[kk & 1] = __builtin_bit_cast(bf16x8, brow[(2 * (kk + 2) + hf) ^ sw]);
+                gacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, cf[0][kk]), kk ? gacc[0] : f32x16{}, 0, 0, 0);
+                gacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, cf[1][kk]), kk ? gacc[1] : f32x16{}, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 cur = bq[kk & 1];
+                if (kk + 2 < 8) bq[kk & 1] = __builtin_bit_cast(bf16x8, brow[(2 * (kk + 2) + hf) ^ sw]);
+                gacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, cf[1][kk]), kk ? gacc[1] : f32x16{}, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
@@ -385,19 +403,22 @@ __global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
         dma4(cs + row, 4u * (uint32_t)tid, lds(csdt_n) + 64 * wave);
         dma4(dtc + row, 4u * (uint32_t)tid, lds(csdt_n) + Q + 64 * wave);
     };
+    // per-lane copy offsets, fixed for the whole workgroup
+    const BxOffsets<W> bxo = bx_offsets<W>(wave, lane, xstride, bstride);
+    uint32_t hoff[DH];
+#pragma unroll
+    for (int i = 0; i < DH; ++i) {
+        const int r = 4 * (wave + i * W) + (lane >> 4);
+        hoff[i] = (uint32_t)(r * N + 8 * ((lane & 15) ^ swz_h(r))) * 2u;
+    }
     auto issue_hin = [&](int h) {
         const bf16_t* hsrc = Hin + ((((int64_t)b * H + h) * nc + c) * (int64_t)(P * N));
 #pragma unroll
-        for (int i = 0; i < DH; ++i) {
-            const int k = wave + i * W;
-            const int r = 4 * k + (lane >> 4);
-            const int cc = (lane & 15) ^ swz_h(r);
-            dma16(hsrc, (uint32_t)(r * N + 8 * cc) * 2u, lds(hs) + k * 64);
-        }
+        for (int i = 0; i < DH; ++i) dma16(hsrc, hoff[i], lds(hs) + (wave + i * W) * 64);
     };
     auto issue_stage = [&](int h, int s, uint4* bst, uint4* xst) {
         const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
-        issue_bx_stage<W>(wave, lane, tok0 + 32 * s, L, xbase, xstride, bbase, bstride, bst, xst);
+        issue_bx_stage<W>(wave, lane, tok0 + 32 * s, L, xbase, xstride, bbase, bstride, bxo, bst, xst);
     };
     // rf table and current cs/dt rows from the copied next-head rows.
     auto make_tables = [&]() {

@@ -75,8 +75,9 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
     float w_v = 0.0f;
     if (tid < Q) w_v = fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid];
     asm volatile("" ::: "memory");
-    issue_bx_stage<W>(wave, lane, tok0, L, xbase, xstride, bbase, bstride, bs0, xs0);
-    if (NT > 1) issue_bx_stage<W>(wave, lane, tok0 + 32, L, xbase, xstride, bbase, bstride, bs1, xs1);
+    const BxOffsets<W> bxo = bx_offsets<W>(wave, lane, xstride, bstride);
+    issue_bx_stage<W>(wave, lane, tok0, L, xbase, xstride, bbase, bstride, bxo, bs0, xs0);
+    if (NT > 1) issue_bx_stage<W>(wave, lane, tok0 + 32, L, xbase, xstride, bbase, bstride, bxo, bs1, xs1);
     if (tid < Q) wv[tid] = w_v;
 
     // tr16 addressing: lane r of group grp supplies token row 8*(grp/2) + r/4
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
         if (jt + 2 < NT) {
             uint4* nb = ((jt + 2) % 3 == 0) ? bs0 : (((jt + 2) % 3 == 1) ? bs1 : bs2);
             uint4* nx = ((jt + 2) % 3 == 0) ? xs0 : (((jt + 2) % 3 == 1) ? xs1 : xs2);
-            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + 2), L, xbase, xstride, bbase, bstride, nb, nx);
+            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + 2), L, xbase, xstride, bbase, bstride, bxo, nb, nx);
         }
         const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
         const SSD_LDS char* bb = (const SSD_LDS char*)lds(bst);

@@ -101,23 +101,54 @@ __device__ __forceinline__ int swz_h(int r) { return (r & 7) | ((r & 16) >> 1); 
 
 // Copy a block of 32 tokens of B (32 rows x 256 B) and x (32 rows x
 // 128 B) into one pipeline buffer: 8 + 4 LDS-copy instructions per
-// workgroup, spread over its W waves.  Tokens past the end of the sequence
-// re-read the last token (finite values whose weights are zero).  Addresses
-// are a wave-uniform base (the block's first token, clamped) plus a 32-bit
-// per-lane byte offset, so the copies use the scalar-base addressing form
-// and keep no 64-bit per-lane addresses alive.
+// workgroup, spread over its W waves.  Addresses are a wave-uniform base
+// (the block's first token) plus a 32-bit per-lane byte offset.  The
+// per-lane offsets of whole blocks do not depend on the block and are
+// computed once (BxOffsets); a block that runs past the end of the sequence
+// re-reads the last token instead (finite values whose weights are zero).
+template <int W>
+struct BxOffsets {
+    uint32_t b[8 / W];
+    uint32_t x[4 / W];
+};
+
+template <int W>
+__device__ __forceinline__ BxOffsets<W> bx_offsets(int wave, int lane, int64_t xstride,
+                                                   int64_t bstride) {
+    BxOffsets<W> o;
+#pragma unroll
+    for (int i = 0; i < 8 / W; ++i) {
+        const int r = 4 * (wave + i * W) + (lane >> 4);
+        o.b[i] = (uint32_t)r * (uint32_t)bstride * 2u + 16u * (uint32_t)((lane & 15) ^ swz_b(r));
+    }
+#pragma unroll
+    for (int i = 0; i < 4 / W; ++i) {
+        const int r = 8 * (wave + i * W) + (lane >> 3);
+        o.x[i] = (uint32_t)r * (uint32_t)xstride * 2u + 16u * (uint32_t)((lane & 7) ^ swz_x(r));
+    }
+    return o;
+}
+
 template <int W>
 __device__ __forceinline__ void issue_bx_stage(int wave, int lane, int tokbase, int L,
                                                  const bf16_t* xbase, int64_t xstride,
                                                  const bf16_t* bbase, int64_t bstride,
-                                                 uint4* bst, uint4* xst) {
-    asm volatile("" : "+s"(tokbase));   // scalar bases likewise
+                                                 const BxOffsets<W>& off, uint4* bst,
+                                                 uint4* xst) {
+    // scalar bases are formed here, not hoisted for every future block
+    asm volatile("" : "+s"(tokbase));
+    if (tokbase + 31 < L) {
+        const char* bb = reinterpret_cast<const char*>(bbase + (int64_t)tokbase * bstride);
+        const char* xb = reinterpret_cast<const char*>(xbase + (int64_t)tokbase * xstride);
+#pragma unroll
+        for (int i = 0; i < 8 / W; ++i) dma16(bb, off.b[i], lds(bst) + (wave + i * W) * 64);
+#pragma unroll
+        for (int i = 0; i < 4 / W; ++i) dma16(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
+        return;
+    }
     const int tb = min(tokbase, L - 1);
     const char* bb = reinterpret_cast<const char*>(bbase + (int64_t)tb * bstride);
     const char* xb = reinterpret_cast<const char*>(xbase + (int64_t)tb * xstride);
-    // Per-lane offsets are formed where the copies are issued: hoisted, the
-    // offsets of every future stage would each hold a register.
-    asm volatile("" : "+v"(lane));
     const uint32_t bs2 = (uint32_t)bstride * 2u, xs2 = (uint32_t)xstride * 2u;
 #pragma unroll
     for (int i = 0; i < 8 / W; ++i) {
