@@ -182,6 +182,21 @@ int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t
                           const float* cs, const float* init_state, void* Hin,
                           float* final_state, hipStream_t stream);
 
+/* Hin and final_state straight from x, B, cs and dtc: what ssd_chunk_state
+ * followed by ssd_state_passing compute, in one pass that keeps the running
+ * state on chip and never writes S (the block recurrence of "Il trucco a
+ * blocchi" run as the token recurrence of "Un sistema che riassume il
+ * passato" with one factor per block).  Same arguments, layouts, aliasing
+ * rules (init_state / final_state may be NULL and may alias) and outputs as
+ * that pair.  Matrix-core path only: dtype bf16, headdim 64, dstate 128,
+ * chunk 256; anything else returns SSD_ERR_UNSUPPORTED.  ssd_forward takes
+ * this path by itself when batch * nheads fills the device. */
+int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                       const void* x, const void* B, const float* cs, const float* dtc,
+                       const float* init_state, void* Hin, float* final_state,
+                       hipStream_t stream);
+
 /* y from the chunk's own tokens (masked C.B^T weighted by exp(Acs_i - Acs_j)
  * dt_j, the attention-like quadratic form), the carried state
  * (exp(Acs_i) Hin_c C_i) and D x. */

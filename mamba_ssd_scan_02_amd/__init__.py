@@ -19,6 +19,7 @@ from .ssd import (  # noqa: F401
     ssd_forward,
     ssm_step,
     state_passing,
+    state_scan,
     status_str,
     workspace_bytes,
     workspace_regions,
@@ -26,6 +27,6 @@ from .ssd import (  # noqa: F401
 
 __all__ = [
     "ssd_forward", "ssm_step", "workspace_bytes", "workspace_regions", "chunk_cumsum",
-    "chunk_state", "state_passing", "chunk_scan", "load", "library_path", "abi_version",
+    "chunk_state", "state_passing", "state_scan", "chunk_scan", "load", "library_path", "abi_version",
     "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16",
 ]

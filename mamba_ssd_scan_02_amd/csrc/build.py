@@ -27,6 +27,7 @@ SOURCES = [
     "chunk_state.hip",
     "state_passing.hip",
     "chunk_scan.hip",
+    "state_scan.hip",
     "ssm_step.hip",
     "ssd_api.cpp",
 ]

@@ -45,6 +45,26 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, SSD_LDS v
                  : "v"(voff), "s"(base), "s"(lds_addr(ldst))
                  : "memory", "m0");
 }
+// Bounds-checked forms: offsets at or beyond the record's size read zeros
+// (every lane still issues, so the memory-counter arithmetic stays fixed).
+__device__ __forceinline__ void dma16_rs(__amdgpu_buffer_rsrc_t rs, uint32_t voff, SSD_LDS void* ldst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(lds_addr(ldst))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_rs(__amdgpu_buffer_rsrc_t rs, uint32_t voff, SSD_LDS void* ldst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(lds_addr(ldst))
+                 : "memory", "m0");
+}
+// Raw buffer record over [base, base + bytes) (bytes clamped at 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rs(const void* base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, SSD_LDS void* ldst) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :

@@ -169,6 +169,25 @@ int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t
     return hip_status(ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream));
 }
 
+int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                       const void* x, const void* B, const float* cs, const float* dtc,
+                       const float* init_state, void* Hin, float* final_state,
+                       hipStream_t stream) {
+    Dims d;
+    int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
+    if (st != SSD_OK) return st;
+    size_t es;
+    if (!elem_size(dtype, &es)) return SSD_ERR_UNSUPPORTED;
+    if (!ssd::mfma_path(dtype, d) || d.chunk != 256) return SSD_ERR_UNSUPPORTED;
+    if (!x || !B || !cs || !dtc || !Hin) return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(Hin, 16) || !aligned(cs, 4) ||
+        !aligned(dtc, 4) || (init_state && !aligned(init_state, 16)) ||
+        (final_state && !aligned(final_state, 16)))
+        return SSD_ERR_ALIGN;
+    return hip_status(ssd::launch_state_scan(d, x, B, cs, dtc, init_state, Hin, final_state, stream));
+}
+
 int32_t ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                        const void* x, const void* B, const void* C, const float* cs,
@@ -236,10 +255,15 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
 
     hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream);
     if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream);
-    if (e != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::state_scan_supported(dtype, d)) {
+        e = ssd::launch_state_scan(d, x, B, cs, dtc, init_state, Hin, final_state, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    } else {
+        e = ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        e = ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    }
     e = ssd::launch_chunk_scan(d, dtype, x, B, C, cs, dtc, Hin, D, y, stream);
     return hip_status(e);
 }

@@ -63,6 +63,8 @@ def load():
     lib.ssd_chunk_state.argtypes = [i64] * 7 + [i32] + [vp] * 5 + [vp]
     lib.ssd_state_passing.restype = i32
     lib.ssd_state_passing.argtypes = [i64] * 6 + [i32] + [vp] * 5 + [vp]
+    lib.ssd_state_scan.restype = i32
+    lib.ssd_state_scan.argtypes = [i64] * 7 + [i32] + [vp] * 7 + [vp]
     lib.ssd_chunk_scan.restype = i32
     lib.ssd_chunk_scan.argtypes = [i64] * 7 + [i32] + [vp] * 8 + [vp]
     _lib = lib
@@ -256,6 +258,28 @@ def state_passing(S, cs, seqlen, chunk, dtype, init_state=None, final_state=None
     _check("ssd_state_passing", lib.ssd_state_passing(batch, seqlen, H, P, N, chunk, code, _p(S),
                                                       _p(cs), _p(init_state), _p(Hin),
                                                       _p(final_state), _stream(S.device)))
+    return Hin, final_state
+
+
+def state_scan(x, B, cs, dtc, chunk, init_state=None, final_state=None):
+    """(Hin [batch, H, nc, P, N] in x's dtype, final [batch, H, P, N] fp32) --
+    see ssd_state_scan (chunk state and state passing in one pass)."""
+    lib = load()
+    x = _dev(x, "x")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = n_chunks(L, chunk)
+    _dev(B, "B", x.dtype, (batch, L, G, N), x.device)
+    _dev(cs, "cs", torch.float32, (batch, H, nc, chunk), x.device)
+    _dev(dtc, "dtc", torch.float32, (batch, H, nc, chunk), x.device)
+    _dev(init_state, "init_state", torch.float32, (batch, H, P, N), x.device)
+    Hin = torch.empty((batch, H, nc, P, N), dtype=x.dtype, device=x.device)
+    if final_state is None:
+        final_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device)
+    _dev(final_state, "final_state", torch.float32, (batch, H, P, N), x.device)
+    _check("ssd_state_scan", lib.ssd_state_scan(batch, L, H, P, N, G, chunk, _dtype_code(x), _p(x),
+                                                _p(B), _p(cs), _p(dtc), _p(init_state), _p(Hin),
+                                                _p(final_state), _stream(x.device)))
     return Hin, final_state
 
 

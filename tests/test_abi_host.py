@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("ssd_forward", "ssm_step", "ssd_forward_workspace_bytes", "ssd_status_str",
               "ssd_abi_version", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-              "ssd_chunk_scan"):
+              "ssd_state_scan", "ssd_chunk_scan"):
         assert n in names
 
 
@@ -124,5 +124,18 @@ def test_stage_argument_errors(lib):
                                P(0x4000), None) == NULL
     assert lib.ssd_state_passing(1, 64, 2, 64, 128, 64, 1, P(0x1000), P(0x2000), None, P(0x3008),
                                  None, None) == ALIGN
+    # the one-pass state stage exists for bf16, P = 64, N = 128, chunk 256 only
+    assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 128, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
+                              None, P(0x4000), None, None) == UNSUP
+    assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 256, 0, P(0x1000), P(0x2000), P(0x10), P(0x20),
+                              None, P(0x4000), None, None) == UNSUP
+    assert lib.ssd_state_scan(1, 64, 2, 32, 128, 1, 256, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
+                              None, P(0x4000), None, None) == UNSUP
+    assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 256, 1, P(0x1000), None, P(0x10), P(0x20),
+                              None, P(0x4000), None, None) == NULL
+    assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 256, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
+                              None, P(0x4008), None, None) == ALIGN
+    assert lib.ssd_state_scan(1, 64, 3, 64, 128, 2, 256, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
+                              None, P(0x4000), None, None) == SHAPE
     assert lib.ssd_chunk_scan(1, 64, 2, 64, 128, 1, 64, 1, P(0x1000), P(0x2000), P(0x3000),
                               P(0x10), P(0x20), P(0x8000), None, P(0x1000), None) == ALIAS

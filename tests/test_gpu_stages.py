@@ -94,3 +94,44 @@ def test_stage_intermediates_deterministic():
         outs.append([t.clone() for t in (cs, S, Hin, fin, y)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+SCAN_CASES = [
+    # (name, batch, L, H, G, init, alias init/final)
+    ("one_chunk", 1, 256, 2, 1, True, False),
+    ("ragged", 2, 700, 4, 2, True, False),
+    ("one_token_tail", 1, 513, 3, 1, False, False),
+    ("many_chunks", 1, 2600, 2, 2, True, False),
+    ("short", 1, 40, 2, 1, True, False),
+    ("aliased_state", 1, 600, 2, 1, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_state_scan(case):
+    """The one-pass chunk-state + state-passing kernel against the fp64 stage
+    definitions (Hin and final state), and against the two-kernel GPU path."""
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    name, batch, L, H, G, init, alias = case
+    P, N, Q = 64, 128, 256
+    say(f"[state_scan] {name}")
+    inp = _inputs(21, batch, L, H, P, N, G, "bf16", init=init)
+    g = to_gpu(inp)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
+    st = g["init"].clone() if init else None
+    fin_buf = st if alias else None
+    Hin, fin = ssd.state_scan(g["x"], g["B"], cs, dtc, Q, init_state=st, final_state=fin_buf)
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    S_ref = stages.chunk_state(inp["x"], inp["dt"], inp["B"], Acs, Q)
+    Hin_ref, fin_ref = stages.state_passing(S_ref, Acs, inp["init"] if init else None)
+    e_h = max_rel_err(Hin, Hin_ref)
+    e_f = max_rel_err(fin, fin_ref)
+    say(f"  Hin {e_h:.3e} final {e_f:.3e}")
+    assert e_h < TOL["bf16"] and e_f < TOL["bf16"]
+    # the two-kernel path on the same device intermediates
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
+    Hin2, fin2 = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"] if init else None)
+    assert max_rel_err(Hin, Hin2.cpu().double().numpy()) < TOL["bf16"]
+    assert max_rel_err(fin, fin2.cpu().double().numpy()) < TOL["bf16"]
