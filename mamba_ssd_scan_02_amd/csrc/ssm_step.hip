@@ -8,7 +8,8 @@
 //     y[p] = sum_n C[n] state[p][n] + D_h x[p]
 //
 // The state ([batch][H][P][N] fp32) is read and written once; everything else
-// is tiny, so the kernel is an HBM stream.  One workgroup per (batch, head):
+// is tiny, so the kernel is an HBM stream (non-temporal state accesses: the
+// state of a large batch does not stay in cache from one step to the next).  One workgroup per (batch, head):
 // NV = N/4 lanes cover one row p with float4 accesses (so a wave reads whole
 // 512-byte rows for N = 128), 256/NV rows are in flight per pass, and each
 // thread issues the loads of all its rows before using any of them.  The
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(256) void ssm_step_vec_kernel(float* __restrict__ s
         for (int k = 0; k < RPT; ++k) {
             const int p = p0 + k * RPP;
             if (p < P) {
-                s[k] = *reinterpret_cast<const float4*>(st + (int64_t)p * N);
+                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (int64_t)p * N));
+                s[k] = make_float4(t[0], t[1], t[2], t[3]);
                 xv[k] = Elem<T>::load(xr, p);
             }
         }
@@ -69,7 +71,8 @@ __global__ __launch_bounds__(256) void ssm_step_vec_kernel(float* __restrict__ s
                 v.y = a * v.y + u * bv[1];
                 v.z = a * v.z + u * bv[2];
                 v.w = a * v.w + u * bv[3];
-                *reinterpret_cast<float4*>(st + (int64_t)p * N) = v;
+                const f32x4 tv = {v.x, v.y, v.z, v.w};
+                __builtin_nontemporal_store(tv, reinterpret_cast<f32x4*>(st + (int64_t)p * N));
                 float part = cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w;
 #pragma unroll
                 for (int off = NV / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);

@@ -8,8 +8,9 @@
 //
 // Pure streaming: every state element is independent, one thread owns VW
 // consecutive elements of one (batch, head) and walks the chunks in order.
-// The loads of S for the next PF chunks do not depend on the carried state, so
-// they are kept in flight in a register ring while the chain advances.
+// The loads of S for the next PF chunks (8 to 32, see the launcher) do not
+// depend on the carried state, so they are kept in flight in a register ring
+// while the chain advances.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -20,22 +21,35 @@ struct Vec {
     float v[VW];
 };
 
+// S is read exactly once: non-temporal loads keep it from displacing data
+// that is reused.
 template <int VW>
 __device__ __forceinline__ Vec<VW> load_vec(const float* p, int64_t i) {
     Vec<VW> r;
-    if constexpr (VW == 4) {
-        const float4 t = reinterpret_cast<const float4*>(p)[i];
-        r.v[0] = t.x; r.v[1] = t.y; r.v[2] = t.z; r.v[3] = t.w;
+    if constexpr (VW >= 4) {
+#pragma unroll
+        for (int q = 0; q < VW / 4; ++q) {
+            const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + i * (VW / 4) + q);
+            r.v[4 * q + 0] = t[0]; r.v[4 * q + 1] = t[1]; r.v[4 * q + 2] = t[2]; r.v[4 * q + 3] = t[3];
+        }
+    } else if constexpr (VW == 2) {
+        const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p) + i);
+        r.v[0] = t[0]; r.v[1] = t[1];
     } else {
-        r.v[0] = p[i];
+        r.v[0] = __builtin_nontemporal_load(p + i);
     }
     return r;
 }
 
 template <int VW>
 __device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r) {
-    if constexpr (VW == 4) {
-        reinterpret_cast<float4*>(p)[i] = make_float4(r.v[0], r.v[1], r.v[2], r.v[3]);
+    if constexpr (VW >= 4) {
+#pragma unroll
+        for (int q = 0; q < VW / 4; ++q)
+            reinterpret_cast<float4*>(p)[i * (VW / 4) + q] =
+                make_float4(r.v[4 * q], r.v[4 * q + 1], r.v[4 * q + 2], r.v[4 * q + 3]);
+    } else if constexpr (VW == 2) {
+        reinterpret_cast<float2*>(p)[i] = make_float2(r.v[0], r.v[1]);
     } else {
         p[i] = r.v[0];
     }
@@ -43,11 +57,13 @@ __device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r)
 
 template <int VW>
 __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r) {
-    if constexpr (VW == 4) {
-        uint2 w;
-        w.x = pack_bf16x2(r.v[0], r.v[1]);
-        w.y = pack_bf16x2(r.v[2], r.v[3]);
-        reinterpret_cast<uint2*>(p)[i] = w;
+    if constexpr (VW == 8) {
+        reinterpret_cast<uint4*>(p)[i] = make_uint4(pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3]),
+                                                    pack_bf16x2(r.v[4], r.v[5]), pack_bf16x2(r.v[6], r.v[7]));
+    } else if constexpr (VW == 4) {
+        reinterpret_cast<uint2*>(p)[i] = make_uint2(pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3]));
+    } else if constexpr (VW == 2) {
+        reinterpret_cast<uint32_t*>(p)[i] = pack_bf16x2(r.v[0], r.v[1]);
     } else {
         p[i].bits = (uint16_t)f32_to_bf16_bits(r.v[0]);
     }
@@ -74,59 +90,70 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
     }
     const int64_t base = bh * nc * (int64_t)pnv + off;
     const float* dec = cs + bh * nc * (int64_t)Q + (Q - 1);
+    const int64_t step = (int64_t)pnv * VW;   // floats of one chunk's states
 
     Vec<VW> buf[PF];
     float lg[PF];
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
         if (k < nc) {
-            buf[k] = load_vec<VW>(S, base + (int64_t)k * pnv);
+            buf[k] = load_vec<VW>(S + (base + (int64_t)k * pnv) * VW, 0);
             lg[k] = dec[(int64_t)k * Q];
         }
     }
+    // running pointers (one chunk apart): the prefetch source PF chunks
+    // ahead, its decay, and the Hin destination
+    const float* sp = S + (base + (int64_t)PF * pnv) * VW;
+    const float* dp = dec + (int64_t)PF * Q;
+    HT* hp = Hin + base * VW;
     for (int c0 = 0; c0 < nc; c0 += PF) {
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
             const int c = c0 + k;
             if (c < nc) {
-                const Vec<VW> s = buf[k];
+                const Vec<VW> sv = buf[k];
                 const float a = fast_exp2(lg[k]);
                 if (c + PF < nc) {
-                    buf[k] = load_vec<VW>(S, base + (int64_t)(c + PF) * pnv);
-                    lg[k] = dec[(int64_t)(c + PF) * Q];
+                    buf[k] = load_vec<VW>(sp, 0);
+                    lg[k] = *dp;
                 }
-                store_vec<VW>(Hin, base + (int64_t)c * pnv, h);
+                sp += step;
+                dp += Q;
+                store_vec<VW>(hp, 0, h);
+                hp += step;
 #pragma unroll
-                for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + s.v[e];
+                for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + sv.v[e];
             }
         }
     }
     if (fin) store_vec<VW>(fin, idx, h);
 }
 
-template <typename HT, int VW>
+template <typename HT, int PF, int VW>
 static void launch_sp_vw(const Dims& d, const float* S, const float* cs, const float* init,
                          void* Hin, float* fin, hipStream_t stream) {
     const int pnv = (int)(d.headdim * d.dstate / VW);
     const int64_t total = d.batch * d.nheads * (int64_t)pnv;
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    HT* hin = reinterpret_cast<HT*>(Hin);
-    if (d.nchunks >= 64) {
-        state_passing_kernel<HT, 16, VW><<<blocks, 256, 0, stream>>>(
-            S, cs, init, hin, fin, total, pnv, (int)d.nchunks, (int)d.chunk);
-    } else {
-        state_passing_kernel<HT, 8, VW><<<blocks, 256, 0, stream>>>(
-            S, cs, init, hin, fin, total, pnv, (int)d.nchunks, (int)d.chunk);
-    }
+    state_passing_kernel<HT, PF, VW><<<blocks, 256, 0, stream>>>(
+        S, cs, init, reinterpret_cast<HT*>(Hin), fin, total, pnv, (int)d.nchunks, (int)d.chunk);
 }
 
+// Four elements per thread where P * N allows (measured best at the
+// 2.7B shape: 2, 8 or a one-round grid were slower), with the S loads of
+// the next 8 chunks in flight, 16 for long sequences where fewer threads
+// carry the whole traffic.
 template <typename HT>
 static void launch_sp(const Dims& d, const float* S, const float* cs, const float* init,
                       void* Hin, float* fin, hipStream_t stream) {
-    if ((d.headdim * d.dstate) % 4 == 0)
-        launch_sp_vw<HT, 4>(d, S, cs, init, Hin, fin, stream);
-    else
-        launch_sp_vw<HT, 1>(d, S, cs, init, Hin, fin, stream);
+    const bool longseq = d.nchunks >= 64;
+    if ((d.headdim * d.dstate) % 4 == 0) {
+        if (longseq) launch_sp_vw<HT, 16, 4>(d, S, cs, init, Hin, fin, stream);
+        else launch_sp_vw<HT, 8, 4>(d, S, cs, init, Hin, fin, stream);
+    } else {
+        if (longseq) launch_sp_vw<HT, 32, 1>(d, S, cs, init, Hin, fin, stream);
+        else launch_sp_vw<HT, 8, 1>(d, S, cs, init, Hin, fin, stream);
+    }
 }
 
 hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, const float* cs,
