@@ -395,7 +395,9 @@ __global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
     const int rowbytes = H * P * 2;
-    const int yrecord = (L - 1 - tok0) * rowbytes + P * 2;   // end of the last valid row
+    // end of the chunk's last valid row (within the chunk: Q rows of a
+    // token row's bytes fit 31 bits)
+    const int yrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
 
     // Copies for head h0: cs/dt rows, the carried state, stages 0..2.
     auto issue_csdt = [&](int h) {
@@ -511,6 +513,373 @@ __global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
             barrier_lds();
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Resident kernel (Q = 256): one workgroup of 4 waves per CU and per (batch,
+// chunk, group, run of heads).  G^T = B_j C_i^T does not depend on the head,
+// so each wave forms its 9 causal G^T tiles once (8 products each, operands
+// loaded straight into registers) and keeps them in registers for all of the
+// run's heads; per head only the decay weights, the Y^T products and the
+// carried-state product remain.  A head's x rows, carried state and cs/dt
+// rows (50 KB) are copied into one of three LDS slots two heads ahead, so
+// the workgroup meets once per head.
+//   per wave and head, in issue order: copies for head k + 2 (x 8, Hin 4,
+//   cs 1, dt 1), then the y stores of its two tiles (4 each).
+// Wave w owns i tiles t1 = 7 - w (blocks 0..7-w, processed first) and
+// t0 = w (blocks 0..w): slot s < 8 - w is (t1, s), slot s >= 8 - w is
+// (t0, s - 8 + w).
+namespace rsl {
+constexpr int kX = 0;          // x: 256 rows x 128 B
+constexpr int kH = 32768;      // Hin: 64 rows x 256 B
+constexpr int kCs = 49152;     // cs: 256 floats
+constexpr int kDt = 50176;     // dt: 256 floats
+constexpr int kSlot = 51200;
+constexpr int kCopies = 14;    // LDS-copy instructions per wave per head
+constexpr int kStores = 8;     // y stores per wave per head
+}  // namespace rsl
+
+// Carried-state term of both of the wave's tiles, acc[q][mt] = sstate_q *
+// Hin C_q^T (q = 0: t0, 1: t1).  All 16 Hin fragments are read first: with
+// one wave per SIMD nothing else would cover their latency.
+__device__ __forceinline__ void rs_state_terms(f32x16 (&acc)[2][2], const SSD_LDS uint4* hs,
+                                               const uint4 (&cf)[2][8], const TileF (&tf)[2], int hf,
+                                               int l32) {
+    bf16x8 a[8][2];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int pr = 32 * mt + perm_sigma(l32);
+            const int ch = 2 * kk + hf;
+            a[kk][mt] = __builtin_bit_cast(bf16x8, hs[pr * 16 + (ch ^ swz_h(pr))]);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[q][mt] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][mt], __builtin_bit_cast(bf16x8, cf[q][kk]), acc[q][mt], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[q][mt][r] *= tf[q].sstate;
+}
+
+// LDS operands of one slot: the rf values of the lane's 16 block tokens and
+// the X^T fragments of the block (xq[mt][u]).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+struct SlotIn {
+    f32x4 f[4];
+    u32x4v xq[2][2];
+};
+__device__ __forceinline__ void rs_fetch(SlotIn& o, const SSD_LDS float* rfs, const SSD_LDS char* xb,
+                                         XtAddr xa, int hf) {
+    const SSD_LDS float* rfb = rfs + 8 * hf;
+    o.f[0] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb);
+    o.f[1] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb + 4);
+    o.f[2] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb + 16);
+    o.f[3] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb + 20);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int pc = 32 * mt + xa.qb;
+        const int chk = pc >> 3, sub = (pc & 7) * 2;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r0 = 16 * u + xa.trow0, r1 = r0 + 4;
+            const u32x2v lo = __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (SSD_LDS v4s*)(xb + r0 * 128 + ((chk ^ swz_x(r0)) << 4) + sub)));
+            const u32x2v hi = __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (SSD_LDS v4s*)(xb + r1 * 128 + ((chk ^ swz_x(r1)) << 4) + sub)));
+            o.xq[mt][u] = u32x4v{lo.x, lo.y, hi.x, hi.y};
+        }
+    }
+}
+
+// One slot: weights of the resident G^T tile gt (a block of the tile whose
+// factors are tf; csb/dtb are the block's cs/dt rows), then acc += X^T G~^T.
+__device__ __forceinline__ void rs_slot(f32x16 (&acc)[2], const f32x16& gt, const SlotIn& in,
+                                        const SSD_LDS float* csb, const SSD_LDS float* dtb,
+                                        const TileF& tf, float csi, float Dh, bool dgb, int hf,
+                                        int l32) {
+    uint32_t pk[8];
+    if (tf.fact) {
+        const f32x4 f0 = in.f[0], f1 = in.f[1], f2 = in.f[2], f3 = in.f[3];
+        auto rf = [&](int r) {
+            const f32x4 q = r < 4 ? f0 : (r < 8 ? f1 : (r < 12 ? f2 : f3));
+            return q[r & 3];
+        };
+        if (!dgb) {
+#pragma unroll
+            for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(gt[2 * r2] * rf(2 * r2), gt[2 * r2 + 1] * rf(2 * r2 + 1));
+        } else {
+            // causal mask j <= i and D on j == i; with t = l32 - 8 hf,
+            // register r holds j - 8 hf = 16 (r / 8) + r % 8
+            int tcol = l32 - 8 * hf;
+            asm volatile("" : "+v"(tcol));
+            float v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int jr = 16 * (r >> 3) + (r & 7);
+                const float w = (tcol >= jr) ? gt[r] * rf(r) : 0.0f;
+                v[r] = (tcol == jr) ? w + tf.dprime : w;
+            }
+#pragma unroll
+            for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
+        }
+    } else {
+        // direct weights for a tile with too much decay to factorise
+        const SSD_LDS float* cb = csb + 8 * hf;
+        const SSD_LDS float* db = dtb + 8 * hf;
+        const uint32_t keep = dgb ? diag_keep_bits(l32, hf) : 0xffffu;
+        const uint32_t deq = dgb ? diag_eq_bits(l32, hf) : 0u;
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+            float v2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = 2 * r2 + e;
+                const int jl = 16 * (r >> 3) + (r & 7);
+                const float kf = (float)((keep >> r) & 1u);
+                const float df = (float)((deq >> r) & 1u);
+                v2[e] = gt[r] * (fast_exp2(fminf(csi - cb[jl], 0.0f)) * db[jl] * kf) + Dh * df;
+            }
+            pk[r2] = pack_bf16x2(v2[0], v2[1]);
+        }
+    }
+    const bf16x8 gq[2] = {__builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3])),
+                          __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]))};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            // opaque until here: a bf16-vector value that crosses this
+            // slot's branches would be copied byte by byte at each join
+            u32x4v xv = in.xq[mt][u];
+            asm volatile("" : "+v"(xv));
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), gq[u], acc[mt], 0, 0, 0);
+        }
+}
+
+// y rows of tile t (lane owns token 32 t + l32, channels 32 mt + 16 hf +
+// 0..15) after the final column scale; 4 buffer stores, dropped past the end.
+__device__ __forceinline__ void rs_store(const f32x16 (&acc)[2], float colf, __amdgpu_buffer_rsrc_t yrs,
+                                         int rowbytes, int t, int hf, int l32) {
+    const int off = (32 * t + l32) * rowbytes + 32 * hf;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        uint32_t w8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w8[k] = pack_bf16x2(acc[mt][2 * k] * colf, acc[mt][2 * k + 1] * colf);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v0 = {w8[0], w8[1], w8[2], w8[3]};
+        const u32x4 v1 = {w8[4], w8[5], w8[6], w8[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(v0, yrs, off + 64 * mt, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, yrs, off + 64 * mt + 16, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
+    const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
+    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg,
+    int nsplit) {
+    constexpr int Q = 256, P = 64, N = 128;
+    __shared__ __align__(16) char slots[3 * rsl::kSlot];
+    __shared__ __align__(16) float rfw[4][288];
+
+    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int split = (int)(wg % (uint32_t)nsplit);
+    const uint32_t bcg = wg / (uint32_t)nsplit;
+    const int g = (int)(bcg % (uint32_t)G);
+    const int bc = (int)(bcg / (uint32_t)G);
+    const int c = bc % nc, b = bc / nc;
+    const int hpg = H / G;
+    const int h0 = g * hpg + split * hg;
+    const int cnt = min(hg, hpg - split * hg);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < 4);
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int tok0 = c * Q;
+    const int rowbytes = H * P * 2;
+    // end of the chunk's last valid row, for x and y (within the chunk: Q
+    // rows of a token row's bytes fit 31 bits)
+    const int xrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
+    const int t0 = wave, t1 = 7 - wave;
+    SSD_LDS char* const sl0 = (SSD_LDS char*)lds(slots);
+
+    // Per-lane copy offsets.  x copy i covers rows 32 i + 8 w .. + 7; Hin
+    // copy i rows 16 i + 4 w .. + 3.
+    const uint32_t xo0 = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)rowbytes +
+                         16u * (uint32_t)((lane & 7) ^ swz_x(lane >> 3));
+    const uint32_t xstep = 32u * (uint32_t)rowbytes;
+    uint32_t ho[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * i + 4 * wave + (lane >> 4);
+        ho[i] = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ swz_h(r)));
+    }
+    // Copies of head k into the slot at byte offset so; past the run's last
+    // head they read empty records (zeros, no memory traffic), which keeps
+    // every wait count fixed.
+    auto issue_head = [&](int k, uint32_t so) {
+        const bool real = k < cnt;
+        const int h = h0 + (real ? k : 0);
+        SSD_LDS char* s = sl0 + so;
+        const __amdgpu_buffer_rsrc_t rx =
+            make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, real ? xrecord : 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16_rs(rx, xo0 + (uint32_t)i * xstep, s + rsl::kX + (4 * i + wave) * 1024);
+        const __amdgpu_buffer_rsrc_t rh =
+            make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), real ? P * N * 2 : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_rs(rh, ho[i], s + rsl::kH + (4 * i + wave) * 1024);
+        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+        dma4_rs(make_rs(cs + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kCs + 256 * wave);
+        dma4_rs(make_rs(dtc + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kDt + 256 * wave);
+    };
+
+    issue_head(0, 0);
+    issue_head(1, rsl::kSlot);
+
+    // C fragments of the wave's tiles (cf[0]: t0, cf[1]: t1) and the
+    // resident G^T tiles.
+    const int it_[2] = {t0, t1};
+    uint4 cf[2][8];
+    load_c_frags(cf, Cm, b, L, G, g, tok0, it_, hf, l32);
+    f32x16 gt[9];
+    {
+        // B rows of slot s's block in registers, two slots ahead of the
+        // products (the scheduler would otherwise pull each load down to its
+        // use and wait out the latency slot by slot)
+        const int jr = perm_pi(l32);
+        uint4 bq[3][8];
+        auto load_b = [&](int s, uint4 (&dst)[8]) {
+            const int jt = s < 8 - wave ? s : s - (8 - wave);
+            const int tok = min(tok0 + 32 * jt + jr, L - 1);
+            const bf16_t* brow = Bm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) dst[kk] = *reinterpret_cast<const uint4*>(brow + 16 * kk);
+        };
+        load_b(0, bq[0]);
+        load_b(1, bq[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+            if (s + 2 < 9) load_b(s + 2, bq[(s + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 (&bs)[8] = bq[s % 3];
+            f32x16 a = {};
+            if (s < 8 - wave) {
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bs[kk]), __builtin_bit_cast(bf16x8, cf[1][kk]), a, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bs[kk]), __builtin_bit_cast(bf16x8, cf[0][kk]), a, 0, 0, 0);
+            }
+            gt[s] = a;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    uint32_t so = 0;   // slot of head k
+    for (int k = 0; k < cnt; ++k) {
+        // head k's copies have landed once only those issued after them are
+        // outstanding: (k >= 2) y stores of k - 2, copies of k + 1, y
+        // stores of k - 1
+        if (k == 0) wait_vmcnt<0>();
+        else if (k == 1) wait_vmcnt<rsl::kCopies + rsl::kStores>();
+        else wait_vmcnt<rsl::kCopies + 2 * rsl::kStores>();
+        barrier_lds();
+        // every wave is past head k - 1: its slot takes head k + 2
+        issue_head(k + 2, so >= (uint32_t)rsl::kSlot ? so - rsl::kSlot : so + 2 * rsl::kSlot);
+
+        const int h = h0 + k;
+        const SSD_LDS char* S = sl0 + so;
+        const SSD_LDS float* css = (const SSD_LDS float*)(S + rsl::kCs);
+        const SSD_LDS float* dts = (const SSD_LDS float*)(S + rsl::kDt);
+        const float Dh = D ? D[h] : 0.0f;
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int hf_o = lane_o >> 5, l32_o = lane_o & 31;
+        const XtAddr xa = xt_addr(lane_o);
+
+        // tile factors (tf[0]: t0, tf[1]: t1)
+        float csi[2];
+        TileF tf[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int i0 = 32 * it_[q];
+            const float cref = css[i0];
+            csi[q] = css[i0 + l32_o];
+            tf[q].fact = uniform_f(cref - css[i0 + 31]) <= kMaxTileDecayLog2;
+            if (tf[q].fact) {
+                tf[q].colf = fast_exp2(csi[q] - cref);
+                tf[q].sstate = fast_exp2(cref);
+                tf[q].dprime = Dh * fast_exp2(cref - csi[q]);
+            } else {
+                tf[q].colf = 1.0f;
+                tf[q].sstate = fast_exp2(csi[q]);
+                tf[q].dprime = 0.0f;
+            }
+        }
+        // rf rows of the wave's 9 slots: rfw[s][j] = exp2(cref_t - cs_j) dt_j
+        SSD_LDS float* rfo = lds(&rfw[wave][0]);
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+            const int e = lane_o + 64 * q;
+            if (q < 4 || e < 288) {
+                const int s = e >> 5, j = e & 31;
+                const bool first = s < 8 - wave;
+                const int t = first ? t1 : t0;
+                const int jt = first ? s : s - (8 - wave);
+                rfo[e] = fast_exp2(fminf(css[32 * t] - css[32 * jt + j], kMaxTileDecayLog2)) * dts[32 * jt + j];
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+            y + (((int64_t)b * L + tok0) * H + h) * P, (short)0, xrecord, 0x00020000);
+        f32x16 acc[2][2];
+        rs_state_terms(acc, (const SSD_LDS uint4*)(S + rsl::kH), cf, tf, hf_o, l32_o);
+        // slot s's LDS operands are read while slot s - 1 computes
+        auto slot_jt = [&](int s) { return s < 8 - wave ? s : s - (8 - wave); };
+        SlotIn cur, nxt;
+        rs_fetch(cur, rfo, S + rsl::kX + slot_jt(0) * 4096, xa, hf_o);
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+            if (s + 1 < 9) rs_fetch(nxt, rfo + 32 * (s + 1), S + rsl::kX + slot_jt(s + 1) * 4096, xa, hf_o);
+            __builtin_amdgcn_sched_barrier(0);
+            const int jt = slot_jt(s);
+            if (s < 8 - wave) {
+                rs_slot(acc[1], gt[s], cur, css + 32 * jt, dts + 32 * jt, tf[1], csi[1], Dh,
+                        s == 7 - wave, hf_o, l32_o);
+                if (s == 7 - wave) rs_store(acc[1], tf[1].colf, yrs, rowbytes, t1, hf_o, l32_o);
+            } else {
+                rs_slot(acc[0], gt[s], cur, css + 32 * jt, dts + 32 * jt, tf[0], csi[0], Dh,
+                        s == 8, hf_o, l32_o);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+        }
+        rs_store(acc[0], tf[0].colf, yrs, rowbytes, t0, hf_o, l32_o);
+        so = so + rsl::kSlot == 3 * rsl::kSlot ? 0 : so + rsl::kSlot;
+    }
+    // the copies of the two heads past the end read empty records; nothing
+    // in flight may outlive the workgroup's LDS
+    wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -665,6 +1034,33 @@ static int scan_heads_per_workgroup(const Dims& d) {
     return best;
 }
 
+// Shortest run of heads for which the resident kernel beats the streaming
+// one (measured on the MI355X: 40-head runs gain, 4- and 6-head runs lose).
+constexpr int kResidentMinHeads = 12;
+
+// Heads per workgroup of the resident kernel (one workgroup per CU): a run
+// of hg heads of one group, the group's heads split into nsplit runs, with
+// a start-up charge (the resident tiles, the first copies) of 1.5 heads.
+static void scan_resident_split(const Dims& d, int* hg_out, int* nsplit_out) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const int64_t hpg = d.nheads / d.ngroups;
+    const double units = (double)d.batch * (double)d.nchunks * (double)d.ngroups;
+    int best = (int)hpg;
+    double best_cost = 1e300;
+    for (int64_t hg = 1; hg <= hpg; ++hg) {
+        const int64_t ns = (hpg + hg - 1) / hg;
+        const double rounds = std::ceil(units * (double)ns / (double)cus);
+        const double cost = rounds * ((double)hg + 1.5);
+        if (cost < best_cost - 1e-9) { best_cost = cost; best = (int)hg; }
+    }
+    *hg_out = best;
+    *nsplit_out = (int)((hpg + best - 1) / best);
+}
+
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream) {
@@ -675,6 +1071,18 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         const bf16_t* hb = static_cast<const bf16_t*>(Hin);
         bf16_t* yb = static_cast<bf16_t*>(y);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
+        if (d.chunk == 256) {
+            // the resident kernel pays for its start-up (9 tiles' products
+            // and a pipeline fill) once per run of heads: worth it for long
+            // runs only
+            int hg = 0, nsplit = 0;
+            scan_resident_split(d, &hg, &nsplit);
+            if (hg >= kResidentMinHeads) {
+                const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
+                chunk_scan_resident_kernel<<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg, nsplit);
+                return hipGetLastError();
+            }
+        }
         const int hg = scan_heads_per_workgroup(d);
         const unsigned blocks = (unsigned)(d.batch * nc * (d.nheads / hg));
         switch (d.chunk) {

@@ -133,8 +133,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int p = 8 * (r >> 2) + 4 * hf + (r & 3);
-        Sp[p * N + n] = acc[0][r];
-        Sp[(32 + p) * N + n] = acc[1][r];
+        __builtin_nontemporal_store(acc[0][r], &Sp[p * N + n]);
+        __builtin_nontemporal_store(acc[1][r], &Sp[(32 + p) * N + n]);
     }
 }
 

@@ -81,6 +81,34 @@ def test_stages(case):
     assert e_y < tol
 
 
+def test_chunk_scan_head_runs():
+    """128 (batch, chunk, group) units of 25 heads: the launcher gives each
+    workgroup a run of 13 or 12 heads of one chunk (on a 256-CU part), the
+    path that keeps the C.B^T tiles in registers across a run.  The first and
+    last head of both runs are checked against the oracle over every chunk,
+    including the ragged last one."""
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    batch, L, H, P, N, G, Q = 1, 128 * 256 - 37, 25, 64, 128, 1, 256
+    say("[stages] chunk_scan head runs")
+    inp = _inputs(13, batch, L, H, P, N, G, "bf16")
+    g = to_gpu(inp)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
+    Hin, _ = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"])
+    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], Q).cpu()
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    Hn = Hin.cpu().double().numpy()
+    for h in (0, 12, 13, 24):
+        sl = slice(h, h + 1)
+        y_ref = stages.chunk_scan(inp["x"][:, :, sl], inp["dt"][:, :, sl], inp["B"], inp["C"],
+                                  Acs[:, sl], Hn[:, sl], inp["D"][sl], Q)
+        e = max_rel_err(y[:, :, sl], y_ref)
+        say(f"  head {h}: max rel err {e:.3e}")
+        assert e < TOL["bf16"], (h, e)
+
+
 def test_stage_intermediates_deterministic():
     import mamba_ssd_scan_02_amd as ssd
     inp = _inputs(12, 1, 512, 4, 64, 128, 1, "bf16")
