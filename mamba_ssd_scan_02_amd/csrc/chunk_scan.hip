@@ -310,24 +310,6 @@ __device__ __forceinline__ T* ring4(int k, T* a0, T* a1, T* a2, T* a3) {
     return m == 0 ? a0 : (m == 1 ? a1 : (m == 2 ? a2 : a3));
 }
 
-// s_waitcnt vmcnt(n) for an n that is a constant once the caller's loop is
-// unrolled (the switch folds to one case).
-__device__ __forceinline__ void wait_vmcnt_n(int n) {
-    switch (n) {
-#define SSD_WAIT_CASE(k) case k: wait_vmcnt<k>(); break;
-        SSD_WAIT_CASE(0) SSD_WAIT_CASE(1) SSD_WAIT_CASE(2) SSD_WAIT_CASE(3) SSD_WAIT_CASE(4)
-        SSD_WAIT_CASE(5) SSD_WAIT_CASE(6) SSD_WAIT_CASE(7) SSD_WAIT_CASE(8) SSD_WAIT_CASE(9)
-        SSD_WAIT_CASE(10) SSD_WAIT_CASE(11) SSD_WAIT_CASE(12) SSD_WAIT_CASE(13) SSD_WAIT_CASE(14)
-        SSD_WAIT_CASE(15) SSD_WAIT_CASE(16) SSD_WAIT_CASE(17) SSD_WAIT_CASE(18) SSD_WAIT_CASE(19)
-        SSD_WAIT_CASE(20) SSD_WAIT_CASE(21) SSD_WAIT_CASE(22) SSD_WAIT_CASE(23) SSD_WAIT_CASE(24)
-        SSD_WAIT_CASE(25) SSD_WAIT_CASE(26) SSD_WAIT_CASE(27) SSD_WAIT_CASE(28) SSD_WAIT_CASE(29)
-        SSD_WAIT_CASE(30) SSD_WAIT_CASE(31) SSD_WAIT_CASE(32) SSD_WAIT_CASE(33) SSD_WAIT_CASE(34)
-        SSD_WAIT_CASE(35) SSD_WAIT_CASE(36) SSD_WAIT_CASE(37) SSD_WAIT_CASE(38) SSD_WAIT_CASE(39)
-#undef SSD_WAIT_CASE
-        default: wait_vmcnt<0>(); break;
-    }
-}
-
 // Memory operations a wave issues at loop step k of a head (stage k + 3 of
 // this head or of the next, and at k = 0 the next head's carried state and
 // cs/dt rows).

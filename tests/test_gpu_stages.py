@@ -132,6 +132,7 @@ SCAN_CASES = [
     ("many_chunks", 1, 2600, 2, 2, True, False),
     ("short", 1, 40, 2, 1, True, False),
     ("aliased_state", 1, 600, 2, 1, True, True),
+    ("head_pairs_two_groups", 2, 1000, 8, 2, True, False),
 ]
 
 
