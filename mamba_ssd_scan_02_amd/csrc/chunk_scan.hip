@@ -522,21 +522,23 @@ constexpr int kStores = 8;     // y stores per wave per head
 }  // namespace rsl
 
 // Carried-state term of both of the wave's tiles, acc[q][mt] = sstate_q *
-// Hin C_q^T (q = 0: t0, 1: t1).  All 16 Hin fragments are read first: with
-// one wave per SIMD nothing else would cover their latency.
-__device__ __forceinline__ void rs_state_terms(f32x16 (&acc)[2][2], const SSD_LDS uint4* hs,
-                                               const uint4 (&cf)[2][8], const TileF (&tf)[2], int hf,
-                                               int l32) {
-    bf16x8 a[8][2];
+// Hin C_q^T (q = 0: t0, 1: t1).  The 16 Hin fragments are read at the top
+// of the head (rs_hin_read), ahead of the head's other LDS work: with one
+// wave per SIMD nothing else would cover their latency.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void rs_hin_read(u32x4v (&a)[8][2], const SSD_LDS uint4* hs, int hf, int l32) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int pr = 32 * mt + perm_sigma(l32);
             const int ch = 2 * kk + hf;
-            a[kk][mt] = __builtin_bit_cast(bf16x8, hs[pr * 16 + (ch ^ swz_h(pr))]);
+            a[kk][mt] = *reinterpret_cast<const SSD_LDS u32x4v*>(hs + pr * 16 + (ch ^ swz_h(pr)));
         }
-    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void rs_state_terms(f32x16 (&acc)[2][2], const u32x4v (&a)[8][2],
+                                               const uint4 (&cf)[2][8], const TileF (&tf)[2]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -547,7 +549,7 @@ __device__ __forceinline__ void rs_state_terms(f32x16 (&acc)[2][2], const SSD_LD
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][mt], __builtin_bit_cast(bf16x8, cf[q][kk]), acc[q][mt], 0, 0, 0);
+                acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kk][mt]), __builtin_bit_cast(bf16x8, cf[q][kk]), acc[q][mt], 0, 0, 0);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -556,21 +558,22 @@ __device__ __forceinline__ void rs_state_terms(f32x16 (&acc)[2][2], const SSD_LD
             for (int r = 0; r < 16; ++r) acc[q][mt][r] *= tf[q].sstate;
 }
 
-// LDS operands of one slot: the rf values of the lane's 16 block tokens and
-// the X^T fragments of the block (xq[mt][u]).
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-struct SlotIn {
+// LDS operands of one slot: the rf values of the lane's 16 block tokens
+// (rs_fetch_rf) and the X^T fragments of the block (rs_fetch_x, xq[mt][u]).
+struct SlotRf {
     f32x4 f[4];
+};
+struct SlotX {
     u32x4v xq[2][2];
 };
-__device__ __forceinline__ void rs_fetch(SlotIn& o, const SSD_LDS float* rfs, const SSD_LDS char* xb,
-                                         XtAddr xa, int hf) {
+__device__ __forceinline__ void rs_fetch_rf(SlotRf& o, const SSD_LDS float* rfs, int hf) {
     const SSD_LDS float* rfb = rfs + 8 * hf;
     o.f[0] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb);
     o.f[1] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb + 4);
     o.f[2] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb + 16);
     o.f[3] = *reinterpret_cast<const SSD_LDS f32x4*>(rfb + 20);
+}
+__device__ __forceinline__ void rs_fetch_x(SlotX& o, const SSD_LDS char* xb, XtAddr xa) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         const int pc = 32 * mt + xa.qb;
@@ -587,37 +590,44 @@ __device__ __forceinline__ void rs_fetch(SlotIn& o, const SSD_LDS float* rfs, co
     }
 }
 
-// One slot: weights of the resident G^T tile gt (a block of the tile whose
-// factors are tf; csb/dtb are the block's cs/dt rows), then acc += X^T G~^T.
-__device__ __forceinline__ void rs_slot(f32x16 (&acc)[2], const f32x16& gt, const SlotIn& in,
-                                        const SSD_LDS float* csb, const SSD_LDS float* dtb,
-                                        const TileF& tf, float csi, float Dh, bool dgb, int hf,
-                                        int l32) {
+// Weights of one slot as the B operand of its products (bf16 pairs): the
+// resident G^T tile gt times rf_j (the common case, rs_weights_fast), or,
+// for a diagonal block or a tile with too much decay to factorise, the
+// masked or direct form (rs_weights_special).
+__device__ __forceinline__ void rs_weights_fast(u32x4v (&gq)[2], const f32x16& gt, const SlotRf& in) {
+    auto rf = [&](int r) {
+        const f32x4 q = r < 4 ? in.f[0] : (r < 8 ? in.f[1] : (r < 12 ? in.f[2] : in.f[3]));
+        return q[r & 3];
+    };
+    uint32_t pk[8];
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(gt[2 * r2] * rf(2 * r2), gt[2 * r2 + 1] * rf(2 * r2 + 1));
+    gq[0] = u32x4v{pk[0], pk[1], pk[2], pk[3]};
+    gq[1] = u32x4v{pk[4], pk[5], pk[6], pk[7]};
+}
+__device__ __forceinline__ void rs_weights_special(u32x4v (&gq)[2], const f32x16& gt, const SlotRf& in,
+                                                   const SSD_LDS float* csb, const SSD_LDS float* dtb,
+                                                   const TileF& tf, float csi, float Dh, bool dgb, int hf,
+                                                   int l32) {
     uint32_t pk[8];
     if (tf.fact) {
-        const f32x4 f0 = in.f[0], f1 = in.f[1], f2 = in.f[2], f3 = in.f[3];
+        // diagonal block: causal mask j <= i and D on j == i; with
+        // t = l32 - 8 hf, register r holds j - 8 hf = 16 (r / 8) + r % 8
         auto rf = [&](int r) {
-            const f32x4 q = r < 4 ? f0 : (r < 8 ? f1 : (r < 12 ? f2 : f3));
+            const f32x4 q = r < 4 ? in.f[0] : (r < 8 ? in.f[1] : (r < 12 ? in.f[2] : in.f[3]));
             return q[r & 3];
         };
-        if (!dgb) {
+        int tcol = l32 - 8 * hf;
+        asm volatile("" : "+v"(tcol));
+        float v[16];
 #pragma unroll
-            for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(gt[2 * r2] * rf(2 * r2), gt[2 * r2 + 1] * rf(2 * r2 + 1));
-        } else {
-            // causal mask j <= i and D on j == i; with t = l32 - 8 hf,
-            // register r holds j - 8 hf = 16 (r / 8) + r % 8
-            int tcol = l32 - 8 * hf;
-            asm volatile("" : "+v"(tcol));
-            float v[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int jr = 16 * (r >> 3) + (r & 7);
-                const float w = (tcol >= jr) ? gt[r] * rf(r) : 0.0f;
-                v[r] = (tcol == jr) ? w + tf.dprime : w;
-            }
-#pragma unroll
-            for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
+        for (int r = 0; r < 16; ++r) {
+            const int jr = 16 * (r >> 3) + (r & 7);
+            const float w = (tcol >= jr) ? gt[r] * rf(r) : 0.0f;
+            v[r] = (tcol == jr) ? w + tf.dprime : w;
         }
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
     } else {
         // direct weights for a tile with too much decay to factorise
         const SSD_LDS float* cb = csb + 8 * hf;
@@ -638,18 +648,19 @@ __device__ __forceinline__ void rs_slot(f32x16 (&acc)[2], const f32x16& gt, cons
             pk[r2] = pack_bf16x2(v2[0], v2[1]);
         }
     }
-    const bf16x8 gq[2] = {__builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]))};
+    gq[0] = u32x4v{pk[0], pk[1], pk[2], pk[3]};
+    gq[1] = u32x4v{pk[4], pk[5], pk[6], pk[7]};
+}
+
+// acc += X^T G~^T for one slot (M = P rows in two 32-row tiles, K = the
+// block's 32 tokens).
+__device__ __forceinline__ void rs_products(f32x16 (&acc)[2], const SlotX& x, const u32x4v (&gq)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            // opaque until here: a bf16-vector value that crosses this
-            // slot's branches would be copied byte by byte at each join
-            u32x4v xv = in.xq[mt][u];
-            asm volatile("" : "+v"(xv));
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), gq[u], acc[mt], 0, 0, 0);
-        }
+        for (int u = 0; u < 2; ++u)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x.xq[mt][u]),
+                                                              __builtin_bit_cast(bf16x8, gq[u]), acc[mt], 0, 0, 0);
 }
 
 // y rows of tile t (lane owns token 32 t + l32, channels 32 mt + 16 hf +
@@ -711,24 +722,34 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
         const int r = 16 * i + 4 * wave + (lane >> 4);
         ho[i] = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ swz_h(r)));
     }
-    // Copies of head k into the slot at byte offset so; past the run's last
-    // head they read empty records (zeros, no memory traffic), which keeps
-    // every wait count fixed.
-    auto issue_head = [&](int k, uint32_t so) {
+    // Copies of head k into the slot at byte offset so, in four parts (x
+    // rows 0..127, x rows 128..255, Hin, cs/dt); past the run's last head
+    // they read empty records (zeros, no memory traffic), which keeps every
+    // wait count fixed.
+    auto issue_part = [&](int k, uint32_t so, int part) {
         const bool real = k < cnt;
         const int h = h0 + (real ? k : 0);
         SSD_LDS char* s = sl0 + so;
-        const __amdgpu_buffer_rsrc_t rx =
-            make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, real ? xrecord : 0);
+        if (part < 2) {
+            const __amdgpu_buffer_rsrc_t rx =
+                make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, real ? xrecord : 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dma16_rs(rx, xo0 + (uint32_t)i * xstep, s + rsl::kX + (4 * i + wave) * 1024);
-        const __amdgpu_buffer_rsrc_t rh =
-            make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), real ? P * N * 2 : 0);
+            for (int i = 4 * part; i < 4 * part + 4; ++i)
+                dma16_rs(rx, xo0 + (uint32_t)i * xstep, s + rsl::kX + (4 * i + wave) * 1024);
+        } else if (part == 2) {
+            const __amdgpu_buffer_rsrc_t rh =
+                make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), real ? P * N * 2 : 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_rs(rh, ho[i], s + rsl::kH + (4 * i + wave) * 1024);
-        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-        dma4_rs(make_rs(cs + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kCs + 256 * wave);
-        dma4_rs(make_rs(dtc + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kDt + 256 * wave);
+            for (int i = 0; i < 4; ++i) dma16_rs(rh, ho[i], s + rsl::kH + (4 * i + wave) * 1024);
+        } else {
+            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+            dma4_rs(make_rs(cs + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kCs + 256 * wave);
+            dma4_rs(make_rs(dtc + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kDt + 256 * wave);
+        }
+    };
+    auto issue_head = [&](int k, uint32_t so) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) issue_part(k, so, part);
     };
 
     issue_head(0, 0);
@@ -785,8 +806,10 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
         else if (k == 1) wait_vmcnt<rsl::kCopies + rsl::kStores>();
         else wait_vmcnt<rsl::kCopies + 2 * rsl::kStores>();
         barrier_lds();
-        // every wave is past head k - 1: its slot takes head k + 2
-        issue_head(k + 2, so >= (uint32_t)rsl::kSlot ? so - rsl::kSlot : so + 2 * rsl::kSlot);
+        // every wave is past head k - 1: its slot takes head k + 2, copied in
+        // parts during slots 0..3 (all before this head's first y stores:
+        // the wait counts above hold)
+        const uint32_t so2 = so >= (uint32_t)rsl::kSlot ? so - rsl::kSlot : so + 2 * rsl::kSlot;
 
         const int h = h0 + k;
         const SSD_LDS char* S = sl0 + so;
@@ -797,64 +820,92 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
         asm volatile("" : "+v"(lane_o));
         const int hf_o = lane_o >> 5, l32_o = lane_o & 31;
         const XtAddr xa = xt_addr(lane_o);
+        u32x4v ha[8][2];
+        rs_hin_read(ha, (const SSD_LDS uint4*)(S + rsl::kH), hf_o, l32_o);
 
-        // tile factors (tf[0]: t0, tf[1]: t1)
-        float csi[2];
-        TileF tf[2];
+        // the head's cs/dt reads all at once: the tile factors' (tf[0]: t0,
+        // tf[1]: t1) and those of the rf rows of the wave's 9 slots,
+        // rfw[s][j] = exp2(cref_t - cs_j) dt_j (row entries e = lane + 64 q)
+        float cref[2], ctail[2], csi[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int i0 = 32 * it_[q];
-            const float cref = css[i0];
+            cref[q] = css[i0];
+            ctail[q] = css[i0 + 31];
             csi[q] = css[i0 + l32_o];
-            tf[q].fact = uniform_f(cref - css[i0 + 31]) <= kMaxTileDecayLog2;
+        }
+        float rft[5], rfc[5], rfd[5];
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+            const int e = min(lane_o + 64 * q, 287);
+            const int s = e >> 5, j = e & 31;
+            const bool first = s < 8 - wave;
+            const int t = first ? t1 : t0;
+            const int jt = first ? s : s - (8 - wave);
+            rft[q] = css[32 * t];
+            rfc[q] = css[32 * jt + j];
+            rfd[q] = dts[32 * jt + j];
+        }
+        TileF tf[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            tf[q].fact = uniform_f(cref[q] - ctail[q]) <= kMaxTileDecayLog2;
             if (tf[q].fact) {
-                tf[q].colf = fast_exp2(csi[q] - cref);
-                tf[q].sstate = fast_exp2(cref);
-                tf[q].dprime = Dh * fast_exp2(cref - csi[q]);
+                tf[q].colf = fast_exp2(csi[q] - cref[q]);
+                tf[q].sstate = fast_exp2(cref[q]);
+                tf[q].dprime = Dh * fast_exp2(cref[q] - csi[q]);
             } else {
                 tf[q].colf = 1.0f;
                 tf[q].sstate = fast_exp2(csi[q]);
                 tf[q].dprime = 0.0f;
             }
         }
-        // rf rows of the wave's 9 slots: rfw[s][j] = exp2(cref_t - cs_j) dt_j
         SSD_LDS float* rfo = lds(&rfw[wave][0]);
 #pragma unroll
         for (int q = 0; q < 5; ++q) {
             const int e = lane_o + 64 * q;
-            if (q < 4 || e < 288) {
-                const int s = e >> 5, j = e & 31;
-                const bool first = s < 8 - wave;
-                const int t = first ? t1 : t0;
-                const int jt = first ? s : s - (8 - wave);
-                rfo[e] = fast_exp2(fminf(css[32 * t] - css[32 * jt + j], kMaxTileDecayLog2)) * dts[32 * jt + j];
-            }
+            if (q < 4 || e < 288) rfo[e] = fast_exp2(fminf(rft[q] - rfc[q], kMaxTileDecayLog2)) * rfd[q];
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
         const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
             y + (((int64_t)b * L + tok0) * H + h) * P, (short)0, xrecord, 0x00020000);
         f32x16 acc[2][2];
-        rs_state_terms(acc, (const SSD_LDS uint4*)(S + rsl::kH), cf, tf, hf_o, l32_o);
+        rs_state_terms(acc, ha, cf, tf);
         // slot s's LDS operands are read while slot s - 1 computes
         auto slot_jt = [&](int s) { return s < 8 - wave ? s : s - (8 - wave); };
-        SlotIn cur, nxt;
-        rs_fetch(cur, rfo, S + rsl::kX + slot_jt(0) * 4096, xa, hf_o);
+        SlotRf rc, rn;
+        SlotX xc, xn;
+        rs_fetch_rf(rc, rfo, hf_o);
+        rs_fetch_x(xc, S + rsl::kX + slot_jt(0) * 4096, xa);
 #pragma unroll
         for (int s = 0; s < 9; ++s) {
-            if (s + 1 < 9) rs_fetch(nxt, rfo + 32 * (s + 1), S + rsl::kX + slot_jt(s + 1) * 4096, xa, hf_o);
-            __builtin_amdgcn_sched_barrier(0);
-            const int jt = slot_jt(s);
-            if (s < 8 - wave) {
-                rs_slot(acc[1], gt[s], cur, css + 32 * jt, dts + 32 * jt, tf[1], csi[1], Dh,
-                        s == 7 - wave, hf_o, l32_o);
-                if (s == 7 - wave) rs_store(acc[1], tf[1].colf, yrs, rowbytes, t1, hf_o, l32_o);
-            } else {
-                rs_slot(acc[0], gt[s], cur, css + 32 * jt, dts + 32 * jt, tf[0], csi[0], Dh,
-                        s == 8, hf_o, l32_o);
+            if (s + 1 < 9) {
+                rs_fetch_rf(rn, rfo + 32 * (s + 1), hf_o);
+                rs_fetch_x(xn, S + rsl::kX + slot_jt(s + 1) * 4096, xa);
             }
             __builtin_amdgcn_sched_barrier(0);
-            cur = nxt;
+            const int jt = slot_jt(s);
+            const bool first = s < 8 - wave;
+            const bool dgb = first ? (s == 7 - wave) : (s == 8);
+            u32x4v gq[2];
+            rs_weights_fast(gq, gt[s], rc);
+            if (dgb || !(first ? tf[1].fact : tf[0].fact))
+                rs_weights_special(gq, gt[s], rc, css + 32 * jt, dts + 32 * jt, first ? tf[1] : tf[0],
+                                   first ? csi[1] : csi[0], Dh, dgb, hf_o, l32_o);
+            if (first) {
+                rs_products(acc[1], xc, gq);
+                if (s == 7 - wave) rs_store(acc[1], tf[1].colf, yrs, rowbytes, t1, hf_o, l32_o);
+            } else {
+                rs_products(acc[0], xc, gq);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < 4) {
+                issue_part(k + 2, so2, s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            rc = rn;
+            xc = xn;
         }
         rs_store(acc[0], tf[0].colf, yrs, rowbytes, t0, hf_o, l32_o);
         so = so + rsl::kSlot == 3 * rsl::kSlot ? 0 : so + rsl::kSlot;
