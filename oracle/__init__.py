@@ -63,6 +63,10 @@ def _load():
     lib.oracle_ssm_step.restype = i32
     lib.oracle_ssm_step.argtypes = [i64, i64, i64, i64, i64, i32,
                                     vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_ssd_forward_ex.restype = i32
+    lib.oracle_ssd_forward_ex.argtypes = lib.oracle_ssd_forward.argtypes + [i32]
+    lib.oracle_ssm_step_ex.restype = i32
+    lib.oracle_ssm_step_ex.argtypes = lib.oracle_ssm_step.argtypes + [i32]
     _lib = lib
     return lib
 
@@ -96,7 +100,7 @@ def _ptr(a):
     return None if a is None else ctypes.c_void_p(a.ctypes.data)
 
 
-def forward(x, dt, A, B, C, D=None, init=None, ngroups=None, bh=None, t_range=None):
+def forward(x, dt, A, B, C, D=None, init=None, ngroups=None, bh=None, t_range=None, zoh=False):
     """Sequential fp64 recurrence over whole sequences.
 
     Shapes: x [batch, L, H, P]; dt [batch, L, H]; A [H]; B, C [batch, L, G, N];
@@ -106,9 +110,14 @@ def forward(x, dt, A, B, C, D=None, init=None, ngroups=None, bh=None, t_range=No
     ``bh`` is a list of (b, h) pairs (default: all, b-major); ``t_range`` limits
     which tokens of y are returned (the recurrence always starts at t = 0).
 
+    ``zoh`` selects the exact zero-order-hold input weight expm1(dt A) / A in
+    place of dt (see ssd_oracle.c).
+
     Returns ``(y_sel [n_bh, T, P] float64, final_sel [n_bh, P, N] float64)``.
     Parity: pinned (water tank, convolution form, materialised semiseparable
-    matrix, linear-attention special case, limits, split invariance).
+    matrix, linear-attention special case, limits, split invariance; the
+    zero-order hold by the convolution demo, its steady state and its
+    small-step limit).
     """
     lib = _load()
     xs, kind = _as_storage(x)
@@ -134,25 +143,25 @@ def forward(x, dt, A, B, C, D=None, init=None, ngroups=None, bh=None, t_range=No
     n = bh_arr.shape[0]
     y = np.empty((n, t1 - t0, P), dtype=np.float64)
     fin = np.empty((n, P, N), dtype=np.float64)
-    rc = lib.oracle_ssd_forward(batch, L, H, P, N, G, kind, _ptr(xs), _ptr(dts), _ptr(As),
-                                _ptr(bs), _ptr(cs), _ptr(Ds), _ptr(inits),
-                                _ptr(bh_arr), n, t0, t1, _ptr(y), _ptr(fin))
+    rc = lib.oracle_ssd_forward_ex(batch, L, H, P, N, G, kind, _ptr(xs), _ptr(dts), _ptr(As),
+                                   _ptr(bs), _ptr(cs), _ptr(Ds), _ptr(inits),
+                                   _ptr(bh_arr), n, t0, t1, _ptr(y), _ptr(fin), int(bool(zoh)))
     if rc != 0:
         raise ValueError(f"oracle_ssd_forward failed with {rc}")
     return y, fin
 
 
-def forward_full(x, dt, A, B, C, D=None, init=None):
+def forward_full(x, dt, A, B, C, D=None, init=None, zoh=False):
     """``forward`` over every (b, h), reshaped to y [batch, L, H, P] and
     final [batch, H, P, N] (float64)."""
     xs, _ = _as_storage(x)
     batch, L, H, P = xs.shape
-    y_sel, fin = forward(x, dt, A, B, C, D, init)
+    y_sel, fin = forward(x, dt, A, B, C, D, init, zoh=zoh)
     y = y_sel.reshape(batch, H, L, P).transpose(0, 2, 1, 3)
     return np.ascontiguousarray(y), fin.reshape(batch, H, P, -1)
 
 
-def step(state, x_t, dt_t, A, B_t, C_t, D=None):
+def step(state, x_t, dt_t, A, B_t, C_t, D=None, zoh=False):
     """One decode step of the same recurrence.  ``state`` [batch, H, P, N]
     float64 is updated in place; returns y_t [batch, H, P] float64.
     Parity: pinned (equals ``forward`` run one token at a time, water tank)."""
@@ -170,8 +179,8 @@ def step(state, x_t, dt_t, A, B_t, C_t, D=None):
     assert xs.shape == (batch, H, P) and dts.shape == (batch, H)
     assert bs.shape == (batch, G, N) and cs.shape == (batch, G, N)
     y = np.empty((batch, H, P), dtype=np.float64)
-    rc = lib.oracle_ssm_step(batch, H, P, N, G, kind, _ptr(state), _ptr(xs), _ptr(dts),
-                             _ptr(As), _ptr(bs), _ptr(cs), _ptr(Ds), _ptr(y))
+    rc = lib.oracle_ssm_step_ex(batch, H, P, N, G, kind, _ptr(state), _ptr(xs), _ptr(dts),
+                                _ptr(As), _ptr(bs), _ptr(cs), _ptr(Ds), _ptr(y), int(bool(zoh)))
     if rc != 0:
         raise ValueError(f"oracle_ssm_step failed with {rc}")
     return y

@@ -34,9 +34,18 @@
  *     S[p][n]    = a * S[p][n] + dt[b,t,h] * x[b,t,h,p] * B[b,t,g,n]
  *     y[b,t,h,p] = sum_n C[b,t,g,n] * S[p][n] + D[h] * x[b,t,h,p]
  *
+ * Two discretisations of the input term (the `zoh` flag of the _ex calls):
+ *   0  Bbar = Delta B, the first-order form the selective scan uses (page
+ *      "State Space Model", section "Un sistema che riassume il passato");
+ *   1  the exact zero-order hold Bbar = (Abar - 1) / A B, i.e. the input weight
+ *      expm1(Delta A) / A in place of Delta (Delta itself where A = 0), as in
+ *      the demonstration of the recurrent and convolutional forms on page
+ *      "State Space Models (SSM)" (ultralytics.com glossary), section "Come
+ *      funzionano gli SSM".
+ *
  * Inputs are read in their storage type (fp32, or bf16 bit patterns widened
- * exactly) and every operation after that is fp64 with libm exp().  Compile
- * without -ffast-math.
+ * exactly) and every operation after that is fp64 with libm exp() and
+ * expm1().  Compile without -ffast-math.
  */
 #include <math.h>
 #include <omp.h>
@@ -57,7 +66,14 @@ static double widen(const void* base, int32_t kind, int64_t i) {
     return (double)f;
 }
 
-int32_t oracle_abi_version(void) { return 1; }
+int32_t oracle_abi_version(void) { return 2; }
+
+/* Weight of the input term for one step: Delta, or the zero-order-hold
+ * (exp(Delta A) - 1) / A (Delta where A = 0). */
+static double input_weight(double d, double Ah, int32_t zoh) {
+    if (!zoh || Ah == 0.0) return d;
+    return expm1(d * Ah) / Ah;
+}
 
 /* Threads an OpenMP parallel region of this library will use. */
 int32_t oracle_max_threads(void) {
@@ -85,11 +101,11 @@ int32_t oracle_max_threads(void) {
  *                   Pass 0 and L for the whole sequence.
  * Returns 0, or a negative number for a bad argument.
  */
-int32_t oracle_ssd_forward(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
-                           int32_t in_kind, const void* x, const float* dt, const float* A,
-                           const void* Bm, const void* Cm, const float* D, const float* init,
-                           const int64_t* bh, int64_t n_bh, int64_t t_begin, int64_t t_end,
-                           double* y_sel, double* final_sel) {
+int32_t oracle_ssd_forward_ex(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                              int64_t G, int32_t in_kind, const void* x, const float* dt,
+                              const float* A, const void* Bm, const void* Cm, const float* D,
+                              const float* init, const int64_t* bh, int64_t n_bh, int64_t t_begin,
+                              int64_t t_end, double* y_sel, double* final_sel, int32_t zoh) {
     if (batch < 1 || L < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0) return -1;
     if (!x || !dt || !A || !Bm || !Cm || !bh || n_bh < 0) return -2;
     if (t_begin < 0 || t_end > L || t_begin > t_end) return -3;
@@ -117,14 +133,15 @@ int32_t oracle_ssd_forward(int64_t batch, int64_t L, int64_t H, int64_t P, int64
         for (int64_t t = 0; t < L; ++t) {
             const double d = (double)dt[(b * L + t) * H + h];
             const double a = exp(d * Ah);
+            const double w = input_weight(d, Ah, zoh);
             for (int64_t p = 0; p < P; ++p) xr[p] = widen(x, in_kind, ((b * L + t) * H + h) * P + p);
             for (int64_t n = 0; n < N; ++n) {
                 br[n] = widen(Bm, in_kind, ((b * L + t) * G + g) * N + n);
                 cr[n] = widen(Cm, in_kind, ((b * L + t) * G + g) * N + n);
             }
-            /* state update: S <- a S + dt * x (outer) B */
+            /* state update: S <- a S + w * x (outer) B, w = dt or the ZOH weight */
             for (int64_t p = 0; p < P; ++p) {
-                const double u = d * xr[p];
+                const double u = w * xr[p];
                 double* row = S + p * N;
                 for (int64_t n = 0; n < N; ++n) row[n] = a * row[n] + u * br[n];
             }
@@ -148,6 +165,15 @@ int32_t oracle_ssd_forward(int64_t batch, int64_t L, int64_t H, int64_t P, int64
     return bad ? -4 : 0;
 }
 
+int32_t oracle_ssd_forward(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                           int32_t in_kind, const void* x, const float* dt, const float* A,
+                           const void* Bm, const void* Cm, const float* D, const float* init,
+                           const int64_t* bh, int64_t n_bh, int64_t t_begin, int64_t t_end,
+                           double* y_sel, double* final_sel) {
+    return oracle_ssd_forward_ex(batch, L, H, P, N, G, in_kind, x, dt, A, Bm, Cm, D, init, bh,
+                                 n_bh, t_begin, t_end, y_sel, final_sel, 0);
+}
+
 /*
  * One decode step for every (batch, head): the same update and read-out as a
  * single iteration of the loop above, on a caller-held fp64 state.  This is the
@@ -160,9 +186,10 @@ int32_t oracle_ssd_forward(int64_t batch, int64_t L, int64_t H, int64_t P, int64
  *   B_t, C_t [batch][G][N] kind in_kind  A, D [H] fp32 (D may be NULL)
  *   y_t   [batch][H][P] fp64 output
  */
-int32_t oracle_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G, int32_t in_kind,
-                        double* state, const void* x_t, const float* dt_t, const float* A,
-                        const void* B_t, const void* C_t, const float* D, double* y_t) {
+int32_t oracle_ssm_step_ex(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G,
+                           int32_t in_kind, double* state, const void* x_t, const float* dt_t,
+                           const float* A, const void* B_t, const void* C_t, const float* D,
+                           double* y_t, int32_t zoh) {
     if (batch < 1 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0) return -1;
     if (!state || !x_t || !dt_t || !A || !B_t || !C_t || !y_t) return -2;
     const int64_t heads_per_group = H / G;
@@ -172,11 +199,12 @@ int32_t oracle_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t 
         const int64_t b = bhi / H, h = bhi % H, g = h / heads_per_group;
         const double d = (double)dt_t[b * H + h];
         const double a = exp(d * (double)A[h]);
+        const double w = input_weight(d, (double)A[h], zoh);
         const double Dh = D ? (double)D[h] : 0.0;
         double* S = state + bhi * P * N;
         for (int64_t p = 0; p < P; ++p) {
             const double xp = widen(x_t, in_kind, bhi * P + p);
-            const double u = d * xp;
+            const double u = w * xp;
             double acc = 0.0;
             for (int64_t n = 0; n < N; ++n) {
                 const double bn = widen(B_t, in_kind, (b * G + g) * N + n);
@@ -188,4 +216,10 @@ int32_t oracle_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t 
         }
     }
     return 0;
+}
+
+int32_t oracle_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G, int32_t in_kind,
+                        double* state, const void* x_t, const float* dt_t, const float* A,
+                        const void* B_t, const void* C_t, const float* D, double* y_t) {
+    return oracle_ssm_step_ex(batch, H, P, N, G, in_kind, state, x_t, dt_t, A, B_t, C_t, D, y_t, 0);
 }

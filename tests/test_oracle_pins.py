@@ -421,3 +421,95 @@ def test_chunk_cumsum_definition():
     assert Acs.shape == (1, 1, 3, 4)
     np.testing.assert_allclose(Acs[0, 0, 0], -2 * np.cumsum(dt[0, :4, 0]), rtol=1e-6)
     np.testing.assert_allclose(Acs[0, 0, 2], [-1.8, -3.8, -3.8, -3.8], rtol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Page "State Space Models (SSM)" (ultralytics.com glossary), section "Come
+# funzionano gli SSM": the exact zero-order hold Bbar = (Abar - 1) / A B used
+# by its recurrent-versus-convolutional demonstration.
+# --------------------------------------------------------------------------
+def test_zoh_convolution_demo(oracle_mod):
+    """The demo again, now with the oracle's own zero-order hold: B is handed
+    in as B, and the recurrence must equal the convolution with kernel
+    K_k = C . (Abar^k Bbar), Bbar = (Abar - 1) / A B, built here in fp64."""
+    g = json.loads((GOLDEN / "conv_demo.json").read_text())
+    L, Ns, delta = g["seqlen"], g["state_size"], g["delta"]
+    r = _rng(17)
+    xs = r.standard_normal(L).astype(np.float32)
+    A32 = (-(r.uniform(0, 1, Ns) + 0.5)).astype(np.float32)
+    B32 = r.standard_normal(Ns).astype(np.float32)
+    C32 = r.standard_normal(Ns).astype(np.float32)
+    d32 = np.float32(delta)
+    x = np.repeat(xs[None, :, None, None], Ns, axis=2)
+    dt = np.full((1, L, Ns), d32, np.float32)
+    Bm = np.broadcast_to(B32[None, None, :, None], (1, L, Ns, 1)).copy()
+    Cm = np.broadcast_to(C32[None, None, :, None], (1, L, Ns, 1)).copy()
+    y_sel, _ = oracle_mod.forward(x, dt, A32, Bm, Cm, zoh=True)
+    y_rec = y_sel[:, :, 0].sum(axis=0)
+    A64, d64 = A32.astype(np.float64), np.float64(d32)
+    Abar = np.exp(d64 * A64)
+    Bbar = (Abar - 1.0) / A64 * B32.astype(np.float64)
+    K = np.array([np.sum(C32.astype(np.float64) * Abar ** k * Bbar) for k in range(L)])
+    y_conv = np.array([np.dot(K[: t + 1][::-1], xs[: t + 1].astype(np.float64)) for t in range(L)])
+    assert np.allclose(y_rec, y_conv, atol=g["compared_with_atol"])          # the page's check
+    np.testing.assert_allclose(y_rec, y_conv, rtol=0, atol=1e-12 * np.abs(y_conv).max())
+
+
+@pytest.mark.parametrize("d", [0.05, 0.7, 3.0])
+def test_zoh_step_response_closed_form(oracle_mod, d):
+    """Constant input x = 1 from an empty state, one scalar decay: with the
+    zero-order hold each state entry is -B/A (1 - exp(A d (t + 1))) after
+    token t, so the level it settles at, -B/A, does not depend on the step
+    size (the hold keeps the continuous system's steady state); the plain
+    dt B form settles at d B / (1 - exp(A d)) instead."""
+    L, N = 40, 6
+    r = _rng(18)
+    A = np.array([-0.9], np.float32)
+    Bv = r.standard_normal(N).astype(np.float32)
+    Cv = r.standard_normal(N).astype(np.float32)
+    x = np.ones((1, L, 1, 1), np.float32)
+    dt = np.full((1, L, 1), np.float32(d), np.float32)
+    Bm = np.broadcast_to(Bv[None, None, None, :], (1, L, 1, N)).copy()
+    Cm = np.broadcast_to(Cv[None, None, None, :], (1, L, 1, N)).copy()
+    y, fin = oracle_mod.forward(x, dt, A, Bm, Cm, zoh=True)
+    a64, d64 = float(A[0]), float(np.float32(d))
+    B64, C64 = Bv.astype(np.float64), Cv.astype(np.float64)
+    t = np.arange(L)
+    expect = float(np.dot(C64, -B64 / a64)) * (1.0 - np.exp(a64 * d64 * (t + 1)))
+    np.testing.assert_allclose(y[0, :, 0], expect, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(fin[0, 0], -B64 / a64 * (1.0 - math.exp(a64 * d64 * L)), rtol=1e-13, atol=0)
+    y_e, _ = oracle_mod.forward(x, dt, A, Bm, Cm)
+    steady_e = float(np.dot(C64, B64)) * d64 / (1.0 - math.exp(a64 * d64))
+    assert abs(y_e[0, -1, 0] - steady_e * (1.0 - math.exp(a64 * d64 * L))) < 1e-12
+
+
+def test_zoh_small_step_limit_and_zero_decay(oracle_mod):
+    """expm1(dt A) / A -> dt as dt A -> 0: with A = 0 the two forms are the
+    same computation, and for tiny dt A they agree to about |dt A| / 2."""
+    c = _rand_case(19, L=30, H=3, G=1)
+    c0 = dict(c, A=np.zeros(3, np.float32))
+    y_z, f_z = oracle_mod.forward(**c0, zoh=True)
+    y_e, f_e = oracle_mod.forward(**c0)
+    assert np.array_equal(y_z, y_e) and np.array_equal(f_z, f_e)
+    cs = dict(c, dt=(c["dt"] * 1e-4).astype(np.float32))
+    y_z, _ = oracle_mod.forward(**cs, zoh=True)
+    y_e, _ = oracle_mod.forward(**cs)
+    bound = float(np.max(np.abs(cs["dt"]))) * float(np.max(np.abs(c["A"]))) * np.abs(y_e).max()
+    assert np.max(np.abs(y_z - y_e)) <= bound
+    assert np.max(np.abs(y_z - y_e)) > 0
+
+
+def test_zoh_step_equals_forward(oracle_mod):
+    """The decode step with the zero-order hold, token by token, reproduces the
+    whole-sequence recurrence with it."""
+    c = _rand_case(20, batch=2, L=12, H=4, P=3, N=5, G=2)
+    y_full, fin_full = oracle_mod.forward(**c, zoh=True)
+    state = np.ascontiguousarray(c["init"].astype(np.float64))
+    ys = []
+    for t in range(12):
+        ys.append(oracle_mod.step(state, c["x"][:, t], c["dt"][:, t], c["A"], c["B"][:, t],
+                                  c["C"][:, t], c["D"], zoh=True))
+    y_steps = np.stack(ys, axis=1)                              # b t h p
+    y_ref = y_full.reshape(2, 4, 12, 3).transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(y_steps, y_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(state, fin_full.reshape(2, 4, 3, 5), rtol=0, atol=1e-12)
