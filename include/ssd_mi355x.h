@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 
@@ -132,6 +132,22 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
                     hipStream_t stream);
 
 /*
+ * ssd_forward with the exact zero-order hold for the input term: the step
+ * adds expm1(dt A) / A * x (outer) B instead of dt * x (outer) B (dt itself
+ * where A = 0), i.e. Bbar = (Abar - 1) / A B, the discretisation of the
+ * recurrent-versus-convolutional demonstration on page "State Space Models
+ * (SSM)" (ultralytics.com glossary), section "Come funzionano gli SSM".  The
+ * decay exp(dt A) is unchanged.  Same arguments, layouts, ownership and
+ * errors as ssd_forward; the workspace's dtc region holds the weights.
+ */
+int32_t ssd_forward_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                        const void* x, const float* dt, const float* A, const void* B,
+                        const void* C, const float* D, const float* init_state, void* y,
+                        float* final_state, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * One decode step for every (batch, head) -- one token of generation with a
  * fixed-size state ("State Space Model", "Un sistema che riassume il
  * passato"; tech.tersel.eu, constant memory while generating):
@@ -151,6 +167,16 @@ int32_t ssm_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
                  const float* D, void* y_t, hipStream_t stream);
 
 /*
+ * ssm_step with the exact zero-order hold: state = a state + w x_t (outer)
+ * B_t with w = expm1(dt_t A) / A (dt_t where A = 0), as in ssd_forward_zoh.
+ * Same arguments, layouts and errors as ssm_step.
+ */
+int32_t ssm_step_zoh(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                     int64_t ngroups, int32_t dtype, float* state, const void* x_t,
+                     const float* dt_t, const float* A, const void* B_t, const void* C_t,
+                     const float* D, void* y_t, hipStream_t stream);
+
+/*
  * The four stages of ssd_forward, callable one by one (per-stage checks and
  * timing).  Arrays named after the workspace regions have the layouts given
  * at ssd_forward_workspace_bytes.
@@ -165,6 +191,13 @@ int32_t ssm_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
 int32_t ssd_chunk_cumsum(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
                          const float* dt, const float* A, float* cs, float* dtc,
                          hipStream_t stream);
+
+/* ssd_chunk_cumsum for the zero-order hold: cs as above; dtc holds the
+ * input weight expm1(dt A) / A (dt where A = 0), evaluated in fp64 and
+ * rounded once (see ssd_forward_zoh). */
+int32_t ssd_chunk_cumsum_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
+                             const float* dt, const float* A, float* cs, float* dtc,
+                             hipStream_t stream);
 
 /* S [B][H][nc][P][N]: each chunk's end state from a zero start,
  * S_c[p][n] = sum_j exp(Acs_last - Acs_j) dt_j x_j[p] B_j[n]

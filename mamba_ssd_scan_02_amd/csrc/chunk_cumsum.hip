@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
                                                            const float* __restrict__ A,
                                                            float* __restrict__ cs,
                                                            float* __restrict__ dtc, int L,
-                                                           int H, int Q, int nc) {
+                                                           int H, int Q, int nc, int zoh) {
     __shared__ float dts[256][kCsHeads + 1];
     __shared__ float css[256][kCsHeads + 1];
     __shared__ double segsum[kCsSegs][kCsHeads];
@@ -72,18 +72,20 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
 
     for (int k = 0; k < nh; ++k) {
         const int64_t off = (((int64_t)b * H + h0 + k) * nc + c) * Q;
+        const float ak = A[h0 + k];
         for (int j = tid; j < Q; j += 256) {
             cs[off + j] = css[j][k];
-            dtc[off + j] = dts[j][k];
+            const float d = dts[j][k];
+            dtc[off + j] = zoh ? zoh_weight(d, ak) : d;
         }
     }
 }
 
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* cs,
-                               float* dtc, hipStream_t stream) {
+                               float* dtc, hipStream_t stream, bool zoh) {
     dim3 grid((unsigned)(d.batch * d.nchunks), (unsigned)((d.nheads + kCsHeads - 1) / kCsHeads));
     chunk_cumsum_kernel<<<grid, 256, 0, stream>>>(dt, A, cs, dtc, (int)d.seqlen, (int)d.nheads,
-                                                  (int)d.chunk, (int)d.nchunks);
+                                                  (int)d.chunk, (int)d.nchunks, zoh ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -57,6 +57,14 @@ struct Elem<bf16_t> {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// Exact zero-order-hold input weight (exp(dt a) - 1) / a, dt where a = 0
+// (page "State Space Models (SSM)", ultralytics.com glossary, section "Come
+// funzionano gli SSM": Bbar = (Abar - 1) / A B).  expm1 keeps the small-step
+// case accurate: the weight tends to dt as dt a -> 0.
+__device__ __forceinline__ float zoh_weight(float dt, float a) {
+    return a == 0.0f ? dt : (float)(expm1((double)dt * (double)a) / (double)a);
+}
+
 // Map a linear workgroup id to a logical work item so that the 8 XCDs each
 // receive one contiguous range of the logical order (workgroups are handed to
 // XCDs round-robin).  Identity when the count is not a multiple of 8.

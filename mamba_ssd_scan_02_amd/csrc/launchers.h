@@ -19,7 +19,7 @@ bool mfma_path(int32_t dtype, const Dims& d);
 bool generic_path(const Dims& d);
 
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* cs,
-                               float* dtc, hipStream_t stream);
+                               float* dtc, hipStream_t stream, bool zoh = false);
 
 hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const void* B,
                               const float* cs, const float* dtc, float* S, hipStream_t stream);
@@ -43,6 +43,6 @@ bool ssm_step_supported(int64_t P, int64_t N);
 hipError_t launch_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G,
                            int32_t dtype, float* state, const void* x, const float* dt,
                            const float* A, const void* B, const void* C, const float* D,
-                           void* y, hipStream_t stream);
+                           void* y, hipStream_t stream, bool zoh = false);
 
 }  // namespace ssd

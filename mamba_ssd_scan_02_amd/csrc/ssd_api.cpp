@@ -128,16 +128,28 @@ size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
     return lo.total;
 }
 
-int32_t ssd_chunk_cumsum(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
-                         const float* dt, const float* A, float* cs, float* dtc,
-                         hipStream_t stream) {
+static int32_t chunk_cumsum_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
+                                 const float* dt, const float* A, float* cs, float* dtc,
+                                 hipStream_t stream, bool zoh) {
     Dims d;
     int32_t st = check_dims(batch, seqlen, nheads, 1, 1, 1, chunk, &d);
     if (st != SSD_OK) return st;
     if (chunk > 256) return SSD_ERR_UNSUPPORTED;
     if (!dt || !A || !cs || !dtc) return SSD_ERR_NULL;
     if (!aligned(dt, 4) || !aligned(A, 4) || !aligned(cs, 4) || !aligned(dtc, 4)) return SSD_ERR_ALIGN;
-    return hip_status(ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream));
+    return hip_status(ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, zoh));
+}
+
+int32_t ssd_chunk_cumsum(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
+                         const float* dt, const float* A, float* cs, float* dtc,
+                         hipStream_t stream) {
+    return chunk_cumsum_impl(batch, seqlen, nheads, chunk, dt, A, cs, dtc, stream, false);
+}
+
+int32_t ssd_chunk_cumsum_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
+                             const float* dt, const float* A, float* cs, float* dtc,
+                             hipStream_t stream) {
+    return chunk_cumsum_impl(batch, seqlen, nheads, chunk, dt, A, cs, dtc, stream, true);
 }
 
 int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -211,12 +223,12 @@ int32_t ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     return hip_status(ssd::launch_chunk_scan(d, dtype, x, B, C, cs, dtc, Hin, D, y, stream));
 }
 
-int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
-                    int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
-                    const void* x, const float* dt, const float* A, const void* B,
-                    const void* C, const float* D, const float* init_state, void* y,
-                    float* final_state, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                            const void* x, const float* dt, const float* A, const void* B,
+                            const void* C, const float* D, const float* init_state, void* y,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream, bool zoh) {
     Dims d;
     int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
     if (st != SSD_OK) return st;
@@ -253,7 +265,7 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
     float* S = reinterpret_cast<float*>(ws + lo.S);
     void* Hin = ws + lo.Hin;
 
-    hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream);
+    hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, zoh);
     if (e != hipSuccess) return SSD_ERR_HIP;
     if (ssd::state_scan_supported(dtype, d)) {
         e = ssd::launch_state_scan(d, x, B, cs, dtc, init_state, Hin, final_state, stream);
@@ -268,10 +280,32 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
     return hip_status(e);
 }
 
-int32_t ssm_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
-                 int64_t ngroups, int32_t dtype, float* state, const void* x_t,
-                 const float* dt_t, const float* A, const void* B_t, const void* C_t,
-                 const float* D, void* y_t, hipStream_t stream) {
+int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                    int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                    const void* x, const float* dt, const float* A, const void* B,
+                    const void* C, const float* D, const float* init_state, void* y,
+                    float* final_state, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    return forward_impl(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, x, dt, A,
+                        B, C, D, init_state, y, final_state, workspace, workspace_bytes, stream,
+                        false);
+}
+
+int32_t ssd_forward_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                        const void* x, const float* dt, const float* A, const void* B,
+                        const void* C, const float* D, const float* init_state, void* y,
+                        float* final_state, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    return forward_impl(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, x, dt, A,
+                        B, C, D, init_state, y, final_state, workspace, workspace_bytes, stream,
+                        true);
+}
+
+static int32_t ssm_step_impl(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                             int64_t ngroups, int32_t dtype, float* state, const void* x_t,
+                             const float* dt_t, const float* A, const void* B_t, const void* C_t,
+                             const float* D, void* y_t, hipStream_t stream, bool zoh) {
     if (batch < 1 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1) return SSD_ERR_SHAPE;
     if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
     if ((double)batch * (double)nheads > 2147483647.0 ||
@@ -293,7 +327,23 @@ int32_t ssm_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
         overlaps(state, sbytes, C_t, bcbytes))
         return SSD_ERR_ALIAS;
     return hip_status(ssd::launch_ssm_step(batch, nheads, headdim, dstate, ngroups, dtype, state,
-                                           x_t, dt_t, A, B_t, C_t, D, y_t, stream));
+                                           x_t, dt_t, A, B_t, C_t, D, y_t, stream, zoh));
+}
+
+int32_t ssm_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int64_t ngroups, int32_t dtype, float* state, const void* x_t,
+                 const float* dt_t, const float* A, const void* B_t, const void* C_t,
+                 const float* D, void* y_t, hipStream_t stream) {
+    return ssm_step_impl(batch, nheads, headdim, dstate, ngroups, dtype, state, x_t, dt_t, A, B_t,
+                         C_t, D, y_t, stream, false);
+}
+
+int32_t ssm_step_zoh(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                     int64_t ngroups, int32_t dtype, float* state, const void* x_t,
+                     const float* dt_t, const float* A, const void* B_t, const void* C_t,
+                     const float* D, void* y_t, hipStream_t stream) {
+    return ssm_step_impl(batch, nheads, headdim, dstate, ngroups, dtype, state, x_t, dt_t, A, B_t,
+                         C_t, D, y_t, stream, true);
 }
 
 }  // extern "C"

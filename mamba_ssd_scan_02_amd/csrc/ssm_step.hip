@@ -4,8 +4,11 @@
 // "State Space Model", section "Un sistema che riassume il passato", end of
 // the water-tank passage; page tech.tersel.eu, section "Porownanie zlozonosci
 // obliczeniowej i zachowania pamieci": constant memory per generated token):
-//     a = exp(dt A_h);  state[p][n] = a state[p][n] + dt x[p] B[n];
+//     a = exp(dt A_h);  state[p][n] = a state[p][n] + w x[p] B[n];
 //     y[p] = sum_n C[n] state[p][n] + D_h x[p]
+// with input weight w = dt, or the exact zero-order hold expm1(dt A_h) / A_h
+// (ssm_step_zoh; page "State Space Models (SSM)", section "Come funzionano
+// gli SSM").
 //
 // The state ([batch][H][P][N] fp32) is read and written once; everything else
 // is tiny, so the kernel is an HBM stream (non-temporal state accesses: the
@@ -28,7 +31,7 @@ __global__ __launch_bounds__(256) void ssm_step_vec_kernel(float* __restrict__ s
                                                            const T* __restrict__ Cm,
                                                            const float* __restrict__ D,
                                                            T* __restrict__ y, int H, int P, int N,
-                                                           int hpg, int G) {
+                                                           int hpg, int G, int zoh) {
     constexpr int RPP = 256 / NV;  // rows per pass
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H, g = h / hpg;
@@ -36,6 +39,7 @@ __global__ __launch_bounds__(256) void ssm_step_vec_kernel(float* __restrict__ s
     const int r0 = threadIdx.x / NV;
     const float d = dt[bh];
     const float a = expf(d * A[h]);
+    const float w = zoh ? zoh_weight(d, A[h]) : d;   // input weight
     const float Dh = D ? D[h] : 0.0f;
 
     const int64_t bc = ((int64_t)b * G + g) * N + 4 * n4;
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void ssm_step_vec_kernel(float* __restrict__ s
         for (int k = 0; k < RPT; ++k) {
             const int p = p0 + k * RPP;
             if (p < P) {
-                const float u = d * xv[k];
+                const float u = w * xv[k];
                 float4 v = s[k];
                 v.x = a * v.x + u * bv[0];
                 v.y = a * v.y + u * bv[1];
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void ssm_step_generic_kernel(
     float* __restrict__ state, const T* __restrict__ x, const float* __restrict__ dt,
     const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ D, T* __restrict__ y, int64_t rows, int H, int P, int N, int hpg,
-    int G) {
+    int G, int zoh) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= rows) return;
     const int64_t bh = r / P;
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256) void ssm_step_generic_kernel(
     const float d = dt[bh];
     const float a = expf(d * A[h]);
     const float xp = Elem<T>::load(x, r);
-    const float u = d * xp;
+    const float u = (zoh ? zoh_weight(d, A[h]) : d) * xp;
     const int64_t bc = ((int64_t)b * G + g) * N;
     float* st = state + r * N;
     float acc = 0.0f;
@@ -114,43 +118,43 @@ bool ssm_step_supported(int64_t P, int64_t N) { return P >= 1 && P <= 1024 && N 
 template <typename T, int NV>
 static void launch_vec(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G, float* state,
                        const void* x, const float* dt, const float* A, const void* B,
-                       const void* C, const float* D, void* y, hipStream_t stream) {
+                       const void* C, const float* D, void* y, hipStream_t stream, int zoh) {
     ssm_step_vec_kernel<T, NV, 8><<<(unsigned)(batch * H), 256, 0, stream>>>(
         state, static_cast<const T*>(x), dt, A, static_cast<const T*>(B),
         static_cast<const T*>(C), D, static_cast<T*>(y), (int)H, (int)P, (int)N, (int)(H / G),
-        (int)G);
+        (int)G, zoh);
 }
 
 template <typename T>
 static void launch_typed(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G,
                          float* state, const void* x, const float* dt, const float* A,
                          const void* B, const void* C, const float* D, void* y,
-                         hipStream_t stream) {
+                         hipStream_t stream, int zoh) {
     switch (N) {
-        case 4: launch_vec<T, 1>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
-        case 8: launch_vec<T, 2>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
-        case 16: launch_vec<T, 4>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
-        case 32: launch_vec<T, 8>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
-        case 64: launch_vec<T, 16>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
-        case 128: launch_vec<T, 32>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
-        case 256: launch_vec<T, 64>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream); return;
+        case 4: launch_vec<T, 1>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
+        case 8: launch_vec<T, 2>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
+        case 16: launch_vec<T, 4>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
+        case 32: launch_vec<T, 8>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
+        case 64: launch_vec<T, 16>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
+        case 128: launch_vec<T, 32>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
+        case 256: launch_vec<T, 64>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh); return;
         default: break;
     }
     const int64_t rows = batch * H * P;
     ssm_step_generic_kernel<T><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
         state, static_cast<const T*>(x), dt, A, static_cast<const T*>(B),
         static_cast<const T*>(C), D, static_cast<T*>(y), rows, (int)H, (int)P, (int)N,
-        (int)(H / G), (int)G);
+        (int)(H / G), (int)G, zoh);
 }
 
 hipError_t launch_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64_t G,
                            int32_t dtype, float* state, const void* x, const float* dt,
                            const float* A, const void* B, const void* C, const float* D,
-                           void* y, hipStream_t stream) {
+                           void* y, hipStream_t stream, bool zoh) {
     if (dtype == 1)
-        launch_typed<bf16_t>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream);
+        launch_typed<bf16_t>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh ? 1 : 0);
     else
-        launch_typed<float>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream);
+        launch_typed<float>(batch, H, P, N, G, state, x, dt, A, B, C, D, y, stream, zoh ? 1 : 0);
     return hipGetLastError();
 }
 

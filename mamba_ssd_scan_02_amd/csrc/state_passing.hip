@@ -142,13 +142,22 @@ static void launch_sp_vw(const Dims& d, const float* S, const float* cs, const f
 // Four elements per thread where P * N allows (measured best at the
 // 2.7B shape: 2, 8 or a one-round grid were slower), with the S loads of
 // the next 8 chunks in flight, 16 for long sequences where fewer threads
-// carry the whole traffic.
+// carry the whole traffic, and 48 when the whole grid is at most two waves
+// per SIMD (the registers are there; 2.51 -> 2.37 ms for 32 chains of 4,096
+// chunks, where 32 gained nothing).
 template <typename HT>
 static void launch_sp(const Dims& d, const float* S, const float* cs, const float* init,
                       void* Hin, float* fin, hipStream_t stream) {
     const bool longseq = d.nchunks >= 64;
     if ((d.headdim * d.dstate) % 4 == 0) {
-        if (longseq) launch_sp_vw<HT, 16, 4>(d, S, cs, init, Hin, fin, stream);
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+        }
+        const double waves = (double)d.batch * (double)d.nheads * (double)(d.headdim * d.dstate / 4) / 64.0;
+        if (longseq && waves <= 8.0 * cus) launch_sp_vw<HT, 48, 4>(d, S, cs, init, Hin, fin, stream);
+        else if (longseq) launch_sp_vw<HT, 16, 4>(d, S, cs, init, Hin, fin, stream);
         else launch_sp_vw<HT, 8, 4>(d, S, cs, init, Hin, fin, stream);
     } else {
         if (longseq) launch_sp_vw<HT, 32, 1>(d, S, cs, init, Hin, fin, stream);

@@ -55,10 +55,16 @@ def load():
     lib.ssd_forward_workspace_bytes.argtypes = [i64] * 7 + [i32]
     lib.ssd_forward.restype = i32
     lib.ssd_forward.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp, sz, vp]
+    lib.ssd_forward_zoh.restype = i32
+    lib.ssd_forward_zoh.argtypes = lib.ssd_forward.argtypes
     lib.ssm_step.restype = i32
     lib.ssm_step.argtypes = [i64] * 5 + [i32] + [vp] * 8 + [vp]
+    lib.ssm_step_zoh.restype = i32
+    lib.ssm_step_zoh.argtypes = lib.ssm_step.argtypes
     lib.ssd_chunk_cumsum.restype = i32
     lib.ssd_chunk_cumsum.argtypes = [i64] * 4 + [vp] * 4 + [vp]
+    lib.ssd_chunk_cumsum_zoh.restype = i32
+    lib.ssd_chunk_cumsum_zoh.argtypes = lib.ssd_chunk_cumsum.argtypes
     lib.ssd_chunk_state.restype = i32
     lib.ssd_chunk_state.argtypes = [i64] * 7 + [i32] + [vp] * 5 + [vp]
     lib.ssd_state_passing.restype = i32
@@ -145,7 +151,7 @@ def workspace_regions(batch, seqlen, nheads, headdim, dstate, chunk, dtype):
 
 
 def ssd_forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, *, y=None,
-                final_state=None, workspace=None, return_final_state=True):
+                final_state=None, workspace=None, return_final_state=True, zoh=False):
     """Whole-sequence SSD forward on the GPU.
 
     x [batch, L, H, P] (bf16 | fp32); dt [batch, L, H] fp32; A [H] fp32;
@@ -153,7 +159,8 @@ def ssd_forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, *, y=None,
     init_state [batch, H, P, N] fp32 or None.
     Returns (y [batch, L, H, P] in x's dtype, final_state [batch, H, P, N] fp32
     or None).  ``y``, ``final_state`` and ``workspace`` (uint8, at least
-    workspace_bytes(...)) may be passed in to avoid allocation.
+    workspace_bytes(...)) may be passed in to avoid allocation.  ``zoh``
+    selects the exact zero-order-hold input weight (ssd_forward_zoh).
     """
     lib = load()
     x = _dev(x, "x")
@@ -179,16 +186,18 @@ def ssd_forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, *, y=None,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace", torch.uint8, None, dev)
-    st = lib.ssd_forward(batch, L, H, P, N, G, chunk, code, _p(x), _p(dt), _p(A), _p(B), _p(C),
-                         _p(D), _p(init_state), _p(y), _p(final_state), _p(workspace),
-                         workspace.numel(), _stream(dev))
-    _check("ssd_forward", st)
+    fn = lib.ssd_forward_zoh if zoh else lib.ssd_forward
+    st = fn(batch, L, H, P, N, G, chunk, code, _p(x), _p(dt), _p(A), _p(B), _p(C),
+            _p(D), _p(init_state), _p(y), _p(final_state), _p(workspace),
+            workspace.numel(), _stream(dev))
+    _check("ssd_forward_zoh" if zoh else "ssd_forward", st)
     return y, final_state
 
 
-def ssm_step(state, x_t, dt_t, A, B_t, C_t, D=None, *, y_t=None):
+def ssm_step(state, x_t, dt_t, A, B_t, C_t, D=None, *, y_t=None, zoh=False):
     """One decode step; ``state`` [batch, H, P, N] fp32 is updated in place.
     x_t [batch, H, P]; dt_t [batch, H] fp32; B_t, C_t [batch, G, N].
+    ``zoh`` selects the exact zero-order-hold input weight (ssm_step_zoh).
     Returns y_t [batch, H, P] in x_t's dtype."""
     lib = load()
     state = _dev(state, "state", torch.float32)
@@ -205,15 +214,17 @@ def ssm_step(state, x_t, dt_t, A, B_t, C_t, D=None, *, y_t=None):
     if y_t is None:
         y_t = torch.empty_like(x_t)
     _dev(y_t, "y_t", x_t.dtype, (batch, H, P), dev)
-    st = lib.ssm_step(batch, H, P, N, G, code, _p(state), _p(x_t), _p(dt_t), _p(A), _p(B_t),
-                      _p(C_t), _p(D), _p(y_t), _stream(dev))
-    _check("ssm_step", st)
+    fn = lib.ssm_step_zoh if zoh else lib.ssm_step
+    st = fn(batch, H, P, N, G, code, _p(state), _p(x_t), _p(dt_t), _p(A), _p(B_t),
+            _p(C_t), _p(D), _p(y_t), _stream(dev))
+    _check("ssm_step_zoh" if zoh else "ssm_step", st)
     return y_t
 
 
 # ----------------------------------------------------------------- stages
-def chunk_cumsum(dt, A, chunk):
-    """(cs [batch, H, nc, Q], dtc [batch, H, nc, Q]) -- see ssd_chunk_cumsum."""
+def chunk_cumsum(dt, A, chunk, zoh=False):
+    """(cs [batch, H, nc, Q], dtc [batch, H, nc, Q]) -- see ssd_chunk_cumsum
+    (ssd_chunk_cumsum_zoh when ``zoh``)."""
     lib = load()
     dt = _dev(dt, "dt", torch.float32)
     batch, L, H = dt.shape
@@ -221,8 +232,9 @@ def chunk_cumsum(dt, A, chunk):
     nc = n_chunks(L, chunk)
     cs = torch.empty((batch, H, nc, chunk), dtype=torch.float32, device=dt.device)
     dtc = torch.empty_like(cs)
-    _check("ssd_chunk_cumsum", lib.ssd_chunk_cumsum(batch, L, H, chunk, _p(dt), _p(A), _p(cs),
-                                                    _p(dtc), _stream(dt.device)))
+    fn = lib.ssd_chunk_cumsum_zoh if zoh else lib.ssd_chunk_cumsum
+    _check("ssd_chunk_cumsum", fn(batch, L, H, chunk, _p(dt), _p(A), _p(cs), _p(dtc),
+                                  _stream(dt.device)))
     return cs, dtc
 
 

@@ -21,10 +21,10 @@ def gpu_forward(inp: dict, chunk: int, **kw):
     return y, fin
 
 
-def oracle_forward(inp: dict, bh=None, t_range=None):
+def oracle_forward(inp: dict, bh=None, t_range=None, zoh=False):
     import oracle
     return oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp.get("D"),
-                          inp.get("init"), bh=bh, t_range=t_range)
+                          inp.get("init"), bh=bh, t_range=t_range, zoh=zoh)
 
 
 def select_y(y: torch.Tensor, bh, t_range=None) -> np.ndarray:

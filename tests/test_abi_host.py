@@ -17,7 +17,7 @@ OK, NULL, SHAPE, UNSUP, WS, ALIGN, HIP, ALIAS = range(8)
 def _declared():
     text = HEADER.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_\w+|ssm_step)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssd_\w+|ssm_step\w*)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("ssd_forward", "ssm_step", "ssd_forward_workspace_bytes", "ssd_status_str",
               "ssd_abi_version", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-              "ssd_state_scan", "ssd_chunk_scan"):
+              "ssd_state_scan", "ssd_chunk_scan", "ssd_forward_zoh", "ssd_chunk_cumsum_zoh",
+              "ssm_step_zoh"):
         assert n in names
 
 
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 1
+    assert lib.ssd_abi_version() == 2
     for s in range(8):
         assert lib.ssd_status_str(s)
     assert lib.ssd_status_str(99) == b"unknown status"

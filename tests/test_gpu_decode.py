@@ -12,7 +12,7 @@ from tests.metrics import max_rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _run_decode(spec, check_every_state=False):
+def _run_decode(spec, check_every_state=False, zoh=False):
     import mamba_ssd_scan_02_amd as ssd
     import oracle
     from mamba_ssd_scan_02_amd.workloads import make_decode_static, make_decode_step
@@ -24,8 +24,8 @@ def _run_decode(spec, check_every_state=False):
     for t in range(spec.steps):
         s = make_decode_step(spec, t)
         g = to_gpu(s)
-        y = ssd.ssm_step(state_gpu, g["x"], g["dt"], A, g["B"], g["C"], D)
-        y_ref = oracle.step(state_ref, s["x"], s["dt"], st["A"], s["B"], s["C"], st["D"])
+        y = ssd.ssm_step(state_gpu, g["x"], g["dt"], A, g["B"], g["C"], D, zoh=zoh)
+        y_ref = oracle.step(state_ref, s["x"], s["dt"], st["A"], s["B"], s["C"], st["D"], zoh=zoh)
         e_y = max_rel_err(y, y_ref)
         worst_y = max(worst_y, e_y)
         assert e_y <= TOL[spec.dtype], (t, e_y)
@@ -85,3 +85,14 @@ def test_prefill_then_decode():
         ref = y_ref.reshape(2, 4, L + k, 64)[:, :, t]
         assert max_rel_err(yt, ref) <= TOL["bf16"]
     assert max_rel_err(state, f_ref.reshape(2, 4, 64, 128)) <= TOL["bf16"]
+
+
+def test_decode_zero_order_hold():
+    """ssm_step_zoh (input weight expm1(dt A) / A) against the oracle's step with
+    the same discretisation, on the vector kernel (N = 128) and the generic one
+    (N = 20), with steps large enough that the two discretisations differ."""
+    from mamba_ssd_scan_02_amd.workloads import DECODE_B256
+    for spec in (DECODE_B256.with_(batch=4, steps=12, dt_shift=1.0, a_hi=2.0, name="zoh_n128"),
+                 DECODE_B256.with_(batch=3, steps=9, nheads=6, ngroups=2, headdim=7, dstate=20,
+                                   dtype="f32", dt_shift=1.0, a_hi=2.0, name="zoh_n20_f32")):
+        _run_decode(spec, check_every_state=True, zoh=True)

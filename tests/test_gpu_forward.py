@@ -211,3 +211,32 @@ def test_bitwise_deterministic():
     y1, f1 = gpu_forward(inp, 256)
     y2, f2 = gpu_forward(inp, 256)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+# ------------------------------------------------- exact zero-order hold (f4)
+@pytest.mark.parametrize("case", [
+    # (label, spec changes, chunk, sampled pairs)
+    ("bf16_2p7b_shape", dict(), 256, 12),
+    ("bf16_130m_ragged", dict(batch=2, seqlen=1500), 256, None),
+    ("f32_generic", dict(batch=2, seqlen=300, nheads=3, headdim=16, dstate=16, dtype="f32"), 64, None),
+])
+def test_zero_order_hold_forward(case):
+    """ssd_forward_zoh against the oracle's zero-order-hold recurrence, with
+    steps long enough (dt ~ softplus(z + 1)) that the hold's weight
+    expm1(dt A) / A is far from dt; the plain forward must then differ."""
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M, MAMBA2_2P7B
+    label, changes, chunk, nsample = case
+    base = MAMBA2_2P7B if label.startswith("bf16_2p7b") else MAMBA2_130M
+    spec = base.with_(dt_shift=1.0, **changes)
+    inp = _spec_inputs(spec)
+    batch, L, H, P = inp["x"].shape
+    bh = all_pairs(batch, H) if nsample is None else sample_pairs(batch, H, nsample, seed=9)
+    y, fin = gpu_forward(inp, chunk, zoh=True)
+    y_ref, f_ref = oracle_forward(inp, bh=bh, zoh=True)
+    e_y = max_rel_err(select_y(y, bh), y_ref)
+    e_f = max_rel_err(select_state(fin, bh), f_ref)
+    say(f"[forward zoh] {label}: y {e_y:.3e} final {e_f:.3e}")
+    assert e_y <= TOL[spec.dtype] and e_f <= TOL[spec.dtype], (e_y, e_f)
+    y_plain, _ = gpu_forward(inp, chunk)
+    d = max_rel_err(select_y(y_plain, bh), y_ref)
+    assert d > 10 * TOL[spec.dtype], d

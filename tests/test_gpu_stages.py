@@ -164,3 +164,26 @@ def test_state_scan(case):
     Hin2, fin2 = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"] if init else None)
     assert max_rel_err(Hin, Hin2.cpu().double().numpy()) < TOL["bf16"]
     assert max_rel_err(fin, fin2.cpu().double().numpy()) < TOL["bf16"]
+
+
+def test_chunk_cumsum_zero_order_hold_weights():
+    """ssd_chunk_cumsum_zoh: cs as the plain call, dtc = expm1(dt A) / A from
+    the same fp32 inputs (fp64 on both sides, one rounding), dt where A = 0,
+    0 past the end."""
+    import mamba_ssd_scan_02_amd as ssd
+    inp = _inputs(31, 2, 700, 5, 64, 128, 1, "bf16")
+    inp["A"][2] = 0.0
+    g = to_gpu(inp)
+    cs0, _ = ssd.chunk_cumsum(g["dt"], g["A"], 256)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], 256, zoh=True)
+    assert torch.equal(cs0, cs)
+    dt = inp["dt"].numpy().astype(np.float64)
+    A = inp["A"].numpy().astype(np.float64)
+    w = np.where(A[None, None, :] == 0.0, dt, np.expm1(dt * A[None, None, :]) / np.where(A == 0.0, 1.0, A))
+    nc = 3
+    ref = np.zeros((2, nc * 256, 5))
+    ref[:, :700] = w
+    ref = ref.reshape(2, nc, 256, 5).transpose(0, 3, 1, 2).astype(np.float32)
+    got = dtc.cpu().numpy()
+    np.testing.assert_allclose(got, ref, rtol=2e-7, atol=0)
+    assert np.array_equal(got[:, 2], ref[:, 2])   # A = 0: dt itself
