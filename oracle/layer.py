@@ -4,10 +4,9 @@ TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module; it never imports
 the product path.
 
-Page "State Space Models (SSM)" (ultralytics.com glossary), section "SSM,
-Mamba e la selettivita'": each Mamba block wraps the selective SSM with a
-short convolution and a SiLU gate, and Delta, B, C are functions of the
-current token.  The page gives no further detail; the plainest reading, kept
+Page "State Space Models (SSM)" (ultralytics.com glossary), section "Da S4 a
+Mamba": each Mamba block wraps the selective SSM with a short convolution and
+a SiLU gate, and Delta, B, C are functions of the current token.  The page gives no further detail; the plainest reading, kept
 here and in the GPU path:
 
 * ``causal_conv``: a depthwise causal convolution along the sequence, one
