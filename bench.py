@@ -2,6 +2,7 @@
 """Throughput of the SSD forward scan on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                    [--no-layer]
 
 Profiling helpers (see profiles/):
     python bench.py --profile-loop K      run each kernel K times, plus a
@@ -17,7 +18,9 @@ state, random initial state.  Inputs are resident in HBM before timing starts.
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (its
 algorithmic bytes per launch over its average launch time, measured here with
 HIP events on the stream it runs on), per-kernel figures, the decode step
-(batch 256, 64 steps) and the fp64 CPU oracle timed on a bounded sample.
+(batch 256, 64 steps), the kernels of the block around the scan (short
+convolution + step, gate) at the same shape, and the fp64 CPU oracle timed on
+a bounded sample.
 """
 from __future__ import annotations
 
@@ -44,7 +47,11 @@ KERNEL_SOURCES = {
     "chunk_scan": "chunk_scan.hip",
     "state_scan": "state_scan.hip",
     "ssm_step": "ssm_step.hip",
+    "layer_in": "layer.hip",
+    "layer_dt": "layer.hip",
+    "layer_out": "layer.hip",
 }
+LAYER_K = 4                     # short-convolution width of the block around the scan
 
 
 def log(msg):
@@ -81,6 +88,17 @@ def forward_model(b, L, H, P, N, G, Q):
         "state_scan": 2 * P * N * th + 2 * b * H * nc * P * N,
     }
     return bytes_, flops
+
+
+def layer_model(b, L, H, P, N, G, K):
+    """Algorithmic HBM bytes of the kernels around the scan (bf16 storage):
+    the convolution reads xbc and writes x, B, C; the step kernel reads dt_raw
+    and writes dt; the gate reads y and z and writes out."""
+    tok = b * L
+    cd = H * P + 2 * G * N
+    return {"layer_in": 2 * tok * cd * 2 + cd * (K + 1) * 4,
+            "layer_dt": 2 * tok * H * 4 + H * 4,
+            "layer_out": 3 * tok * H * P * 2}
 
 
 def compulsory_bytes(b, L, H, P, N, G):
@@ -211,6 +229,43 @@ def bench_decode(ssd, steps_warm=3):
     }
 
 
+def bench_layer(ssd, spec, steps=20):
+    """ssd_layer_in (convolution + step kernels) and ssd_layer_out at the
+    forward workload's shape, filter width LAYER_K, timed with HIP events on
+    the stream they run on."""
+    import torch
+    from mamba_ssd_scan_02_amd.workloads import make_layer_inputs
+    b, L, H, P, N, G = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups
+    li = {k: v.cuda() for k, v in make_layer_inputs(spec, LAYER_K).items() if v is not None}
+    x = torch.empty((b, L, H, P), dtype=torch.bfloat16, device="cuda")
+    Bm = torch.empty((b, L, G, N), dtype=torch.bfloat16, device="cuda")
+    Cm = torch.empty_like(Bm)
+    dt = torch.empty((b, L, H), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(x)
+    run_in = lambda: ssd.layer_in(li["xbc"], li["conv_w"], li["conv_b"], li["dt_raw"],
+                                  li["dt_bias"], H, P, G, N, x=x, B=Bm, C=Cm, dt=dt)
+    run_out = lambda: ssd.layer_out(x, li["z"], out=out)
+    res = {}
+    mb = layer_model(b, L, H, P, N, G, LAYER_K)
+    for name, fn, byts in (("layer_in", run_in, mb["layer_in"] + mb["layer_dt"]),
+                           ("layer_out", run_out, mb["layer_out"])):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = byts / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "alg_bytes": byts, "GBps": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    res["kernel_width"] = LAYER_K
+    return res
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences of (batch, head) pairs, in batches of one pair per core, until
@@ -263,6 +318,8 @@ def profile_loop(k: int):
     s0 = {kk: v.cuda() for kk, v in make_decode_step(dspec, 0).items()}
     for _ in range(k):
         ssd.ssm_step(state, s0["x"], s0["dt"], A, s0["B"], s0["C"], D)
+    del g, y, ws
+    bench_layer(ssd, spec, steps=k)
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(k):
@@ -340,6 +397,7 @@ def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str,
                            MAMBA2_2P7B.headdim, MAMBA2_2P7B.dstate, MAMBA2_2P7B.ngroups,
                            MAMBA2_2P7B.chunk)
     alg, _ = forward_model(b, L, H, P, N, G, Q)
+    alg.update(layer_model(b, L, H, P, N, G, LAYER_K))
     db = DECODE_B256
     alg["ssm_step"] = (db.batch * db.nheads * db.headdim * db.dstate * 4 * 2 +
                        db.batch * db.nheads * db.headdim * 2 * 2 + db.batch * db.nheads * 4 +
@@ -377,6 +435,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--profile-loop", type=int, default=0)
     ap.add_argument("--summarize-trace", default=None)
     ap.add_argument("--summarize-counters", nargs=2, default=None)
@@ -467,6 +526,9 @@ def main():
     if not args.no_decode:
         log("[bench] decode")
         out["decode"] = bench_decode(ssd)
+    if not args.no_layer:
+        log("[bench] layer around the scan")
+        out["layer"] = bench_layer(ssd, spec)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(inp)

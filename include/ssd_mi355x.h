@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 
@@ -238,6 +238,47 @@ int32_t ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
                        const void* x, const void* B, const void* C, const float* cs,
                        const float* dtc, const void* Hin, const float* D, void* y,
                        hipStream_t stream);
+
+/*
+ * The steps a Mamba block puts around the scan: each block wraps the selective
+ * SSM with a short convolution and a SiLU gate, and Delta, B, C depend on the
+ * current token (page "State Space Models (SSM)", ultralytics.com glossary,
+ * section "Da S4 a Mamba").  silu(v) = v / (1 + exp(-v)),
+ * softplus(v) = log(1 + exp(v)).
+ *
+ * ssd_layer_in: the scan's inputs from the block's pre-activations.
+ *   xbc     [B][L][Cd] (dtype), Cd = H P + 2 G N: the channels of x (head
+ *           major, then p), then of B (group major, then n), then of C.
+ *   conv_w  fp32 [Cd][K], 1 <= K <= 8: a depthwise causal filter per channel;
+ *           tap k weighs the input K - 1 - k tokens back (tap K - 1 is the
+ *           current token); inputs before the first token are zero.
+ *   conv_b  fp32 [Cd] or NULL (no bias).
+ *   dt_raw  fp32 [B][L][H];  dt_bias fp32 [H] or NULL.
+ *   outputs x [B][L][H][P], B and C [B][L][G][N] (dtype):
+ *           silu(conv_b + filter * xbc) split by channel;
+ *           dt fp32 [B][L][H] = softplus(dt_raw + dt_bias).
+ *   The outputs must not overlap the inputs or each other (SSD_ERR_ALIAS).
+ *   Errors: SSD_ERR_SHAPE (non-positive sizes, H % G, batch > 65535,
+ *   Cd > 134215680, batch L Cd > 1e12),
+ *   SSD_ERR_UNSUPPORTED (dtype, K), SSD_ERR_NULL, SSD_ERR_ALIGN (element
+ *   alignment).  8-channel vector accesses are used when H P and G N are
+ *   multiples of 8 and the arrays are 16-byte aligned.
+ */
+int32_t ssd_layer_in(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t dstate, int64_t ngroups, int64_t kernel_width, int32_t dtype,
+                     const void* xbc, const float* conv_w, const float* conv_b,
+                     const float* dt_raw, const float* dt_bias, void* x, void* B, void* C,
+                     float* dt, hipStream_t stream);
+
+/*
+ * ssd_layer_out: the gate behind the scan, out = y * silu(z), over n
+ * elements of dtype (any layout, the same for all three), 1 <= n <= 1e12.
+ * out may be y (in place) but must not overlap z or partly overlap y.
+ * Errors: SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED (dtype), SSD_ERR_NULL,
+ * SSD_ERR_ALIGN (element alignment), SSD_ERR_ALIAS.
+ */
+int32_t ssd_layer_out(int64_t n, int32_t dtype, const void* y, const void* z, void* out,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,15 +8,19 @@ torch tensors into that ABI.
 from .ssd import (  # noqa: F401
     DTYPE_BF16,
     DTYPE_F32,
+    ABI_VERSION,
     SSDError,
     abi_version,
     chunk_cumsum,
     chunk_scan,
     chunk_state,
+    layer_in,
+    layer_out,
     library_path,
     load,
     n_chunks,
     ssd_forward,
+    ssd_layer,
     ssm_step,
     state_passing,
     state_scan,
@@ -28,5 +32,6 @@ from .ssd import (  # noqa: F401
 __all__ = [
     "ssd_forward", "ssm_step", "workspace_bytes", "workspace_regions", "chunk_cumsum",
     "chunk_state", "state_passing", "state_scan", "chunk_scan", "load", "library_path", "abi_version",
-    "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16",
+    "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16", "ABI_VERSION", "layer_in",
+    "layer_out", "ssd_layer",
 ]

@@ -28,6 +28,7 @@ SOURCES = [
     "state_passing.hip",
     "chunk_scan.hip",
     "state_scan.hip",
+    "layer.hip",
     "ssm_step.hip",
     "ssd_api.cpp",
 ]

@@ -45,4 +45,12 @@ hipError_t launch_ssm_step(int64_t batch, int64_t H, int64_t P, int64_t N, int64
                            const float* A, const void* B, const void* C, const float* D,
                            void* y, hipStream_t stream, bool zoh = false);
 
+// The steps around the scan (layer.hip).
+hipError_t launch_layer_in(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                           int K, int32_t dtype, const void* xbc, const float* w, const float* bias,
+                           const float* dt_raw, const float* dt_bias, void* x, void* B, void* C,
+                           float* dt, hipStream_t stream);
+hipError_t launch_layer_out(int64_t n, int32_t dtype, const void* y, const void* z, void* out,
+                            hipStream_t stream);
+
 }  // namespace ssd

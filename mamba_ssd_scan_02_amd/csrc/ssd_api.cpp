@@ -346,4 +346,50 @@ int32_t ssm_step_zoh(int64_t batch, int64_t nheads, int64_t headdim, int64_t dst
                          C_t, D, y_t, stream, true);
 }
 
+int32_t ssd_layer_in(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t dstate, int64_t ngroups, int64_t kernel_width, int32_t dtype,
+                     const void* xbc, const float* conv_w, const float* conv_b,
+                     const float* dt_raw, const float* dt_bias, void* x, void* B, void* C,
+                     float* dt, hipStream_t stream) {
+    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+        return SSD_ERR_SHAPE;
+    if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
+    size_t es;
+    if (!elem_size(dtype, &es)) return SSD_ERR_UNSUPPORTED;
+    if (kernel_width < 1 || kernel_width > 8) return SSD_ERR_UNSUPPORTED;
+    const double cd = (double)nheads * headdim + 2.0 * (double)ngroups * dstate;
+    if (cd > 8.0 * 65535.0 * 256.0 || (double)batch > 65535.0 || (double)seqlen > 2147483647.0 ||
+        (double)batch * seqlen * cd > 1.0e12)
+        return SSD_ERR_SHAPE;
+    if (!xbc || !conv_w || !dt_raw || !x || !B || !C || !dt) return SSD_ERR_NULL;
+    if (!aligned(xbc, es) || !aligned(x, es) || !aligned(B, es) || !aligned(C, es) ||
+        !aligned(conv_w, 4) || !aligned(dt_raw, 4) || !aligned(dt, 4) ||
+        (conv_b && !aligned(conv_b, 4)) || (dt_bias && !aligned(dt_bias, 4)))
+        return SSD_ERR_ALIGN;
+    const size_t tok = (size_t)batch * (size_t)seqlen;
+    const size_t inb = tok * (size_t)cd * es;
+    const size_t xb = tok * (size_t)(nheads * headdim) * es, bcb = tok * (size_t)(ngroups * dstate) * es;
+    const size_t dtb = tok * (size_t)nheads * 4;
+    if (overlaps(x, xb, xbc, inb) || overlaps(B, bcb, xbc, inb) || overlaps(C, bcb, xbc, inb) ||
+        overlaps(x, xb, B, bcb) || overlaps(x, xb, C, bcb) || overlaps(B, bcb, C, bcb) ||
+        overlaps(dt, dtb, dt_raw, dtb) || overlaps(dt, dtb, xbc, inb))
+        return SSD_ERR_ALIAS;
+    return hip_status(ssd::launch_layer_in(batch, seqlen, nheads, headdim, ngroups, dstate,
+                                           (int)kernel_width, dtype, xbc, conv_w, conv_b, dt_raw,
+                                           dt_bias, x, B, C, dt, stream));
+}
+
+int32_t ssd_layer_out(int64_t n, int32_t dtype, const void* y, const void* z, void* out,
+                      hipStream_t stream) {
+    if (n < 1 || n > (int64_t)1000000000000LL) return SSD_ERR_SHAPE;
+    size_t es;
+    if (!elem_size(dtype, &es)) return SSD_ERR_UNSUPPORTED;
+    if (!y || !z || !out) return SSD_ERR_NULL;
+    if (!aligned(y, es) || !aligned(z, es) || !aligned(out, es)) return SSD_ERR_ALIGN;
+    const size_t bytes = (size_t)n * es;
+    if (overlaps(out, bytes, z, bytes) || (out != y && overlaps(out, bytes, y, bytes)))
+        return SSD_ERR_ALIAS;
+    return hip_status(ssd::launch_layer_out(n, dtype, y, z, out, stream));
+}
+
 }  // extern "C"

@@ -19,6 +19,10 @@ _LIB_PATH = _PKG / "libssd_mi355x.so"
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
+# The SSD_ABI_VERSION this binding was written against; load() refuses a
+# library that reports another one (a stale build).
+ABI_VERSION = 3
+
 _STATUS_OK = 0
 
 _lib = None
@@ -73,6 +77,14 @@ def load():
     lib.ssd_state_scan.argtypes = [i64] * 7 + [i32] + [vp] * 7 + [vp]
     lib.ssd_chunk_scan.restype = i32
     lib.ssd_chunk_scan.argtypes = [i64] * 7 + [i32] + [vp] * 8 + [vp]
+    lib.ssd_layer_in.restype = i32
+    lib.ssd_layer_in.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp]
+    lib.ssd_layer_out.restype = i32
+    lib.ssd_layer_out.argtypes = [i64, i32, vp, vp, vp, vp]
+    got = int(lib.ssd_abi_version())
+    if got != ABI_VERSION:
+        raise RuntimeError(f"{_LIB_PATH} reports ABI version {got}, this binding needs "
+                           f"{ABI_VERSION}: rebuild the library")
     _lib = lib
     return lib
 
@@ -314,3 +326,65 @@ def chunk_scan(x, B, C, cs, dtc, Hin, D, chunk, y=None):
                                                 _p(B), _p(C), _p(cs), _p(dtc), _p(Hin), _p(D),
                                                 _p(y), _stream(x.device)))
     return y
+
+
+# ------------------------------------------------------ block around the scan
+def layer_in(xbc, conv_w, conv_b, dt_raw, dt_bias, nheads, headdim, ngroups, dstate, *,
+             x=None, B=None, C=None, dt=None):
+    """The scan's inputs from a block's pre-activations -- see ssd_layer_in.
+
+    xbc [batch, L, H*P + 2*G*N] (bf16 | fp32); conv_w [channels, K] fp32;
+    conv_b [channels] fp32 or None; dt_raw [batch, L, H] fp32; dt_bias [H]
+    fp32 or None.  Returns (x [batch, L, H, P], B [batch, L, G, N],
+    C [batch, L, G, N] in xbc's dtype, dt [batch, L, H] fp32)."""
+    lib = load()
+    xbc = _dev(xbc, "xbc")
+    dev = xbc.device
+    batch, L, Cd = xbc.shape
+    H, P, G, N = int(nheads), int(headdim), int(ngroups), int(dstate)
+    if Cd != H * P + 2 * G * N:
+        raise ValueError(f"xbc has {Cd} channels, expected H*P + 2*G*N = {H * P + 2 * G * N}")
+    K = conv_w.shape[1] if conv_w.dim() == 2 else -1
+    _dev(conv_w, "conv_w", torch.float32, (Cd, K), dev)
+    _dev(conv_b, "conv_b", torch.float32, (Cd,), dev)
+    _dev(dt_raw, "dt_raw", torch.float32, (batch, L, H), dev)
+    _dev(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    if x is None:
+        x = torch.empty((batch, L, H, P), dtype=xbc.dtype, device=dev)
+    if B is None:
+        B = torch.empty((batch, L, G, N), dtype=xbc.dtype, device=dev)
+    if C is None:
+        C = torch.empty((batch, L, G, N), dtype=xbc.dtype, device=dev)
+    if dt is None:
+        dt = torch.empty((batch, L, H), dtype=torch.float32, device=dev)
+    _dev(x, "x", xbc.dtype, (batch, L, H, P), dev)
+    _dev(B, "B", xbc.dtype, (batch, L, G, N), dev)
+    _dev(C, "C", xbc.dtype, (batch, L, G, N), dev)
+    _dev(dt, "dt", torch.float32, (batch, L, H), dev)
+    _check("ssd_layer_in", lib.ssd_layer_in(batch, L, H, P, N, G, K, _dtype_code(xbc), _p(xbc),
+                                            _p(conv_w), _p(conv_b), _p(dt_raw), _p(dt_bias),
+                                            _p(x), _p(B), _p(C), _p(dt), _stream(dev)))
+    return x, B, C, dt
+
+
+def layer_out(y, z, out=None):
+    """out = y * silu(z), elementwise (``out`` may be ``y``) -- see ssd_layer_out."""
+    lib = load()
+    y = _dev(y, "y")
+    _dev(z, "z", y.dtype, y.shape, y.device)
+    if out is None:
+        out = torch.empty_like(y)
+    _dev(out, "out", y.dtype, y.shape, y.device)
+    _check("ssd_layer_out", lib.ssd_layer_out(y.numel(), _dtype_code(y), _p(y), _p(z), _p(out),
+                                              _stream(y.device)))
+    return out
+
+
+def ssd_layer(xbc, z, dt_raw, A, D, conv_w, conv_b, dt_bias, nheads, headdim, ngroups, dstate,
+              chunk=256, init_state=None, zoh=False):
+    """The block around the scan, each step in the library's kernels:
+    layer_in -> ssd_forward -> layer_out.  z [batch, L, H, P] in xbc's dtype.
+    Returns (out [batch, L, H, P], final_state [batch, H, P, N] fp32)."""
+    x, B, C, dt = layer_in(xbc, conv_w, conv_b, dt_raw, dt_bias, nheads, headdim, ngroups, dstate)
+    y, fin = ssd_forward(x, dt, A, B, C, D, chunk, init_state, zoh=zoh)
+    return layer_out(y, z, out=y), fin

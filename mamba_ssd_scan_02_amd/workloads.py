@@ -12,6 +12,12 @@ standard deviation sqrt(0.1)):
     A = -exp(U(0, a_hi)) per head  B, C ~ N(0, 1/N)       D ~ N(0, 1)
     init ~ N(0, init_var) or absent
 
+Inputs of the block around the scan (``make_layer_inputs``):
+
+    xbc ~ N(0, 1) over the H P + 2 G N channels   z ~ N(0, 1)
+    conv_w ~ N(0, 1/K), conv_b ~ N(0, 0.1)       dt_raw ~ N(dt_shift, 1)
+    dt_bias ~ N(0, 0.1); A, D as above
+
 Seeding: the per-head parameters and the initial state come from
 ``numpy.random.default_rng(seed)``; the per-token arrays are drawn in slabs of
 at most 65,536 tokens, slab ``s`` of batch row ``b`` from
@@ -157,3 +163,38 @@ def make_decode_step(spec: DecodeSpec, t: int) -> dict:
         B=_store(r.standard_normal((Bt, G, N)) * bc_std, spec.dtype),
         C=_store(r.standard_normal((Bt, G, N)) * bc_std, spec.dtype),
     )
+
+
+def make_layer_inputs(spec: ForwardSpec, kernel_width: int = 4) -> dict:
+    """CPU tensors for the block around the scan: xbc [B,L,H*P+2*G*N] and
+    z [B,L,H,P] in the storage type; conv_w [Cd,K], conv_b [Cd], dt_raw [B,L,H],
+    dt_bias [H], A [H], D [H] (f32); init [B,H,P,N] f32 or None.
+
+    Per-head and per-channel parameters come from default_rng([seed, K]) in
+    the order A, D, dt_bias, conv_w, conv_b, init; per-token arrays in slabs
+    from default_rng([seed, K, b, s]) in the order xbc, dt_raw, z."""
+    Bt, L, H, P, N, G = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups
+    K = int(kernel_width)
+    Cd = H * P + 2 * G * N
+    sd = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    rng = np.random.default_rng([spec.seed, K])
+    A, D = _head_params(rng, H, spec.a_hi)
+    dt_bias = rng.standard_normal(H) * math.sqrt(0.1)
+    conv_w = rng.standard_normal((Cd, K)) * math.sqrt(1.0 / K)
+    conv_b = rng.standard_normal(Cd) * math.sqrt(0.1)
+    init = None
+    if spec.init_var > 0:
+        init = _store(rng.standard_normal((Bt, H, P, N)) * math.sqrt(spec.init_var), "f32")
+    xbc = torch.empty((Bt, L, Cd), dtype=sd)
+    dt_raw = torch.empty((Bt, L, H), dtype=torch.float32)
+    z = torch.empty((Bt, L, H, P), dtype=sd)
+    for b in range(Bt):
+        for s, t0 in enumerate(range(0, L, SLAB)):
+            n = min(SLAB, L - t0)
+            r = np.random.default_rng([spec.seed, K, b, s])
+            xbc[b, t0:t0 + n] = _store(r.standard_normal((n, Cd)), spec.dtype)
+            dt_raw[b, t0:t0 + n] = _store(r.standard_normal((n, H)) + spec.dt_shift, "f32")
+            z[b, t0:t0 + n] = _store(r.standard_normal((n, H, P)), spec.dtype)
+    return dict(xbc=xbc, z=z, conv_w=_store(conv_w, "f32"), conv_b=_store(conv_b, "f32"),
+                dt_raw=dt_raw, dt_bias=_store(dt_bias, "f32"), A=_store(A, "f32"),
+                D=_store(D, "f32"), init=init)
