@@ -8,7 +8,7 @@
 //
 // Pure streaming: every state element is independent, one thread owns VW
 // consecutive elements of one (batch, head) and walks the chunks in order.
-// The loads of S for the next PF chunks (8 to 32, see the launcher) do not
+// The loads of S for the next PF chunks (4 to 32, see the launcher) do not
 // depend on the carried state, so they are kept in flight in a register ring
 // while the chain advances.
 #include "device_common.h"
@@ -74,12 +74,14 @@ template <typename HT, int PF, int VW>
 __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ S,
                                                             const float* __restrict__ cs,
                                                             const float* init, HT* __restrict__ Hin,
-                                                            float* fin, int64_t total, int pnv,
-                                                            int nc, int Q) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    const int64_t bh = idx / pnv;
-    const int off = (int)(idx - bh * pnv);
+                                                            float* fin, int pnv, int nc, int Q) {
+    // grid: (batch * heads, element blocks): bh is uniform across the
+    // workgroup, so the per-chunk decays are scalar loads, off the vector
+    // memory counter that paces the S ring.
+    const int64_t bh = blockIdx.x;
+    const int off = blockIdx.y * 256 + threadIdx.x;
+    if (off >= pnv) return;
+    const int64_t idx = bh * pnv + off;
 
     Vec<VW> h;
     if (init) {
@@ -90,40 +92,50 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
     }
     const int64_t base = bh * nc * (int64_t)pnv + off;
     const float* dec = cs + bh * nc * (int64_t)Q + (Q - 1);
-    const int64_t step = (int64_t)pnv * VW;   // floats of one chunk's states
 
+    // The ring holds the next PF chunks.  Its loads are unconditional: a load
+    // past the last chunk re-reads the last chunk (always in bounds) and is
+    // never used.  Whole groups of PF chunks then run without a branch while
+    // chunks remain beyond the group; the last 1..PF chunks run from the ring
+    // with no further loads.  (A load
+    // or store under a branch makes the compiler wait for the ring's loads at
+    // the join, which serialises it.)
     Vec<VW> buf[PF];
     float lg[PF];
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
-        if (k < nc) {
-            buf[k] = load_vec<VW>(S + (base + (int64_t)k * pnv) * VW, 0);
-            lg[k] = dec[(int64_t)k * Q];
-        }
+        const int cl = min(k, nc - 1);
+        buf[k] = load_vec<VW>(S + (base + (int64_t)cl * pnv) * VW, 0);
+        lg[k] = dec[(int64_t)cl * Q];
     }
-    // running pointers (one chunk apart): the prefetch source PF chunks
-    // ahead, its decay, and the Hin destination
-    const float* sp = S + (base + (int64_t)PF * pnv) * VW;
-    const float* dp = dec + (int64_t)PF * Q;
     HT* hp = Hin + base * VW;
-    for (int c0 = 0; c0 < nc; c0 += PF) {
+    const int64_t step = (int64_t)pnv * VW;   // floats of one chunk's states
+    int c0 = 0;
+    for (; c0 + PF < nc; c0 += PF) {
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
-            const int c = c0 + k;
-            if (c < nc) {
-                const Vec<VW> sv = buf[k];
-                const float a = fast_exp2(lg[k]);
-                if (c + PF < nc) {
-                    buf[k] = load_vec<VW>(sp, 0);
-                    lg[k] = *dp;
-                }
-                sp += step;
-                dp += Q;
-                store_vec<VW>(hp, 0, h);
-                hp += step;
+            // slot k is consumed before its refill is issued, so the refill
+            // can land in the same registers (no copy, hence no wait, at the
+            // loop's back edge); the barrier keeps that order
+            const float a = fast_exp2(lg[k]);
+            store_vec<VW>(hp, 0, h);
+            hp += step;
 #pragma unroll
-                for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + sv.v[e];
-            }
+            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
+            __builtin_amdgcn_sched_barrier(0);
+            const int cn = min(c0 + k + PF, nc - 1);
+            buf[k] = load_vec<VW>(S + (base + (int64_t)cn * pnv) * VW, 0);
+            lg[k] = dec[(int64_t)cn * Q];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        if (c0 + k < nc) {
+            const float a = fast_exp2(lg[k]);
+            store_vec<VW>(hp, 0, h);
+            hp += step;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
         }
     }
     if (fin) store_vec<VW>(fin, idx, h);
@@ -133,18 +145,17 @@ template <typename HT, int PF, int VW>
 static void launch_sp_vw(const Dims& d, const float* S, const float* cs, const float* init,
                          void* Hin, float* fin, hipStream_t stream) {
     const int pnv = (int)(d.headdim * d.dstate / VW);
-    const int64_t total = d.batch * d.nheads * (int64_t)pnv;
-    const unsigned blocks = (unsigned)((total + 255) / 256);
-    state_passing_kernel<HT, PF, VW><<<blocks, 256, 0, stream>>>(
-        S, cs, init, reinterpret_cast<HT*>(Hin), fin, total, pnv, (int)d.nchunks, (int)d.chunk);
+    const dim3 grid((unsigned)(d.batch * d.nheads), (unsigned)((pnv + 255) / 256));
+    state_passing_kernel<HT, PF, VW><<<grid, 256, 0, stream>>>(
+        S, cs, init, reinterpret_cast<HT*>(Hin), fin, pnv, (int)d.nchunks, (int)d.chunk);
 }
 
 // Four elements per thread where P * N allows (measured best at the
-// 2.7B shape: 2, 8 or a one-round grid were slower), with the S loads of
-// the next 8 chunks in flight, 16 for long sequences where fewer threads
-// carry the whole traffic, and 48 when the whole grid is at most two waves
-// per SIMD (the registers are there; 2.51 -> 2.37 ms for 32 chains of 4,096
-// chunks, where 32 gained nothing).
+// 2.7B shape: 2, 8 or a one-round grid were slower).  Ring depth: 4 chunks
+// for short chains, where many waves per SIMD hide the latency; 16 for long
+// chains, and 32 when the whole grid is at most two waves per SIMD (32
+// chains of 4,096 chunks: 2.32 ms with the old branchy ring, 1.28 ms now, the
+// same at depths 16 to 48).
 template <typename HT>
 static void launch_sp(const Dims& d, const float* S, const float* cs, const float* init,
                       void* Hin, float* fin, hipStream_t stream) {
@@ -156,9 +167,9 @@ static void launch_sp(const Dims& d, const float* S, const float* cs, const floa
             if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
         }
         const double waves = (double)d.batch * (double)d.nheads * (double)(d.headdim * d.dstate / 4) / 64.0;
-        if (longseq && waves <= 8.0 * cus) launch_sp_vw<HT, 48, 4>(d, S, cs, init, Hin, fin, stream);
+        if (longseq && waves <= 8.0 * cus) launch_sp_vw<HT, 32, 4>(d, S, cs, init, Hin, fin, stream);
         else if (longseq) launch_sp_vw<HT, 16, 4>(d, S, cs, init, Hin, fin, stream);
-        else launch_sp_vw<HT, 8, 4>(d, S, cs, init, Hin, fin, stream);
+        else launch_sp_vw<HT, 4, 4>(d, S, cs, init, Hin, fin, stream);
     } else {
         if (longseq) launch_sp_vw<HT, 32, 1>(d, S, cs, init, Hin, fin, stream);
         else launch_sp_vw<HT, 8, 1>(d, S, cs, init, Hin, fin, stream);
