@@ -9,11 +9,15 @@ Profiling helpers (see profiles/):
                                           1 GiB device copy for calibration
     python bench.py --summarize-trace DIR --out FILE
     python bench.py --summarize-counters DIR_FETCH DIR_WRITE --out-dir profiles
+    python bench.py --state-passing-long  sequential vs segmented state passing
+                                          at the long-context shape
 
 A step is one ssd_forward call over the Mamba-2-2.7B-shaped workload (at this
 shape: chunk cumsum, the one-pass state stage and chunk scan): batch 4, seqlen 8192, 80
 heads, P = 64, N = 128, one B/C group, chunk 256, bf16 x/B/C, fp32 dt/A/D and
-state, random initial state.  Inputs are resident in HBM before timing starts.
+state, random initial state.  Inputs are resident in HBM before timing starts;
+about 0.3 s of untimed forward calls let the GPU clocks ramp before the W
+warm-up steps and the K timed ones.
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (its
 algorithmic bytes per launch over its average launch time, measured here with
@@ -129,8 +133,25 @@ def counter_traffic(kernel: str, workload: str):
 
 
 # -------------------------------------------------------------------- timing
+SETTLE_S = 0.3
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Run fn untimed for about ``seconds`` of wall time so that the GPU's
+    clocks have ramped before anything is timed (without it the first tens
+    of steps run up to 8% slower)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup):
     import torch
+    settle(lambda: ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk,
+                                   g["init"], y=y, final_state=fin, workspace=ws))
     for _ in range(warmup):
         ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk, g["init"], y=y,
                         final_state=fin, workspace=ws)
@@ -264,6 +285,54 @@ def bench_layer(ssd, spec, steps=20):
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     res["kernel_width"] = LAYER_K
     return res
+
+
+def bench_state_passing_long(nsegs=(8, 32, 128), steps=10):
+    """State passing at the long-context shape (1 x 32 chains of 4,096 chunks):
+    the sequential kernel against the segmented associative scan.  S and the
+    decays are drawn on the device (only their shapes matter for timing)."""
+    import ctypes
+    import torch
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import LONG_1M as spec
+    b, L, H, P, N, Q = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.chunk
+    nc = -(-L // Q)
+    lib = ssd.load()
+    gen = torch.Generator(device="cuda").manual_seed(spec.seed)
+    dt = torch.nn.functional.softplus(torch.randn(b, L, H, device="cuda", generator=gen) + spec.dt_shift)
+    A = -torch.exp(torch.rand(H, device="cuda", generator=gen) * spec.a_hi)
+    cs, _ = ssd.chunk_cumsum(dt, A, Q)
+    del dt
+    S = torch.randn(b, H, nc, P, N, device="cuda", generator=gen)
+    Hin = torch.empty(b, H, nc, P, N, dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty(b, H, P, N, device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    byts = S.numel() * 4 + Hin.numel() * 2 + fin.numel() * 4
+
+    def timed(f):
+        assert f() == 0
+        settle(f, 0.1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        return {"us": round(us, 1), "hbm_frac_one_pass": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    out = {"workload": f"state passing, {b * H} chains x {nc} chunks (P {P}, N {N})",
+           "one_pass_bytes": byts,
+           "sequential": timed(lambda: lib.ssd_state_passing(b, L, H, P, N, Q, 1, p(S), p(cs), None,
+                                                             p(Hin), p(fin), st))}
+    for ns in nsegs:
+        need = lib.ssd_state_passing_seg_workspace_bytes(b, H, P, N, ns)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        out[f"segmented_{ns}"] = timed(lambda: lib.ssd_state_passing_seg(
+            b, L, H, P, N, Q, ns, 1, p(S), p(cs), None, p(Hin), p(fin), p(ws), need, st))
+        del ws
+    return out
 
 
 def cpu_baseline(inp, budget_s=12.0):
@@ -436,6 +505,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--state-passing-long", action="store_true",
+                    help="only compare sequential and segmented state passing at the "
+                         "long-context shape")
     ap.add_argument("--profile-loop", type=int, default=0)
     ap.add_argument("--summarize-trace", default=None)
     ap.add_argument("--summarize-counters", nargs=2, default=None)
@@ -468,6 +540,9 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     if args.profile_loop:
         profile_loop(args.profile_loop)
+        return
+    if args.state_passing_long:
+        print(json.dumps(bench_state_passing_long()), flush=True)
         return
     dims = (spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups,
             spec.chunk)

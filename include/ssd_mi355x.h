@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 
@@ -214,6 +214,29 @@ int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t
                           int64_t dstate, int64_t chunk, int32_t dtype, const float* S,
                           const float* cs, const float* init_state, void* Hin,
                           float* final_state, hipStream_t stream);
+
+/* The same outputs as ssd_state_passing, by a two-level associative scan:
+ * two steps of a linear recurrence merge into one step of the same kind
+ * (page "State Space Model", book.paithon.it, section "Dai sistemi dinamici a
+ * Mamba", the parallel scan), so the nc chunks are cut into segments of
+ * ceil(nc / nsegments) chunks (fewer segments if that leaves some empty);
+ * each segment's end state from zero and its summed decay are formed in
+ * parallel, a short chain over the segments gives the state entering each
+ * one, and every segment is walked again from that state to write Hin.  The
+ * depth is about nc / nsegments + nsegments steps instead of nc, for 1.5x the
+ * reads of S.  Results equal ssd_state_passing's up to rounding order.
+ * nsegments: 1 .. 65535 (values above nc act as nc).  workspace: device
+ * memory of at least ssd_state_passing_seg_workspace_bytes(batch, nheads,
+ * headdim, dstate, nsegments) bytes, 256-byte aligned, owned by the caller
+ * and free for the call's duration (SSD_ERR_WORKSPACE otherwise).  Other
+ * arguments, layouts and errors as ssd_state_passing. */
+size_t ssd_state_passing_seg_workspace_bytes(int64_t batch, int64_t nheads, int64_t headdim,
+                                             int64_t dstate, int64_t nsegments);
+int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t dstate, int64_t chunk, int64_t nsegments, int32_t dtype,
+                              const float* S, const float* cs, const float* init_state, void* Hin,
+                              float* final_state, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /* Hin and final_state straight from x, B, cs and dtc: what ssd_chunk_state
  * followed by ssd_state_passing compute, in one pass that keeps the running

@@ -23,6 +23,7 @@ from .ssd import (  # noqa: F401
     ssd_layer,
     ssm_step,
     state_passing,
+    state_passing_seg,
     state_scan,
     status_str,
     workspace_bytes,
@@ -33,5 +34,5 @@ __all__ = [
     "ssd_forward", "ssm_step", "workspace_bytes", "workspace_regions", "chunk_cumsum",
     "chunk_state", "state_passing", "state_scan", "chunk_scan", "load", "library_path", "abi_version",
     "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16", "ABI_VERSION", "layer_in",
-    "layer_out", "ssd_layer",
+    "layer_out", "ssd_layer", "state_passing_seg",
 ]

@@ -38,6 +38,8 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, const float (&w)[8]) {
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+constexpr int kStateRing = 3;
+
 // One workgroup (4 waves) per (batch, chunk, head).  Wave w owns state
 // columns n in [32w, 32w+32) for both 32-row tiles of p.  The chunk's tokens
 // stream through a 3-buffer ring of 32-token blocks of B and x copied
@@ -52,9 +54,10 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
                                                                   float* __restrict__ S, int L, int H,
                                                                   int G, int nc) {
     constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
-    constexpr int DPS = 12 / W;
-    __shared__ uint4 bs0[512], bs1[512], bs2[512];
-    __shared__ uint4 xs0[256], xs1[256], xs2[256];
+    constexpr int DPS = 12 / W;          // copies per wave per 32-token stage
+    constexpr int R = kStateRing;        // ring stages (R - 1 issued ahead)
+    __shared__ uint4 bsr[R][512];
+    __shared__ uint4 xsr[R][256];
     __shared__ float wv[Q];
 
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -76,8 +79,9 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
     if (tid < Q) w_v = fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid];
     asm volatile("" ::: "memory");
     const BxOffsets<W> bxo = bx_offsets<W>(wave, lane, xstride, bstride);
-    issue_bx_stage<W>(wave, lane, tok0, L, xbase, xstride, bbase, bstride, bxo, bs0, xs0);
-    if (NT > 1) issue_bx_stage<W>(wave, lane, tok0 + 32, L, xbase, xstride, bbase, bstride, bxo, bs1, xs1);
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k)
+        if (k < NT) issue_bx_stage<W>(wave, lane, tok0 + 32 * k, L, xbase, xstride, bbase, bstride, bxo, bsr[k], xsr[k]);
     if (tid < Q) wv[tid] = w_v;
 
     // tr16 addressing: lane r of group grp supplies token row 8*(grp/2) + r/4
@@ -89,15 +93,15 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
-        uint4* bst = (jt % 3 == 0) ? bs0 : ((jt % 3 == 1) ? bs1 : bs2);
-        uint4* xst = (jt % 3 == 0) ? xs0 : ((jt % 3 == 1) ? xs1 : xs2);
-        if (jt + 1 < NT) wait_vmcnt<DPS>(); else wait_vmcnt<0>();
+        uint4* bst = bsr[jt % R];
+        uint4* xst = xsr[jt % R];
+        // stages issued after jt: up to R - 2 of them
+        const int ahead = (NT - 1 - jt) < (R - 2) ? (NT - 1 - jt) : (R - 2);
+        wait_vmcnt_n(DPS * ahead);   // a constant once the loop is unrolled
         barrier_lds();
-        if (jt + 2 < NT) {
-            uint4* nb = ((jt + 2) % 3 == 0) ? bs0 : (((jt + 2) % 3 == 1) ? bs1 : bs2);
-            uint4* nx = ((jt + 2) % 3 == 0) ? xs0 : (((jt + 2) % 3 == 1) ? xs1 : xs2);
-            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + 2), L, xbase, xstride, bbase, bstride, bxo, nb, nx);
-        }
+        if (jt + R - 1 < NT)
+            issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + R - 1), L, xbase, xstride, bbase, bstride, bxo,
+                              bsr[(jt + R - 1) % R], xsr[(jt + R - 1) % R]);
         const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
         const SSD_LDS char* bb = (const SSD_LDS char*)lds(bst);
 #pragma unroll

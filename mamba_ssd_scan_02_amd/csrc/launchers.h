@@ -28,6 +28,15 @@ hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, co
                                 const float* init, void* Hin, float* final_state,
                                 hipStream_t stream);
 
+// Segmented (two-level associative) form of the same recurrence; the
+// workspace holds the segment end states, entering states and decays.
+void state_passing_segments(int64_t nc, int64_t nseg_req, int64_t* seg, int64_t* nseg);
+size_t state_passing_seg_workspace_bytes(int64_t batch, int64_t H, int64_t P, int64_t N,
+                                         int64_t nseg);
+hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_req, const float* S,
+                                    const float* cs, const float* init, void* Hin,
+                                    float* final_state, void* workspace, hipStream_t stream);
+
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream);

@@ -181,6 +181,37 @@ int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t
     return hip_status(ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream));
 }
 
+size_t ssd_state_passing_seg_workspace_bytes(int64_t batch, int64_t nheads, int64_t headdim,
+                                             int64_t dstate, int64_t nsegments) {
+    if (batch < 1 || nheads < 1 || headdim < 1 || dstate < 1 || nsegments < 1) return 0;
+    const double states = (double)batch * nheads * nsegments * headdim * dstate * 4.0;
+    if (states > 1.0e15) return 0;
+    return ssd::state_passing_seg_workspace_bytes(batch, nheads, headdim, dstate, nsegments);
+}
+
+int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t dstate, int64_t chunk, int64_t nsegments, int32_t dtype,
+                              const float* S, const float* cs, const float* init_state, void* Hin,
+                              float* final_state, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    Dims d;
+    int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, 1, chunk, &d);
+    if (st != SSD_OK) return st;
+    if ((st = check_supported(dtype, d)) != SSD_OK) return st;
+    if (nsegments < 1 || nsegments > 65535) return SSD_ERR_SHAPE;
+    if (!S || !cs || !Hin) return SSD_ERR_NULL;
+    if (!workspace) return SSD_ERR_WORKSPACE;
+    if (!aligned(S, 16) || !aligned(Hin, 16) || !aligned(cs, 4) || !aligned(workspace, 256) ||
+        (init_state && !aligned(init_state, 16)) || (final_state && !aligned(final_state, 16)))
+        return SSD_ERR_ALIGN;
+    int64_t seg, nseg;
+    ssd::state_passing_segments(d.nchunks, nsegments, &seg, &nseg);
+    if (workspace_bytes < ssd::state_passing_seg_workspace_bytes(batch, nheads, headdim, dstate, nseg))
+        return SSD_ERR_WORKSPACE;
+    return hip_status(ssd::launch_state_passing_seg(d, dtype, nsegments, S, cs, init_state, Hin,
+                                                    final_state, workspace, stream));
+}
+
 int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                        const void* x, const void* B, const float* cs, const float* dtc,

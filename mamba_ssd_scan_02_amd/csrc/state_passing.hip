@@ -1,4 +1,5 @@
-// state_passing.hip -- the linear recurrence between chunks.
+// state_passing.hip -- the linear recurrence between chunks, sequential and
+// segmented.
 //
 // Only the summary state travels from one block to the next (page "Mamba-2
 // (2024): SSM e attention sono la stessa cosa", section "Il trucco a blocchi"),
@@ -69,20 +70,70 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
     }
 }
 
-// Element indices below are in units of VW floats.
-template <typename HT, int PF, int VW>
-__global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ S,
-                                                            const float* __restrict__ cs,
-                                                            const float* init, HT* __restrict__ Hin,
-                                                            float* fin, int pnv, int nc, int Q) {
-    // grid: (batch * heads, element blocks): bh is uniform across the
-    // workgroup, so the per-chunk decays are scalar loads, off the vector
-    // memory counter that paces the S ring.
-    const int64_t bh = blockIdx.x;
-    const int off = blockIdx.y * 256 + threadIdx.x;
-    if (off >= pnv) return;
-    const int64_t idx = bh * pnv + off;
+// Walks n >= 1 chunks of one thread's VW state elements:
+//     [store h at hp], h <- exp2(lg_c) h + S_c,   c = 0 .. n - 1,
+// where S_c sits at src + c * sstep (floats) and lg_c, the chunk's decay in
+// log2 units, at dec[c * dstep].  kStore writes the entering state of every
+// chunk (hp advances by sstep); kSum adds the lg_c into *lsum.
+//
+// The ring holds the next PF chunks.  Its loads are unconditional: a load past
+// the last chunk re-reads the last chunk (always in bounds) and is never used.
+// Whole groups of PF chunks then run without a branch while chunks remain
+// beyond the group; the last 1..PF chunks run from the ring with no further
+// loads.  (A load or store under a branch makes the compiler wait for the
+// ring's loads at the join, which serialises it.)
+template <typename HT, int PF, int VW, bool kStore, bool kSum>
+__device__ __forceinline__ void walk_chunks(const float* __restrict__ src, int64_t sstep,
+                                            const float* __restrict__ dec, int64_t dstep, int n,
+                                            HT* hp, Vec<VW>& h, float* lsum) {
+    Vec<VW> buf[PF];
+    float lg[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        const int cl = min(k, n - 1);
+        buf[k] = load_vec<VW>(src + (int64_t)cl * sstep, 0);
+        lg[k] = dec[(int64_t)cl * dstep];
+    }
+    float ls = 0.0f;
+    int c0 = 0;
+    for (; c0 + PF < n; c0 += PF) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            // slot k is consumed before its refill is issued, so the refill
+            // can land in the same registers (no copy, hence no wait, at the
+            // loop's back edge); the barrier keeps that order
+            const float a = fast_exp2(lg[k]);
+            if (kSum) ls += lg[k];
+            if (kStore) {
+                store_vec<VW>(hp, 0, h);
+                hp += sstep;
+            }
+#pragma unroll
+            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
+            __builtin_amdgcn_sched_barrier(0);
+            const int cn = min(c0 + k + PF, n - 1);
+            buf[k] = load_vec<VW>(src + (int64_t)cn * sstep, 0);
+            lg[k] = dec[(int64_t)cn * dstep];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        if (c0 + k < n) {
+            const float a = fast_exp2(lg[k]);
+            if (kSum) ls += lg[k];
+            if (kStore) {
+                store_vec<VW>(hp, 0, h);
+                hp += sstep;
+            }
+#pragma unroll
+            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
+        }
+    }
+    if (kSum) *lsum = ls;
+}
 
+template <int VW>
+__device__ __forceinline__ Vec<VW> start_state(const float* init, int64_t idx) {
     Vec<VW> h;
     if (init) {
         h = load_vec<VW>(init, idx);
@@ -90,55 +141,97 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
 #pragma unroll
         for (int e = 0; e < VW; ++e) h.v[e] = 0.0f;
     }
-    const int64_t base = bh * nc * (int64_t)pnv + off;
-    const float* dec = cs + bh * nc * (int64_t)Q + (Q - 1);
+    return h;
+}
 
-    // The ring holds the next PF chunks.  Its loads are unconditional: a load
-    // past the last chunk re-reads the last chunk (always in bounds) and is
-    // never used.  Whole groups of PF chunks then run without a branch while
-    // chunks remain beyond the group; the last 1..PF chunks run from the ring
-    // with no further loads.  (A load
-    // or store under a branch makes the compiler wait for the ring's loads at
-    // the join, which serialises it.)
-    Vec<VW> buf[PF];
-    float lg[PF];
-#pragma unroll
-    for (int k = 0; k < PF; ++k) {
-        const int cl = min(k, nc - 1);
-        buf[k] = load_vec<VW>(S + (base + (int64_t)cl * pnv) * VW, 0);
-        lg[k] = dec[(int64_t)cl * Q];
-    }
-    HT* hp = Hin + base * VW;
-    const int64_t step = (int64_t)pnv * VW;   // floats of one chunk's states
-    int c0 = 0;
-    for (; c0 + PF < nc; c0 += PF) {
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            // slot k is consumed before its refill is issued, so the refill
-            // can land in the same registers (no copy, hence no wait, at the
-            // loop's back edge); the barrier keeps that order
-            const float a = fast_exp2(lg[k]);
-            store_vec<VW>(hp, 0, h);
-            hp += step;
-#pragma unroll
-            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
-            __builtin_amdgcn_sched_barrier(0);
-            const int cn = min(c0 + k + PF, nc - 1);
-            buf[k] = load_vec<VW>(S + (base + (int64_t)cn * pnv) * VW, 0);
-            lg[k] = dec[(int64_t)cn * Q];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < PF; ++k) {
-        if (c0 + k < nc) {
-            const float a = fast_exp2(lg[k]);
-            store_vec<VW>(hp, 0, h);
-            hp += step;
-#pragma unroll
-            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
-        }
-    }
+// Element indices below are in units of VW floats; pnv = P N / VW.  Grids put
+// (batch, head) on x, so the decays are uniform across a workgroup and come
+// from scalar loads, off the vector memory counter that paces the S ring.
+template <typename HT, int PF, int VW>
+__global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ S,
+                                                            const float* __restrict__ cs,
+                                                            const float* init, HT* __restrict__ Hin,
+                                                            float* fin, int pnv, int nc, int Q) {
+    const int64_t bh = blockIdx.x;
+    const int off = blockIdx.y * 256 + threadIdx.x;
+    if (off >= pnv) return;
+    const int64_t idx = bh * pnv + off;
+    Vec<VW> h = start_state<VW>(init, idx);
+    const int64_t base = (bh * nc * (int64_t)pnv + off) * VW;
+    walk_chunks<HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW, cs + bh * nc * (int64_t)Q + (Q - 1),
+                                         Q, nc, Hin + base, h, nullptr);
     if (fin) store_vec<VW>(fin, idx, h);
+}
+
+// ---------------------------------------------------------------------------
+// Segmented form: two consecutive steps of a linear recurrence merge into one
+// step of the same kind (the parallel scan of page "State Space Model",
+// section "Dai sistemi dinamici a Mamba"): (a1, s1) then (a2, s2) is
+// (a2 a1, a2 s1 + s2).  So the chunks are cut into segments of `seg` chunks
+// and scanned in two levels:
+//   1. seg_reduce: each segment's end state from zero, E_s, and its summed
+//      log2 decay D_s (all segments in parallel);
+//   2. seg_carry:  the state entering each segment, Hs_{s+1} = exp2(D_s) Hs_s
+//      + E_s from the initial state, and the final state (a chain of nseg);
+//   3. seg_down:   each segment again from Hs_s, writing Hin (all in parallel).
+// Depth nc / nseg + nseg instead of nc, for 1.5x the S reads.
+
+template <int PF, int VW>
+__global__ __launch_bounds__(256) void sp_seg_reduce_kernel(const float* __restrict__ S,
+                                                            const float* __restrict__ cs,
+                                                            float* __restrict__ E,
+                                                            float* __restrict__ Dseg, int pnv,
+                                                            int nc, int Q, int seg, int nseg) {
+    const int64_t bh = blockIdx.x;
+    const int s = blockIdx.y;
+    const int off = blockIdx.z * 256 + threadIdx.x;
+    if (off >= pnv) return;
+    const int c0 = s * seg, n = min(seg, nc - c0);
+    Vec<VW> h;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) h.v[e] = 0.0f;
+    float ls = 0.0f;
+    walk_chunks<float, PF, VW, false, true>(S + ((bh * nc + c0) * (int64_t)pnv + off) * VW,
+                                            (int64_t)pnv * VW,
+                                            cs + (bh * nc + c0) * (int64_t)Q + (Q - 1), Q, n,
+                                            (float*)nullptr, h, &ls);
+    store_vec<VW>(E, (bh * nseg + s) * (int64_t)pnv + off, h);
+    if (off == 0) Dseg[bh * nseg + s] = ls;
+}
+
+template <int PF, int VW>
+__global__ __launch_bounds__(256) void sp_seg_carry_kernel(const float* __restrict__ E,
+                                                           const float* __restrict__ Dseg,
+                                                           const float* init,
+                                                           float* __restrict__ Hs, float* fin,
+                                                           int pnv, int nseg) {
+    const int64_t bh = blockIdx.x;
+    const int off = blockIdx.y * 256 + threadIdx.x;
+    if (off >= pnv) return;
+    const int64_t idx = bh * pnv + off;
+    Vec<VW> h = start_state<VW>(init, idx);
+    const int64_t base = (bh * nseg * (int64_t)pnv + off) * VW;
+    walk_chunks<float, PF, VW, true, false>(E + base, (int64_t)pnv * VW, Dseg + bh * nseg, 1, nseg,
+                                            Hs + base, h, nullptr);
+    if (fin) store_vec<VW>(fin, idx, h);
+}
+
+template <typename HT, int PF, int VW>
+__global__ __launch_bounds__(256) void sp_seg_down_kernel(const float* __restrict__ S,
+                                                          const float* __restrict__ cs,
+                                                          const float* __restrict__ Hs,
+                                                          HT* __restrict__ Hin, int pnv, int nc,
+                                                          int Q, int seg, int nseg) {
+    const int64_t bh = blockIdx.x;
+    const int s = blockIdx.y;
+    const int off = blockIdx.z * 256 + threadIdx.x;
+    if (off >= pnv) return;
+    const int c0 = s * seg, n = min(seg, nc - c0);
+    Vec<VW> h = load_vec<VW>(Hs, (bh * nseg + s) * (int64_t)pnv + off);
+    const int64_t base = ((bh * nc + c0) * (int64_t)pnv + off) * VW;
+    walk_chunks<HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW,
+                                         cs + (bh * nc + c0) * (int64_t)Q + (Q - 1), Q, n, Hin + base,
+                                         h, nullptr);
 }
 
 template <typename HT, int PF, int VW>
@@ -174,6 +267,57 @@ static void launch_sp(const Dims& d, const float* S, const float* cs, const floa
         if (longseq) launch_sp_vw<HT, 32, 1>(d, S, cs, init, Hin, fin, stream);
         else launch_sp_vw<HT, 8, 1>(d, S, cs, init, Hin, fin, stream);
     }
+}
+
+// Segment length and count actually used for a requested count.
+void state_passing_segments(int64_t nc, int64_t nseg_req, int64_t* seg, int64_t* nseg) {
+    const int64_t want = nseg_req < 1 ? 1 : (nseg_req > nc ? nc : nseg_req);
+    *seg = (nc + want - 1) / want;
+    *nseg = (nc + *seg - 1) / *seg;
+}
+
+static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+
+size_t state_passing_seg_workspace_bytes(int64_t batch, int64_t H, int64_t P, int64_t N,
+                                         int64_t nseg) {
+    const int64_t states = batch * H * nseg * P * N * 4;
+    return (size_t)(2 * up256(states) + up256(batch * H * nseg * 4));
+}
+
+template <typename HT, int VW>
+static void launch_seg_vw(const Dims& d, int64_t seg, int64_t nseg, const float* S, const float* cs,
+                          const float* init, void* Hin, float* fin, char* ws, hipStream_t stream) {
+    const int pnv = (int)(d.headdim * d.dstate / VW);
+    const int64_t states = d.batch * d.nheads * nseg * d.headdim * d.dstate * 4;
+    float* E = reinterpret_cast<float*>(ws);
+    float* Hs = reinterpret_cast<float*>(ws + up256(states));
+    float* Dseg = reinterpret_cast<float*>(ws + 2 * up256(states));
+    const unsigned bh = (unsigned)(d.batch * d.nheads), eb = (unsigned)((pnv + 255) / 256);
+    const dim3 g3(bh, (unsigned)nseg, eb), g2(bh, eb);
+    constexpr int PFS = VW == 4 ? 8 : 16;   // segment walks: many waves hide the latency
+    sp_seg_reduce_kernel<PFS, VW><<<g3, 256, 0, stream>>>(S, cs, E, Dseg, pnv, (int)d.nchunks,
+                                                          (int)d.chunk, (int)seg, (int)nseg);
+    sp_seg_carry_kernel<16, VW><<<g2, 256, 0, stream>>>(E, Dseg, init, Hs, fin, pnv, (int)nseg);
+    sp_seg_down_kernel<HT, PFS, VW><<<g3, 256, 0, stream>>>(S, cs, Hs, reinterpret_cast<HT*>(Hin), pnv,
+                                                            (int)d.nchunks, (int)d.chunk, (int)seg,
+                                                            (int)nseg);
+}
+
+hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_req, const float* S,
+                                    const float* cs, const float* init, void* Hin,
+                                    float* final_state, void* workspace, hipStream_t stream) {
+    int64_t seg, nseg;
+    state_passing_segments(d.nchunks, nseg_req, &seg, &nseg);
+    char* ws = static_cast<char*>(workspace);
+    const bool v4 = (d.headdim * d.dstate) % 4 == 0;
+    if (dtype == 1) {
+        if (v4) launch_seg_vw<bf16_t, 4>(d, seg, nseg, S, cs, init, Hin, final_state, ws, stream);
+        else launch_seg_vw<bf16_t, 1>(d, seg, nseg, S, cs, init, Hin, final_state, ws, stream);
+    } else {
+        if (v4) launch_seg_vw<float, 4>(d, seg, nseg, S, cs, init, Hin, final_state, ws, stream);
+        else launch_seg_vw<float, 1>(d, seg, nseg, S, cs, init, Hin, final_state, ws, stream);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, const float* cs,

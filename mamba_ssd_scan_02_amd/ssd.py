@@ -21,7 +21,7 @@ DTYPE_BF16 = 1
 
 # The SSD_ABI_VERSION this binding was written against; load() refuses a
 # library that reports another one (a stale build).
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _STATUS_OK = 0
 
@@ -77,6 +77,10 @@ def load():
     lib.ssd_state_scan.argtypes = [i64] * 7 + [i32] + [vp] * 7 + [vp]
     lib.ssd_chunk_scan.restype = i32
     lib.ssd_chunk_scan.argtypes = [i64] * 7 + [i32] + [vp] * 8 + [vp]
+    lib.ssd_state_passing_seg_workspace_bytes.restype = sz
+    lib.ssd_state_passing_seg_workspace_bytes.argtypes = [i64] * 5
+    lib.ssd_state_passing_seg.restype = i32
+    lib.ssd_state_passing_seg.argtypes = [i64] * 7 + [i32] + [vp] * 6 + [sz, vp]
     lib.ssd_layer_in.restype = i32
     lib.ssd_layer_in.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp]
     lib.ssd_layer_out.restype = i32
@@ -282,6 +286,31 @@ def state_passing(S, cs, seqlen, chunk, dtype, init_state=None, final_state=None
     _check("ssd_state_passing", lib.ssd_state_passing(batch, seqlen, H, P, N, chunk, code, _p(S),
                                                       _p(cs), _p(init_state), _p(Hin),
                                                       _p(final_state), _stream(S.device)))
+    return Hin, final_state
+
+
+def state_passing_seg(S, cs, seqlen, chunk, dtype, nsegments, init_state=None, final_state=None,
+                      workspace=None):
+    """(Hin, final) as state_passing, by the two-level associative scan over
+    ``nsegments`` segments of chunks -- see ssd_state_passing_seg."""
+    lib = load()
+    S = _dev(S, "S", torch.float32)
+    batch, H, nc, P, N = S.shape
+    _dev(cs, "cs", torch.float32, (batch, H, nc, chunk), S.device)
+    _dev(init_state, "init_state", torch.float32, (batch, H, P, N), S.device)
+    Hin = torch.empty((batch, H, nc, P, N), dtype=dtype, device=S.device)
+    if final_state is None:
+        final_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=S.device)
+    _dev(final_state, "final_state", torch.float32, (batch, H, P, N), S.device)
+    need = lib.ssd_state_passing_seg_workspace_bytes(batch, H, P, N, nsegments)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=S.device)
+    _dev(workspace, "workspace", torch.uint8, None, S.device)
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    _check("ssd_state_passing_seg",
+           lib.ssd_state_passing_seg(batch, seqlen, H, P, N, chunk, nsegments, code, _p(S), _p(cs),
+                                     _p(init_state), _p(Hin), _p(final_state), _p(workspace),
+                                     workspace.numel(), _stream(S.device)))
     return Hin, final_state
 
 

@@ -187,3 +187,60 @@ def test_chunk_cumsum_zero_order_hold_weights():
     got = dtc.cpu().numpy()
     np.testing.assert_allclose(got, ref, rtol=2e-7, atol=0)
     assert np.array_equal(got[:, 2], ref[:, 2])   # A = 0: dt itself
+
+
+SEG_CASES = [
+    # (name, batch, L, H, P, N, Q, nsegments, dtype, init, alias init/final)
+    ("one_segment", 2, 700, 3, 64, 128, 256, 1, "bf16", True, False),
+    ("segment_per_chunk", 2, 700, 3, 64, 128, 256, 3, "bf16", True, False),
+    ("more_segments_than_chunks", 1, 700, 2, 64, 128, 256, 9, "bf16", False, False),
+    ("ragged_segments", 1, 65 * 64 + 17, 2, 64, 128, 64, 7, "bf16", True, False),
+    ("many_segments", 1, 65 * 64 + 17, 2, 64, 128, 64, 33, "f32", True, True),
+    ("scalar_lanes_f32", 2, 300, 2, 3, 5, 16, 4, "f32", True, False),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_state_passing_segmented(case):
+    """ssd_state_passing_seg against the fp64 stage definition (from the GPU's
+    own S and cs) and against the sequential GPU kernel."""
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    name, batch, L, H, P, N, Q, nseg, dtype, init, alias = case
+    say(f"[state_passing_seg] {name}")
+    inp = _inputs(41, batch, L, H, P, N, 1, dtype, init=init)
+    g = to_gpu(inp)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
+    sd = torch.bfloat16 if dtype == "bf16" else torch.float32
+    st = g["init"].clone() if init else None
+    Hin, fin = ssd.state_passing_seg(S, cs, L, Q, sd, nseg, init_state=st,
+                                     final_state=st if alias else None)
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    Hin_ref, fin_ref = stages.state_passing(S.cpu().double().numpy(), Acs,
+                                            inp["init"] if init else None)
+    e_h, e_f = max_rel_err(Hin, Hin_ref), max_rel_err(fin, fin_ref)
+    say(f"  Hin {e_h:.3e} final {e_f:.3e}")
+    assert e_h < (8e-3 if dtype == "bf16" else 1e-6)
+    assert e_f < 1e-5
+    Hin2, fin2 = ssd.state_passing(S, cs, L, Q, sd, g["init"] if init else None)
+    assert max_rel_err(fin, fin2.cpu().double().numpy()) < 1e-5
+    assert max_rel_err(Hin, Hin2.cpu().double().numpy()) < (8e-3 if dtype == "bf16" else 1e-6)
+
+
+def test_state_passing_segmented_errors():
+    import mamba_ssd_scan_02_amd as ssd
+    lib = ssd.load()
+    t = torch.zeros(1 << 16, device="cuda")
+    vp = t.data_ptr()
+    need = lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 4)
+    assert need > 0
+    # workspace too small, NULL workspace, zero segments
+    assert lib.ssd_state_passing_seg(1, 1024, 2, 64, 128, 256, 4, 1, vp, vp, None, vp, None, vp,
+                                     need - 1, None) == 4
+    assert lib.ssd_state_passing_seg(1, 1024, 2, 64, 128, 256, 4, 1, vp, vp, None, vp, None, None,
+                                     need, None) == 4
+    assert lib.ssd_state_passing_seg(1, 1024, 2, 64, 128, 256, 0, 1, vp, vp, None, vp, None, vp,
+                                     need, None) == 2
+    assert lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 0) == 0
