@@ -54,32 +54,33 @@ __global__ __launch_bounds__(256) void ssm_step_vec_kernel(float* __restrict__ s
     T* yr = y + (int64_t)bh * P;
 
     for (int p0 = r0; p0 < P; p0 += RPP * RPT) {
+        // Loads are unconditional (rows past P re-read row P - 1 and are
+        // never stored): a load under a branch makes the compiler wait for it
+        // at the join, which would issue the rows one at a time.
         float4 s[RPT];
         float xv[RPT];
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            const int p = p0 + k * RPP;
-            if (p < P) {
-                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (int64_t)p * N));
-                s[k] = make_float4(t[0], t[1], t[2], t[3]);
-                xv[k] = Elem<T>::load(xr, p);
-            }
+            const int pl = min(p0 + k * RPP, P - 1);
+            const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (int64_t)pl * N));
+            s[k] = make_float4(t[0], t[1], t[2], t[3]);
+            xv[k] = Elem<T>::load(xr, pl);
         }
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
             const int p = p0 + k * RPP;
+            const float u = w * xv[k];
+            float4 v = s[k];
+            v.x = a * v.x + u * bv[0];
+            v.y = a * v.y + u * bv[1];
+            v.z = a * v.z + u * bv[2];
+            v.w = a * v.w + u * bv[3];
+            float part = cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w;
+#pragma unroll
+            for (int off = NV / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
             if (p < P) {
-                const float u = w * xv[k];
-                float4 v = s[k];
-                v.x = a * v.x + u * bv[0];
-                v.y = a * v.y + u * bv[1];
-                v.z = a * v.z + u * bv[2];
-                v.w = a * v.w + u * bv[3];
                 const f32x4 tv = {v.x, v.y, v.z, v.w};
                 __builtin_nontemporal_store(tv, reinterpret_cast<f32x4*>(st + (int64_t)p * N));
-                float part = cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w;
-#pragma unroll
-                for (int off = NV / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
                 if (n4 == 0) Elem<T>::store(yr, p, part + Dh * xv[k]);
             }
         }
