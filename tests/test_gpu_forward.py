@@ -240,3 +240,52 @@ def test_zero_order_hold_forward(case):
     y_plain, _ = gpu_forward(inp, chunk)
     d = max_rel_err(select_y(y_plain, bh), y_ref)
     assert d > 10 * TOL[spec.dtype], d
+
+
+CONV_CASES = [
+    # (label, batch, L, H, P, N, G, chunk, dtype, zoh)
+    ("bf16_mfma", 2, 700, 4, 64, 128, 2, 256, "bf16", False),
+    ("bf16_mfma_zoh", 1, 600, 2, 64, 128, 1, 128, "bf16", True),
+    ("f32_generic", 1, 333, 3, 16, 32, 1, 64, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=[c[0] for c in CONV_CASES])
+def test_time_invariant_is_a_convolution(case):
+    """With dt, B and C constant over the tokens (the time-invariant case of
+    page "State Space Model", section "Un sistema che riassume il passato"),
+    the GPU forward equals the causal convolution of x with the kernel
+    K_k = (C . B) w a^k (a = exp(dt A), w = dt or expm1(dt A) / A), D x added,
+    computed here by FFT from the same stored values -- no recurrence."""
+    from scipy.signal import fftconvolve
+
+    label, batch, L, H, P, N, G, chunk, dtype, zoh = case
+    say(f"[forward conv] {label}")
+    sd = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rng = np.random.default_rng(77)
+    x = torch.from_numpy(rng.standard_normal((batch, L, H, P)).astype(np.float32)).to(sd)
+    dt_h = np.log1p(np.exp(rng.standard_normal((batch, H)) - 1.0)).astype(np.float32)
+    A = (-np.exp(rng.uniform(0.0, 1.0, H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    Bv = torch.from_numpy((rng.standard_normal((batch, G, N)) / math.sqrt(N)).astype(np.float32)).to(sd)
+    Cv = torch.from_numpy((rng.standard_normal((batch, G, N)) / math.sqrt(N)).astype(np.float32)).to(sd)
+    dt = torch.from_numpy(np.repeat(dt_h[:, None, :], L, axis=1))
+    B = Bv[:, None].expand(batch, L, G, N).contiguous()
+    C = Cv[:, None].expand(batch, L, G, N).contiguous()
+    inp = dict(x=x, dt=dt, A=torch.from_numpy(A), B=B, C=C, D=torch.from_numpy(D), init=None)
+    y, _ = gpu_forward(inp, chunk, zoh=zoh)
+
+    x64 = x.double().numpy()
+    B64, C64 = Bv.double().numpy(), Cv.double().numpy()
+    ref = np.empty_like(x64)
+    k = np.arange(L, dtype=np.float64)
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            d, a_h = float(dt_h[b, h]), float(A[h])
+            w = math.expm1(d * a_h) / a_h if zoh else d
+            K = float(C64[b, g] @ B64[b, g]) * w * np.exp(d * a_h * k)
+            ref[b, :, h] = fftconvolve(x64[b, :, h], K[:, None], axes=0)[:L] + float(D[h]) * x64[b, :, h]
+    e = max_rel_err(y, ref)
+    say(f"  y {e:.3e}")
+    assert e <= TOL[dtype], e
