@@ -96,12 +96,15 @@ def forward_model(b, L, H, P, N, G, Q):
 
 def layer_model(b, L, H, P, N, G, K):
     """Algorithmic HBM bytes of the kernels around the scan (bf16 storage):
-    the convolution reads xbc and writes x, B, C; the step kernel reads dt_raw
-    and writes dt; the gate reads y and z and writes out."""
+    the convolution launch reads xbc (and the filter) and writes x, B, C, and
+    its extra blocks read dt_raw (and dt_bias) and write dt; the gate reads y
+    and z and writes out.  (layer_dt: the step kernel the per-element path
+    launches on its own.)"""
     tok = b * L
     cd = H * P + 2 * G * N
-    return {"layer_in": 2 * tok * cd * 2 + cd * (K + 1) * 4,
-            "layer_dt": 2 * tok * H * 4 + H * 4,
+    dt = 2 * tok * H * 4 + H * 4
+    return {"layer_in": 2 * tok * cd * 2 + cd * (K + 1) * 4 + dt,
+            "layer_dt": dt,
             "layer_out": 3 * tok * H * P * 2}
 
 
@@ -268,7 +271,7 @@ def bench_layer(ssd, spec, steps=20):
     run_out = lambda: ssd.layer_out(x, li["z"], out=out)
     res = {}
     mb = layer_model(b, L, H, P, N, G, LAYER_K)
-    for name, fn, byts in (("layer_in", run_in, mb["layer_in"] + mb["layer_dt"]),
+    for name, fn, byts in (("layer_in", run_in, mb["layer_in"]),
                            ("layer_out", run_out, mb["layer_out"])):
         for _ in range(3):
             fn()
