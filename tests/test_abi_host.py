@@ -141,3 +141,60 @@ def test_stage_argument_errors(lib):
                               None, P(0x4000), None, None) == SHAPE
     assert lib.ssd_chunk_scan(1, 64, 2, 64, 128, 1, 64, 1, P(0x1000), P(0x2000), P(0x3000),
                               P(0x10), P(0x20), P(0x8000), None, P(0x1000), None) == ALIAS
+
+
+def test_layer_argument_errors(lib):
+    P = ctypes.c_void_p
+
+    def lin(**over):
+        a = dict(batch=1, seqlen=64, nheads=2, headdim=8, dstate=8, ngroups=1, K=4, dtype=1,
+                 xbc=0x10000, w=0x20000, b=None, dtr=0x30000, dtb=None, x=0x40000, B=0x50000,
+                 C=0x60000, dt=0x70000)
+        a.update(over)
+        return lib.ssd_layer_in(a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["dstate"],
+                                a["ngroups"], a["K"], a["dtype"], P(a["xbc"]), P(a["w"]),
+                                P(a["b"]), P(a["dtr"]), P(a["dtb"]), P(a["x"]), P(a["B"]),
+                                P(a["C"]), P(a["dt"]), None)
+
+    assert lin(seqlen=0) == SHAPE
+    assert lin(nheads=3, ngroups=2) == SHAPE
+    assert lin(batch=70000) == SHAPE
+    assert lin(K=0) == UNSUP and lin(K=9) == UNSUP
+    assert lin(dtype=4) == UNSUP
+    assert lin(xbc=None) == NULL and lin(dt=None) == NULL and lin(w=None) == NULL
+    assert lin(x=0x40001) == ALIGN
+    assert lin(dtr=0x30002) == ALIGN
+    assert lin(x=0x10000) == ALIAS                 # x on top of xbc
+    assert lin(C=0x50000) == ALIAS                 # C on top of B
+    assert lin(dt=0x30000) == ALIAS                # dt on top of dt_raw
+    assert lib.ssd_layer_out(0, 1, P(0x1000), P(0x2000), P(0x3000), None) == SHAPE
+    assert lib.ssd_layer_out(16, 3, P(0x1000), P(0x2000), P(0x3000), None) == UNSUP
+    assert lib.ssd_layer_out(16, 1, P(0x1000), None, P(0x3000), None) == NULL
+    assert lib.ssd_layer_out(16, 1, P(0x1001), P(0x2000), P(0x3000), None) == ALIGN
+    assert lib.ssd_layer_out(16, 1, P(0x1000), P(0x2000), P(0x2010), None) == ALIAS   # out on z
+    assert lib.ssd_layer_out(16, 1, P(0x1000), P(0x2000), P(0x1010), None) == ALIAS   # part of y
+
+
+def test_segmented_state_passing_argument_errors(lib):
+    P = ctypes.c_void_p
+    need = lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 4)
+    # two state buffers of 2 x 4 x 64 x 128 fp32 plus the decays, 256-byte rounded
+    assert need == 2 * (2 * 4 * 64 * 128 * 4) + 256
+    assert lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 0) == 0
+
+    def seg(**over):
+        a = dict(nseg=4, S=0x100000, cs=0x2000, init=None, Hin=0x400000, fin=None, ws=0x800000,
+                 wsb=need)
+        a.update(over)
+        return lib.ssd_state_passing_seg(1, 1024, 2, 64, 128, 256, a["nseg"], 1, P(a["S"]),
+                                         P(a["cs"]), P(a["init"]), P(a["Hin"]), P(a["fin"]),
+                                         P(a["ws"]), a["wsb"], None)
+
+    assert seg(nseg=0) == SHAPE
+    assert seg(S=None) == NULL
+    assert seg(ws=None) == WS
+    assert seg(wsb=need - 1) == WS
+    assert seg(ws=0x800010) == ALIGN
+    assert seg(Hin=0x400008) == ALIGN
+    # more segments than chunks act as one per chunk (4 here): the same workspace suffices
+    assert lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 4) == need
