@@ -245,8 +245,9 @@ int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int
  * passato" with one factor per block).  Same arguments, layouts, aliasing
  * rules (init_state / final_state may be NULL and may alias) and outputs as
  * that pair.  Matrix-core path only: dtype bf16, headdim 64, dstate 128,
- * chunk 256; anything else returns SSD_ERR_UNSUPPORTED.  ssd_forward takes
- * this path by itself when batch * nheads fills the device. */
+ * chunk 256; anything else returns SSD_ERR_UNSUPPORTED.  (ssd_forward runs
+ * ssd_chunk_state and ssd_state_passing instead: on the MI355X that pair,
+ * with two heads per chunk-state workgroup, measured faster.) */
 int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                        const void* x, const void* B, const float* cs, const float* dtc,

@@ -39,6 +39,9 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, const float (&w)[8]) {
 }
 
 constexpr int kStateRing = 3;
+// Heads per workgroup where a group's head count allows it, else one.  At the
+// 2.7B shape: 1 head 151 us, 2 heads 134-138 us, 4 heads 139-141 us.
+constexpr int kStateHeads = 2;
 
 // One workgroup (4 waves) per (batch, chunk, head).  Wave w owns state
 // columns n in [32w, 32w+32) for both 32-row tiles of p.  The chunk's tokens
@@ -139,6 +142,187 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
         const int p = 8 * (r >> 2) + 4 * hf + (r & 3);
         __builtin_nontemporal_store(acc[0][r], &Sp[p * N + n]);
         __builtin_nontemporal_store(acc[1][r], &Sp[(32 + p) * N + n]);
+    }
+}
+
+// HG (2 or 4) heads per workgroup: one workgroup per (batch, chunk, HG
+// consecutive heads of one group).  Their x rows are HG * 128 contiguous
+// bytes per token, copied with the same swizzle as B's rows (the LDS banks
+// repeat every 256 bytes, so rows of 256 or 512 bytes see the same pattern),
+// and each B fragment read from LDS serves all HG heads (scaled by each
+// head's weights).  Wave w owns state columns n in [32w, 32w+32) of every
+// head.  Wider rows read faster from HBM than one head's 128-byte rows, and B
+// crosses L2 -> LDS once per HG heads.
+template <int W, int HG>
+struct BxhOffsets {
+    static constexpr int XC = 4 * HG / W;   // x copies per wave per stage
+    uint32_t b[8 / W];
+    uint32_t x[XC];
+};
+
+template <int W, int HG>
+__device__ __forceinline__ BxhOffsets<W, HG> bxh_offsets(int wave, int lane, int64_t xstride,
+                                                         int64_t bstride) {
+    constexpr int PPR = 8 * HG, RPC = 64 / PPR;   // x: 16-byte pieces per row, rows per copy
+    BxhOffsets<W, HG> o;
+#pragma unroll
+    for (int i = 0; i < 8 / W; ++i) {
+        const int r = 4 * (wave + i * W) + (lane >> 4);
+        o.b[i] = (uint32_t)r * (uint32_t)bstride * 2u + 16u * (uint32_t)((lane & 15) ^ swz_b(r));
+    }
+#pragma unroll
+    for (int i = 0; i < BxhOffsets<W, HG>::XC; ++i) {
+        const int r = RPC * (wave + i * W) + lane / PPR;
+        o.x[i] = (uint32_t)r * (uint32_t)xstride * 2u + 16u * (uint32_t)((lane % PPR) ^ swz_b(r));
+    }
+    return o;
+}
+
+// 32 tokens of B (32 x 256 B) and of the heads' x (32 x HG * 128 B) into one
+// pipeline buffer; rows past the end re-read the last token (their weights
+// are zero).
+template <int W, int HG>
+__device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase, int L,
+                                                const bf16_t* xbase, int64_t xstride,
+                                                const bf16_t* bbase, int64_t bstride,
+                                                const BxhOffsets<W, HG>& off, uint4* bst, uint4* xst) {
+    constexpr int PPR = 8 * HG, RPC = 64 / PPR, XC = BxhOffsets<W, HG>::XC;
+    asm volatile("" : "+s"(tokbase));
+    if (tokbase + 31 < L) {
+        const char* bb = reinterpret_cast<const char*>(bbase + (int64_t)tokbase * bstride);
+        const char* xb = reinterpret_cast<const char*>(xbase + (int64_t)tokbase * xstride);
+#pragma unroll
+        for (int i = 0; i < 8 / W; ++i) dma16(bb, off.b[i], lds(bst) + (wave + i * W) * 64);
+#pragma unroll
+        for (int i = 0; i < XC; ++i) dma16(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
+        return;
+    }
+    const int tb = min(tokbase, L - 1);
+    const char* bb = reinterpret_cast<const char*>(bbase + (int64_t)tb * bstride);
+    const char* xb = reinterpret_cast<const char*>(xbase + (int64_t)tb * xstride);
+    const uint32_t bs2 = (uint32_t)bstride * 2u, xs2 = (uint32_t)xstride * 2u;
+#pragma unroll
+    for (int i = 0; i < 8 / W; ++i) {
+        const int k = wave + i * W;
+        const int r = 4 * k + (lane >> 4);
+        const uint32_t dr = (uint32_t)(min(tokbase + r, L - 1) - tb);
+        dma16(bb, dr * bs2 + 16u * (uint32_t)((lane & 15) ^ swz_b(r)), lds(bst) + k * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+        const int k = wave + i * W;
+        const int r = RPC * k + lane / PPR;
+        const uint32_t dr = (uint32_t)(min(tokbase + r, L - 1) - tb);
+        dma16(xb, dr * xs2 + 16u * (uint32_t)((lane % PPR) ^ swz_b(r)), lds(xst) + k * 64);
+    }
+}
+
+template <int Q, int HG>
+__global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t* __restrict__ x,
+                                                                   const bf16_t* __restrict__ Bm,
+                                                                   const float* __restrict__ cs,
+                                                                   const float* __restrict__ dtc,
+                                                                   float* __restrict__ S, int L,
+                                                                   int H, int G, int nc) {
+    constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
+    constexpr int XR = 128 * HG;                         // bytes of a token's x row
+    constexpr int DPS = 8 / W + BxhOffsets<W, HG>::XC;   // copies per wave per stage
+    constexpr int R = kStateRing;
+    __shared__ uint4 bsr[R][512];
+    __shared__ uint4 xsr[R][32 * XR / 16];
+    __shared__ float wv[HG][Q];
+
+    const int HP = H / HG;
+    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int h0 = HG * (int)(wg % (uint32_t)HP);
+    const int bc = (int)(wg / (uint32_t)HP);
+    const int c = bc % nc, b = bc / nc;
+    const int g = h0 / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int64_t row0 = (((int64_t)b * H + h0) * nc + c) * Q;   // head h0 + e: + e * nc * Q
+    const int tok0 = c * Q;
+    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+    const bf16_t* xbase = x + ((int64_t)b * L * H + h0) * P;
+    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
+
+    // ordinary loads first: w_j = exp2(cs_last - cs_j) dt_j for each head
+    float wreg[HG];
+#pragma unroll
+    for (int e = 0; e < HG; ++e) {
+        const int64_t row = row0 + (int64_t)e * nc * Q;
+        wreg[e] = tid < Q ? fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid] : 0.0f;
+    }
+    asm volatile("" ::: "memory");
+    const BxhOffsets<W, HG> off = bxh_offsets<W, HG>(wave, lane, xstride, bstride);
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k)
+        if (k < NT) issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * k, L, xbase, xstride, bbase, bstride, off, bsr[k], xsr[k]);
+    if (tid < Q) {
+#pragma unroll
+        for (int e = 0; e < HG; ++e) wv[e][tid] = wreg[e];
+    }
+
+    const int grp = lane >> 4, rr = lane & 15;
+    const int trow0 = 8 * (grp >> 1) + (rr >> 2);
+    const int qcol = 16 * (grp & 1) + 4 * (rr & 3);
+
+    f32x16 acc[HG][2];   // [head][p tile]
+#pragma unroll
+    for (int e = 0; e < HG; ++e) acc[e][0] = acc[e][1] = f32x16{};
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+        uint4* bst = bsr[jt % R];
+        uint4* xst = xsr[jt % R];
+        const int ahead = (NT - 1 - jt) < (R - 2) ? (NT - 1 - jt) : (R - 2);
+        wait_vmcnt_n(DPS * ahead);   // a constant once the loop is unrolled
+        barrier_lds();
+        if (jt + R - 1 < NT)
+            issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * (jt + R - 1), L, xbase, xstride, bbase, bstride,
+                                   off, bsr[(jt + R - 1) % R], xsr[(jt + R - 1) % R]);
+        const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
+        const SSD_LDS char* bb = (const SSD_LDS char*)lds(bst);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r0 = 16 * u + trow0, r1 = r0 + 4;
+            uint4 bq;
+            {
+                const int nc4 = 32 * wave + qcol;
+                const int chk = nc4 >> 3, sub = (nc4 & 7) * 2;
+                const uint2 lo = tr16(bb + r0 * 256 + ((chk ^ swz_b(r0)) << 4) + sub);
+                const uint2 hi = tr16(bb + r1 * 256 + ((chk ^ swz_b(r1)) << 4) + sub);
+                bq = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+#pragma unroll
+            for (int e = 0; e < HG; ++e) {
+                float wj[8];
+#pragma unroll
+                for (int sidx = 0; sidx < 8; ++sidx) wj[sidx] = wv[e][32 * jt + 16 * u + 8 * hf + sidx];
+                const bf16x8 bw = __builtin_bit_cast(bf16x8, scale_bf16x8(bq, wj));
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int pc = 64 * e + 32 * mt + qcol;
+                    const int chk = pc >> 3, sub = (pc & 7) * 2;
+                    const uint2 lo = tr16(xb + r0 * XR + ((chk ^ swz_b(r0)) << 4) + sub);
+                    const uint2 hi = tr16(xb + r1 * XR + ((chk ^ swz_b(r1)) << 4) + sub);
+                    const bf16x8 xq = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    acc[e][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, bw, acc[e][mt], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    const int n = 32 * wave + l32;
+#pragma unroll
+    for (int e = 0; e < HG; ++e) {
+        float* Sp = S + (((int64_t)b * H + h0 + e) * nc + c) * (int64_t)(P * N);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int p = 8 * (r >> 2) + 4 * hf + (r & 3);
+            __builtin_nontemporal_store(acc[e][0][r], &Sp[p * N + n]);
+            __builtin_nontemporal_store(acc[e][1][r], &Sp[(32 + p) * N + n]);
+        }
     }
 }
 
@@ -248,6 +432,15 @@ hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const
         const bf16_t* xb = static_cast<const bf16_t*>(x);
         const bf16_t* bb = static_cast<const bf16_t*>(B);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
+        if ((d.nheads / d.ngroups) % kStateHeads == 0) {
+            const unsigned hblocks = blocks / (unsigned)kStateHeads;
+            switch (d.chunk) {
+                case 64: chunk_state_mfmah_kernel<64, kStateHeads><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
+                case 128: chunk_state_mfmah_kernel<128, kStateHeads><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
+                default: chunk_state_mfmah_kernel<256, kStateHeads><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
+            }
+            return hipGetLastError();
+        }
         switch (d.chunk) {
             case 64: chunk_state_mfma_kernel<64><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
             case 128: chunk_state_mfma_kernel<128><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;

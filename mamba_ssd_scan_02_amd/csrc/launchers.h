@@ -41,9 +41,7 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream);
 
-// Chunk state and state passing in one pass (bf16 matrix-core path, with
-// enough (batch, head) pairs to fill the machine).
-bool state_scan_supported(int32_t dtype, const Dims& d);
+// Chunk state and state passing in one pass (bf16 matrix-core path, chunk 256).
 hipError_t launch_state_scan(const Dims& d, const void* x, const void* B, const float* cs,
                              const float* dtc, const float* init, void* Hin, float* final_state,
                              hipStream_t stream);

@@ -230,18 +230,6 @@ __global__ __launch_bounds__(256, 3) void state_scan_mfma_kernel(
     }
 }
 
-bool state_scan_supported(int32_t dtype, const Dims& d) {
-    if (!mfma_path(dtype, d) || d.chunk != 256) return false;
-    // one workgroup per (batch, head, half of P) walks the whole sequence:
-    // worth it only with enough of them to fill the machine
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    return (double)d.batch * (double)d.nheads * 2.0 >= 2.0 * cus;
-}
-
 hipError_t launch_state_scan(const Dims& d, const void* x, const void* B, const float* cs,
                              const float* dtc, const float* init, void* Hin, float* final_state,
                              hipStream_t stream) {
