@@ -22,9 +22,9 @@ warm-up steps and the K timed ones.
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (its
 algorithmic bytes per launch over its average launch time, measured here with
 HIP events on the stream it runs on), per-kernel figures, the decode step
-(batch 256, 64 steps), the kernels of the block around the scan (short
-convolution + step, gate) at the same shape, and the fp64 CPU oracle timed on
-a bounded sample.
+(batch 256, 64 steps), the zero-order-hold forward, the kernels of the block
+around the scan (short convolution + step, gate) at the same shape, and the
+fp64 CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -151,20 +151,22 @@ def settle(fn, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
-def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup):
+def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup, zoh=False):
     import torch
-    settle(lambda: ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk,
-                                   g["init"], y=y, final_state=fin, workspace=ws))
-    for _ in range(warmup):
+
+    def step():
         ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk, g["init"], y=y,
-                        final_state=fin, workspace=ws)
+                        final_state=fin, workspace=ws, zoh=zoh)
+
+    settle(step)
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for _ in range(steps):
-        ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk, g["init"], y=y,
-                        final_state=fin, workspace=ws)
+        step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -594,6 +596,10 @@ def main():
                  "algorithmic_flops": flops_total, "wall_s_timed_region": round(wall, 4)},
         "kernels": kernels,
     }
+    log("[bench] zero-order-hold forward")
+    ms_zoh, _ = time_forward(ssd, g, y, fin, ws, Q, args.steps, args.warmup, zoh=True)
+    out["forward_zoh"] = {"us_per_step": round(ms_zoh * 1e3, 2),
+                          "tokens_per_s": round(b * L / (ms_zoh * 1e-3), 1)}
     if not args.no_decode:
         log("[bench] decode")
         out["decode"] = bench_decode(ssd)
