@@ -244,3 +244,29 @@ def test_state_passing_segmented_errors():
     assert lib.ssd_state_passing_seg(1, 1024, 2, 64, 128, 256, 0, 1, vp, vp, None, vp, None, vp,
                                      need, None) == 2
     assert lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 0) == 0
+
+
+def test_state_passing_segmented_long_context():
+    """At the long-context shape (32 chains of 4,096 chunks) the segmented scan
+    gives the sequential kernel's results up to rounding order (the
+    sequential kernel is checked against the oracle by the 1M-token forward)."""
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import LONG_1M as spec
+    say("[state_passing_seg] long context")
+    b, L, H, P, N, Q = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.chunk
+    nc = L // Q
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    dt = torch.nn.functional.softplus(torch.randn(b, L, H, device="cuda", generator=gen) - 4.0)
+    A = -torch.exp(torch.rand(H, device="cuda", generator=gen))
+    cs, _ = ssd.chunk_cumsum(dt, A, Q)
+    del dt
+    S = torch.randn(b, H, nc, P, N, device="cuda", generator=gen) * 0.1
+    init = torch.randn(b, H, P, N, device="cuda", generator=gen) * 0.3
+    Hin, fin = ssd.state_passing(S, cs, L, Q, torch.bfloat16, init)
+    Hin2, fin2 = ssd.state_passing_seg(S, cs, L, Q, torch.bfloat16, 64, init_state=init)
+    e_f = ((fin2 - fin).abs().max() / fin.abs().max()).item()
+    say(f"  final {e_f:.3e}")
+    assert e_f < 1e-5
+    # bf16 entering states: equal up to one rounding step
+    d = (Hin2.float() - Hin.float()).abs()
+    assert bool((d <= Hin.float().abs() * 2.0 ** -7 + 1e-6 * Hin.float().abs().max()).all())
