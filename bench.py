@@ -335,24 +335,26 @@ def bench_state_passing_long(nsegs=(8, 32, 128), steps=10):
 
 def cpu_baseline(inp, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the same workload: whole
-    sequences of (batch, head) pairs, in batches of one pair per core, until
-    the time budget is spent."""
+    sequences of (batch, head) pairs, in batches of one pair per core,
+    cycling over the pairs until the time budget is spent."""
     import oracle
     b, L, H = inp["x"].shape[0], inp["x"].shape[1], inp["x"].shape[2]
     cores = oracle.threads()
     pairs = [(i, h) for i in range(b) for h in range(H)]
-    done, t_total = 0, 0.0
-    while done < len(pairs) and t_total < budget_s:
-        chunk = pairs[done:done + cores]
+    done, t_total, k = 0, 0.0, 0
+    while t_total < budget_s:
+        chunk = [pairs[(k + i) % len(pairs)] for i in range(min(cores, len(pairs)))]
         t0 = time.perf_counter()
         oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"],
                        bh=chunk)
         t_total += time.perf_counter() - t0
         done += len(chunk)
+        k = (k + len(chunk)) % len(pairs)
     tokens_equiv = done * L / H
     return {"value": tokens_equiv / t_total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {len(pairs)} (batch, head) pairs x {L} tokens of the same "
-                      f"workload (= {tokens_equiv:.0f} full-width tokens) in {t_total:.1f} s"}
+            "sample": f"{done} (batch, head) sequences of {L} tokens of the same workload, cycling "
+                      f"over its {len(pairs)} pairs (= {tokens_equiv:.0f} full-width tokens), "
+                      f"in {t_total:.1f} s"}
 
 
 # ----------------------------------------------------------------- profiling
