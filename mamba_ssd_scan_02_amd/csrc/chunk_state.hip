@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
 // and each B fragment read from LDS serves all HG heads (scaled by each
 // head's weights).  Wave w owns state columns n in [32w, 32w+32) of every
 // head.  Wider rows read faster from HBM than one head's 128-byte rows, and B
-// crosses L2 -> LDS once per HG heads.
+// crosses L2 -> LDS once per HG heads.  x is read once, with non-temporal
+// copies (138 -> 132 us at the 2.7B shape).
 template <int W, int HG>
 struct BxhOffsets {
     static constexpr int XC = 4 * HG / W;   // x copies per wave per stage
@@ -194,7 +195,7 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
 #pragma unroll
         for (int i = 0; i < 8 / W; ++i) dma16(bb, off.b[i], lds(bst) + (wave + i * W) * 64);
 #pragma unroll
-        for (int i = 0; i < XC; ++i) dma16(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
+        for (int i = 0; i < XC; ++i) dma16_nt(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
         return;
     }
     const int tb = min(tokbase, L - 1);
@@ -213,7 +214,7 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
         const int k = wave + i * W;
         const int r = RPC * k + lane / PPR;
         const uint32_t dr = (uint32_t)(min(tokbase + r, L - 1) - tb);
-        dma16(xb, dr * xs2 + 16u * (uint32_t)((lane % PPR) ^ swz_b(r)), lds(xst) + k * 64);
+        dma16_nt(xb, dr * xs2 + 16u * (uint32_t)((lane % PPR) ^ swz_b(r)), lds(xst) + k * 64);
     }
 }
 

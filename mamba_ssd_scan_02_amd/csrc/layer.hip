@@ -33,6 +33,10 @@ __device__ __forceinline__ float silu_f(float v) {
 // log(1 + e^v) without overflow: max(v, 0) + log1p(e^-|v|)
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
 
+typedef uint32_t u32x4e __attribute__((ext_vector_type(4)));
+
+// 8 elements of T: raw 16- or 32-byte loads (optionally non-temporal, for
+// data read once), unpacking to fp32, and stores from fp32.
 template <typename T>
 struct Vec8;
 template <>
@@ -40,6 +44,15 @@ struct Vec8<bf16_t> {
     struct Raw { uint4 u; };
     __device__ __forceinline__ static Raw load_raw(const bf16_t* p) {
         return Raw{*reinterpret_cast<const uint4*>(p)};
+    }
+    __device__ __forceinline__ static Raw load_raw_nt(const bf16_t* p) {
+        const u32x4e v = __builtin_nontemporal_load(reinterpret_cast<const u32x4e*>(p));
+        return Raw{make_uint4(v.x, v.y, v.z, v.w)};
+    }
+    __device__ __forceinline__ static void store_nt(bf16_t* p, const float (&v)[8]) {
+        const u32x4e u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7])};
+        __builtin_nontemporal_store(u, reinterpret_cast<u32x4e*>(p));
     }
     __device__ __forceinline__ static void unpack(const Raw& r, float (&v)[8]) {
         const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
@@ -66,6 +79,16 @@ struct Vec8<float> {
     struct Raw { float4 a, b; };
     __device__ __forceinline__ static Raw load_raw(const float* p) {
         return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+    }
+    __device__ __forceinline__ static Raw load_raw_nt(const float* p) {
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+        return Raw{make_float4(a[0], a[1], a[2], a[3]), make_float4(b[0], b[1], b[2], b[3])};
+    }
+    __device__ __forceinline__ static void store_nt(float* p, const float (&v)[8]) {
+        const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+        __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
     }
     __device__ __forceinline__ static void unpack(const Raw& r, float (&v)[8]) {
         v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
@@ -225,7 +248,9 @@ __global__ __launch_bounds__(256) void layer_dt_kernel(const float* __restrict__
 // y and out may be one array (in-place gate), so neither is __restrict__.
 // Each thread takes kOutVec 8-element vectors, a block's vectors being
 // contiguous and each step of the block coalesced; all loads of a full tile
-// are issued before any arithmetic.
+// are issued before any arithmetic.  Every element is touched once, so full
+// tiles use non-temporal loads and stores (172 -> 154 us at the 2.7B shape;
+// the same hint on the convolution's input made no difference).
 constexpr int kOutVec = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void layer_out_vec_kernel(const T* y, const T* __restrict__ z,
@@ -235,8 +260,8 @@ __global__ __launch_bounds__(256) void layer_out_vec_kernel(const T* y, const T*
     if ((int64_t)(blockIdx.x + 1) * (256 * kOutVec) <= n8) {
 #pragma unroll
         for (int v = 0; v < kOutVec; ++v) {
-            ry[v] = Vec8<T>::load_raw(y + 8 * (i0 + 256 * v));
-            rz[v] = Vec8<T>::load_raw(z + 8 * (i0 + 256 * v));
+            ry[v] = Vec8<T>::load_raw_nt(y + 8 * (i0 + 256 * v));
+            rz[v] = Vec8<T>::load_raw_nt(z + 8 * (i0 + 256 * v));
         }
 #pragma unroll
         for (int v = 0; v < kOutVec; ++v) {
@@ -245,7 +270,7 @@ __global__ __launch_bounds__(256) void layer_out_vec_kernel(const T* y, const T*
             Vec8<T>::unpack(rz[v], zv);
 #pragma unroll
             for (int k = 0; k < 8; ++k) yv[k] *= silu_f(zv[k]);
-            Vec8<T>::store(out + 8 * (i0 + 256 * v), yv);
+            Vec8<T>::store_nt(out + 8 * (i0 + 256 * v), yv);
         }
         return;
     }

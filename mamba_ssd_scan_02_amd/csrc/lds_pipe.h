@@ -53,6 +53,20 @@ __device__ __forceinline__ void dma16_rs(__amdgpu_buffer_rsrc_t rs, uint32_t vof
                  : "v"(voff), "s"(rs), "s"(lds_addr(ldst))
                  : "memory", "m0");
 }
+// Non-temporal forms, for data a workgroup reads exactly once (x rows): they
+// leave L2 and the last-level cache to data that is reused.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, SSD_LDS void* ldst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr(ldst))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_rs_nt(__amdgpu_buffer_rsrc_t rs, uint32_t voff, SSD_LDS void* ldst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(lds_addr(ldst))
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void dma4_rs(__amdgpu_buffer_rsrc_t rs, uint32_t voff, SSD_LDS void* ldst) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :
