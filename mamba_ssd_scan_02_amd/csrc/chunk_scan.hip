@@ -725,7 +725,8 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
     // Copies of head k into the slot at byte offset so, in four parts (x
     // rows 0..127, x rows 128..255, Hin, cs/dt); past the run's last head
     // they read empty records (zeros, no memory traffic), which keeps every
-    // wait count fixed.  x is read once: non-temporal copies.
+    // wait count fixed.  (Non-temporal x copies were 1% faster alone and made
+    // the whole forward 1-2% slower.)
     auto issue_part = [&](int k, uint32_t so, int part) {
         const bool real = k < cnt;
         const int h = h0 + (real ? k : 0);
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
                 make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, real ? xrecord : 0);
 #pragma unroll
             for (int i = 4 * part; i < 4 * part + 4; ++i)
-                dma16_rs_nt(rx, xo0 + (uint32_t)i * xstep, s + rsl::kX + (4 * i + wave) * 1024);
+                dma16_rs(rx, xo0 + (uint32_t)i * xstep, s + rsl::kX + (4 * i + wave) * 1024);
         } else if (part == 2) {
             const __amdgpu_buffer_rsrc_t rh =
                 make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), real ? P * N * 2 : 0);
