@@ -218,13 +218,21 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
     }
 }
 
-template <int Q, int HG>
+// FUSE: the workgroup also forms its heads' chunk cumsum (what
+// chunk_cumsum_kernel computes) from dt and A instead of reading cs and dtc:
+// an fp64 inclusive prefix of dt A log2(e) over the chunk's tokens (a wave
+// scan, then the wave totals), rounded once to fp32, and dt (or its
+// zero-order-hold weight) as dtc.  Both rows are written out at the end for
+// the later stages.
+template <int Q, int HG, bool FUSE>
 __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t* __restrict__ x,
                                                                    const bf16_t* __restrict__ Bm,
-                                                                   const float* __restrict__ cs,
-                                                                   const float* __restrict__ dtc,
+                                                                   const float* cs, const float* dtc,
                                                                    float* __restrict__ S, int L,
-                                                                   int H, int G, int nc) {
+                                                                   int H, int G, int nc,
+                                                                   const float* __restrict__ dtin,
+                                                                   const float* __restrict__ A,
+                                                                   float* csw, float* dtcw, int zoh) {
     constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
     constexpr int XR = 128 * HG;                         // bytes of a token's x row
     constexpr int DPS = 8 / W + BxhOffsets<W, HG>::XC;   // copies per wave per stage
@@ -248,18 +256,64 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     const bf16_t* xbase = x + ((int64_t)b * L * H + h0) * P;
     const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
 
-    // ordinary loads first: w_j = exp2(cs_last - cs_j) dt_j for each head
+    // ordinary loads first (their values are used, so waited for, before the
+    // copies are issued): w_j = exp2(cs_last - cs_j) dt_j for each head
     float wreg[HG];
+    float csv[HG], dcv[HG];    // FUSE: this thread's token's cs and dtc
+    __shared__ double wsum[HG][4];
+    __shared__ float cslast[HG];
+    double v[HG];              // FUSE: dt A log2(e) of this thread's token, then its prefix
+    if constexpr (FUSE) {
+        float dl[HG];
+        const int t = tok0 + tid;
+        const bool in = tid < Q && t < L;
+        const float* dsrc = dtin + ((int64_t)b * L + min(t, L - 1)) * H + h0;
 #pragma unroll
-    for (int e = 0; e < HG; ++e) {
-        const int64_t row = row0 + (int64_t)e * nc * Q;
-        wreg[e] = tid < Q ? fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid] : 0.0f;
+        for (int e = 0; e < HG; ++e) dl[e] = dsrc[e];   // both loads in flight together
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const float d = in ? dl[e] : 0.0f;
+            const float ah = A[h0 + e];
+            dcv[e] = zoh ? zoh_weight(d, ah) : d;
+            v[e] = (double)d * ((double)ah * 1.4426950408889634074);
+            asm volatile("" : "+v"(v[e]), "+v"(dcv[e]));   // formed (loads waited for) here
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const int64_t row = row0 + (int64_t)e * nc * Q;
+            wreg[e] = tid < Q ? fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid] : 0.0f;
+        }
     }
     asm volatile("" ::: "memory");
     const BxhOffsets<W, HG> off = bxh_offsets<W, HG>(wave, lane, xstride, bstride);
 #pragma unroll
     for (int k = 0; k < R - 1; ++k)
         if (k < NT) issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * k, L, xbase, xstride, bbase, bstride, off, bsr[k], xsr[k]);
+    if constexpr (FUSE) {
+        // the prefix while the first copies are in flight (LDS-only barriers:
+        // a full barrier would wait for the copies)
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+#pragma unroll
+            for (int off2 = 1; off2 < 64; off2 <<= 1) {
+                const double o = __shfl_up(v[e], off2, 64);
+                if (lane >= off2) v[e] += o;
+            }
+            if (lane == 63) wsum[e][wave] = v[e];
+        }
+        barrier_lds();
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            double base = 0.0;
+            for (int w2 = 0; w2 < wave; ++w2) base += wsum[e][w2];
+            csv[e] = (float)(base + v[e]);
+            if (tid == Q - 1) cslast[e] = csv[e];
+        }
+        barrier_lds();
+#pragma unroll
+        for (int e = 0; e < HG; ++e) wreg[e] = tid < Q ? fast_exp2(cslast[e] - csv[e]) * dcv[e] : 0.0f;
+    }
     if (tid < Q) {
 #pragma unroll
         for (int e = 0; e < HG; ++e) wv[e][tid] = wreg[e];
@@ -314,6 +368,16 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
         }
     }
 
+    if constexpr (FUSE) {   // the cumsum rows, after every copy (they would skew the wait counts)
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const int64_t row = row0 + (int64_t)e * nc * Q;
+            if (tid < Q) {
+                csw[row + tid] = csv[e];
+                dtcw[row + tid] = dcv[e];
+            }
+        }
+    }
     const int n = 32 * wave + l32;
 #pragma unroll
     for (int e = 0; e < HG; ++e) {
@@ -426,6 +490,26 @@ bool generic_path(const Dims& d) {
            d.chunk >= 1 && d.chunk <= 256;
 }
 
+bool chunk_state_fuses_cumsum(int32_t dtype, const Dims& d) {
+    return mfma_path(dtype, d) && (d.nheads / d.ngroups) % kStateHeads == 0;
+}
+
+hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B, const float* dt,
+                                    const float* A, bool zoh, float* cs, float* dtc, float* S,
+                                    hipStream_t stream) {
+    const unsigned hblocks = (unsigned)(d.batch * d.nchunks * d.nheads / kStateHeads);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* bb = static_cast<const bf16_t*>(B);
+    const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
+    const int z = zoh ? 1 : 0;
+    switch (d.chunk) {
+        case 64: chunk_state_mfmah_kernel<64, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
+        case 128: chunk_state_mfmah_kernel<128, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
+        default: chunk_state_mfmah_kernel<256, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const void* B,
                               const float* cs, const float* dtc, float* S, hipStream_t stream) {
     if (mfma_path(dtype, d)) {
@@ -436,9 +520,9 @@ hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const
         if ((d.nheads / d.ngroups) % kStateHeads == 0) {
             const unsigned hblocks = blocks / (unsigned)kStateHeads;
             switch (d.chunk) {
-                case 64: chunk_state_mfmah_kernel<64, kStateHeads><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
-                case 128: chunk_state_mfmah_kernel<128, kStateHeads><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
-                default: chunk_state_mfmah_kernel<256, kStateHeads><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
+                case 64: chunk_state_mfmah_kernel<64, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
+                case 128: chunk_state_mfmah_kernel<128, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
+                default: chunk_state_mfmah_kernel<256, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
             }
             return hipGetLastError();
         }

@@ -24,6 +24,13 @@ hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, f
 hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const void* B,
                               const float* cs, const float* dtc, float* S, hipStream_t stream);
 
+// Chunk state that also forms the chunk cumsum (cs, dtc written for the
+// later stages), where the paired-head matrix-core kernel applies.
+bool chunk_state_fuses_cumsum(int32_t dtype, const Dims& d);
+hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B, const float* dt,
+                                    const float* A, bool zoh, float* cs, float* dtc, float* S,
+                                    hipStream_t stream);
+
 hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, const float* cs,
                                 const float* init, void* Hin, float* final_state,
                                 hipStream_t stream);

@@ -296,12 +296,19 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     float* S = reinterpret_cast<float*>(ws + lo.S);
     void* Hin = ws + lo.Hin;
 
-    hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, zoh);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-    // chunk states, then the recurrence between chunks (the one-pass
+    // chunk cumsum and chunk states (one launch where the paired-head kernel
+    // applies), then the recurrence between chunks (the one-pass
     // ssd_state_scan measured slower than this pair at every shape tried)
-    e = ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream);
-    if (e != hipSuccess) return SSD_ERR_HIP;
+    hipError_t e;
+    if (ssd::chunk_state_fuses_cumsum(dtype, d)) {
+        e = ssd::launch_chunk_state_fused(d, x, B, dt, A, zoh, cs, dtc, S, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    } else {
+        e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, zoh);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        e = ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    }
     e = ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream);
     if (e != hipSuccess) return SSD_ERR_HIP;
     e = ssd::launch_chunk_scan(d, dtype, x, B, C, cs, dtc, Hin, D, y, stream);
