@@ -404,6 +404,8 @@ def profile_loop(k: int):
 
 
 def _short_kernel(name: str) -> str:
+    if "chunk_state" in name and ", true>" in name:
+        return "chunk_state+cumsum"   # the forward's chunk state with the cumsum inside
     for k in KERNEL_SOURCES:
         if k in name:
             return k
