@@ -254,7 +254,7 @@ def bench_decode(ssd, steps_warm=3):
     }
 
 
-def bench_layer(ssd, spec, steps=20):
+def bench_layer(ssd, spec, steps=20, block=True):
     """ssd_layer_in (convolution + step kernels) and ssd_layer_out at the
     forward workload's shape, filter width LAYER_K, timed with HIP events on
     the stream they run on."""
@@ -288,6 +288,29 @@ def bench_layer(ssd, spec, steps=20):
         res[name] = {"us": round(us, 2), "alg_bytes": byts, "GBps": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     res["kernel_width"] = LAYER_K
+    if not block:
+        return res
+    # the whole block: layer_in -> ssd_forward -> layer_out (in place)
+    A, D, init = li["A"], li["D"], li.get("init")
+    y = torch.empty_like(x)
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ssd.workspace_bytes(b, L, H, P, N, G, spec.chunk, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def block():
+        run_in()
+        ssd.ssd_forward(x, dt, A, Bm, Cm, D, spec.chunk, init, y=y, final_state=fin, workspace=ws)
+        ssd.layer_out(y, li["z"], out=y)
+
+    settle(block, 0.1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        block()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    res["block"] = {"us": round(us, 2), "tokens_per_s": round(b * L / (us * 1e-6), 1)}
     return res
 
 
@@ -394,7 +417,7 @@ def profile_loop(k: int):
     for _ in range(k):
         ssd.ssm_step(state, s0["x"], s0["dt"], A, s0["B"], s0["C"], D)
     del g, y, ws
-    bench_layer(ssd, spec, steps=k)
+    bench_layer(ssd, spec, steps=k, block=False)
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(k):
