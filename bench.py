@@ -197,7 +197,7 @@ def time_stages(ssd, g, y, fin, ws, dims, steps):
     base = ws.data_ptr()
     cs, dtc, S, Hin = (ctypes.c_void_p(base + reg[k][0]) for k in ("cs", "dtc", "S", "Hin"))
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    p = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
     names = ["chunk_cumsum", "chunk_state", "state_passing", "state_scan", "chunk_scan"]
     calls = [
         lambda: lib.ssd_chunk_cumsum(b, L, H, Q, p(g["dt"]), p(g["A"]), cs, dtc, stream),
@@ -536,6 +536,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--workload", default="mamba2_2p7b_b4_l8192_h80_p64_n128",
+                    choices=["mamba2_2p7b_b4_l8192_h80_p64_n128", "mamba2_130m_b8_l2048_h24_p64_n128"],
+                    help="forward workload (the default is the headline one; the other prints "
+                         "the same line for the 130M-shaped layer)")
     ap.add_argument("--state-passing-long", action="store_true",
                     help="only compare sequential and segmented state passing at the "
                          "long-context shape")
@@ -563,8 +567,8 @@ def main():
     import torch
 
     import mamba_ssd_scan_02_amd as ssd
-    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as spec
-    from mamba_ssd_scan_02_amd.workloads import make_forward_inputs
+    from mamba_ssd_scan_02_amd.workloads import FORWARD_SPECS, make_forward_inputs
+    spec = FORWARD_SPECS[args.workload]
 
     ssd.load()
     if not torch.cuda.is_available():
@@ -580,12 +584,13 @@ def main():
     b, L, H, P, N, G, Q = dims
     log(f"[bench] generating {spec.name}")
     inp = make_forward_inputs(spec)
-    g = {k: v.cuda() for k, v in inp.items()}
+    g = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y = torch.empty_like(g["x"])
     fin = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
     ws = torch.empty(ssd.workspace_bytes(b, L, H, P, N, G, Q, torch.bfloat16), dtype=torch.uint8,
                      device="cuda")
     torch.cuda.synchronize()
+    headline = spec.name == "mamba2_2p7b_b4_l8192_h80_p64_n128"
 
     log(f"[bench] forward: {args.warmup} warmup + {args.steps} timed steps")
     ms, wall = time_forward(ssd, g, y, fin, ws, Q, args.steps, args.warmup)
@@ -615,7 +620,8 @@ def main():
     flops_total = sum(kflops[n] for n in path)
 
     out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC if headline else f"SSD fwd tokens/s at {spec.name}",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; x,dt,B,C,D,A,init drawn from the workload's distributions)",
