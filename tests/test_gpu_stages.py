@@ -270,3 +270,14 @@ def test_state_passing_segmented_long_context():
     # bf16 entering states: equal up to one rounding step
     d = (Hin2.float() - Hin.float()).abs()
     assert bool((d <= Hin.float().abs() * 2.0 ** -7 + 1e-6 * Hin.float().abs().max()).all())
+
+
+def test_state_passing_segmented_deterministic():
+    import mamba_ssd_scan_02_amd as ssd
+    inp = _inputs(43, 2, 1000, 3, 64, 128, 1, "bf16")
+    g = to_gpu(inp)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], 64)
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, 64)
+    r1 = ssd.state_passing_seg(S, cs, 1000, 64, torch.bfloat16, 5, init_state=g["init"])
+    r2 = ssd.state_passing_seg(S, cs, 1000, 64, torch.bfloat16, 5, init_state=g["init"])
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
