@@ -198,3 +198,22 @@ def test_segmented_state_passing_argument_errors(lib):
     assert seg(Hin=0x400008) == ALIGN
     # more segments than chunks act as one per chunk (4 here): the same workspace suffices
     assert lib.ssd_state_passing_seg_workspace_bytes(1, 2, 64, 128, 4) == need
+
+
+def test_plain_c_caller(tmp_path):
+    """The header compiles as C99 and a C program linked against the library
+    gets the documented results from the calls that need no GPU."""
+    import shutil
+    import mamba_ssd_scan_02_amd as ssd
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc is not available")
+    root = Path(__file__).resolve().parents[1]
+    libdir = ssd.library_path().parent
+    exe = tmp_path / "abi_smoke"
+    cmd = ["gcc", "-std=c99", "-D__HIP_PLATFORM_AMD__", f"-I{root / 'include'}",
+           "-I/opt/rocm/include", str(root / "tests" / "c" / "abi_smoke.c"), "-o", str(exe),
+           f"-L{libdir}", "-lssd_mi355x", f"-Wl,-rpath,{libdir}"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "abi_smoke: ok" in out.stdout
