@@ -9,6 +9,7 @@ Profiling helpers (see profiles/):
                                           1 GiB device copy for calibration
     python bench.py --summarize-trace DIR --out FILE
     python bench.py --summarize-counters DIR_FETCH DIR_WRITE --out-dir profiles
+    python bench.py --summarize-sq DIR --out-dir profiles
     python bench.py --state-passing-long  sequential vs segmented state passing
                                           at the long-context shape
 
@@ -527,6 +528,47 @@ def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str,
         print(text)
 
 
+SQ_COUNTERS = ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+               "SQ_VALU_MFMA_BUSY_CYCLES"]
+
+
+def summarize_sq(d: str, out_dir: str, cmd: str):
+    """Per-kernel issue profile from one rocprofv3 --pmc pass over SQ_COUNTERS:
+    averages per dispatch, and the wait / VALU / LDS / VMEM shares of the
+    waves' cycles (as the counters report them, summed over the device)."""
+    import csv
+    import glob
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B, DECODE_B256
+    f = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for r in csv.DictReader(open(f[0])):
+        k = _short_kernel(r["Kernel_Name"])
+        if k not in KERNEL_SOURCES and k != "chunk_state+cumsum":
+            continue
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for k, cnt in acc.items():
+        avg = {c: sum(v) / len(v) for c, v in cnt.items()}
+        wc = avg.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        wl = DECODE_B256.name if k == "ssm_step" else MAMBA2_2P7B.name
+        lines = [f"# issue profile of {k} on {wl} (rocprofv3 SQ counters, per dispatch)",
+                 f"command: {cmd}",
+                 f"dispatches: {len(next(iter(cnt.values())))}"]
+        for c in SQ_COUNTERS:
+            if c in avg:
+                lines.append(f"{c}: {avg[c]:.6g}")
+        for c, label in (("SQ_WAIT_ANY", "waiting"), ("SQ_WAIT_INST_ANY", "waiting to issue"),
+                         ("SQ_ACTIVE_INST_VALU", "issuing VALU"), ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
+                         ("SQ_ACTIVE_INST_VMEM", "issuing VMEM")):
+            if c in avg:
+                lines.append(f"share_of_wave_cycles_{label.replace(' ', '_')}: {avg[c] / wc:.4f}")
+        name = "chunk_state_cumsum" if k == "chunk_state+cumsum" else k
+        Path(out_dir, f"{name}_{wl}_issue.txt").write_text("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+
 # ---------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -546,6 +588,7 @@ def main():
     ap.add_argument("--profile-loop", type=int, default=0)
     ap.add_argument("--summarize-trace", default=None)
     ap.add_argument("--summarize-counters", nargs=2, default=None)
+    ap.add_argument("--summarize-sq", default=None)
     ap.add_argument("--out", default=None)
     ap.add_argument("--out-dir", default="profiles")
     ap.add_argument("--cmd", default="", help="command recorded in a summary")
@@ -553,6 +596,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.cmd)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.out_dir, args.cmd)
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.out_dir,
