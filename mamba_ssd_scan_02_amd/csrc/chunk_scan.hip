@@ -591,62 +591,57 @@ __device__ __forceinline__ void rs_fetch_x(SlotX& o, const SSD_LDS char* xb, XtA
 }
 
 // Weights of one slot as the B operand of its products (bf16 pairs): the
-// resident G^T tile gt times rf_j (the common case, rs_weights_fast), or,
-// for a diagonal block or a tile with too much decay to factorise, the
-// masked or direct form (rs_weights_special).
-__device__ __forceinline__ void rs_weights_fast(u32x4v (&gq)[2], const f32x16& gt, const SlotRf& in) {
+// resident G^T tile gt times rf_j, plus D' on the entry j == i of a
+// diagonal block (rs_weights_fact; the causal mask of the diagonal blocks is
+// already in gt), or, for a tile with too much decay to factorise, the
+// direct form (rs_weights_direct).  Register r of a lane holds the entry
+// j - 8 hf = 16 (r / 8) + r % 8 of column i = l32 of the block.
+__device__ __forceinline__ void rs_weights_fact(u32x4v (&gq)[2], const f32x16& gt, const SlotRf& in,
+                                                bool dgb, float dprime) {
     auto rf = [&](int r) {
         const f32x4 q = r < 4 ? in.f[0] : (r < 8 ? in.f[1] : (r < 12 ? in.f[2] : in.f[3]));
         return q[r & 3];
     };
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = gt[r] * rf(r);
+    if (dgb) {
+        // register r holds j == i in two fixed lanes (and only there): in
+        // lanes r and 40 + r for r < 8, in lanes r + 8 and 48 + r above;
+        // a select on that constant lane mask takes no compare
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint64_t m = r < 8 ? (1ull << r) | (1ull << (40 + r)) : (1ull << (r + 8)) | (1ull << (48 + r));
+            float d;
+            asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(v[r]), "v"(v[r] + dprime), "s"(m));
+            v[r] = d;
+        }
+    }
     uint32_t pk[8];
 #pragma unroll
-    for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(gt[2 * r2] * rf(2 * r2), gt[2 * r2 + 1] * rf(2 * r2 + 1));
+    for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
     gq[0] = u32x4v{pk[0], pk[1], pk[2], pk[3]};
     gq[1] = u32x4v{pk[4], pk[5], pk[6], pk[7]};
 }
-__device__ __forceinline__ void rs_weights_special(u32x4v (&gq)[2], const f32x16& gt, const SlotRf& in,
-                                                   const SSD_LDS float* csb, const SSD_LDS float* dtb,
-                                                   const TileF& tf, float csi, float Dh, bool dgb, int hf,
-                                                   int l32) {
+__device__ __forceinline__ void rs_weights_direct(u32x4v (&gq)[2], const f32x16& gt,
+                                                  const SSD_LDS float* csb, const SSD_LDS float* dtb,
+                                                  float csi, float Dh, bool dgb, int hf, int l32) {
+    // gt is zero above the diagonal of a diagonal block
+    const SSD_LDS float* cb = csb + 8 * hf;
+    const SSD_LDS float* db = dtb + 8 * hf;
+    const uint32_t deq = dgb ? diag_eq_bits(l32, hf) : 0u;
     uint32_t pk[8];
-    if (tf.fact) {
-        // diagonal block: causal mask j <= i and D on j == i; with
-        // t = l32 - 8 hf, register r holds j - 8 hf = 16 (r / 8) + r % 8
-        auto rf = [&](int r) {
-            const f32x4 q = r < 4 ? in.f[0] : (r < 8 ? in.f[1] : (r < 12 ? in.f[2] : in.f[3]));
-            return q[r & 3];
-        };
-        int tcol = l32 - 8 * hf;
-        asm volatile("" : "+v"(tcol));
-        float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int jr = 16 * (r >> 3) + (r & 7);
-            const float w = (tcol >= jr) ? gt[r] * rf(r) : 0.0f;
-            v[r] = (tcol == jr) ? w + tf.dprime : w;
+    for (int r2 = 0; r2 < 8; ++r2) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = 2 * r2 + e;
+            const int jl = 16 * (r >> 3) + (r & 7);
+            const float df = (float)((deq >> r) & 1u);
+            v2[e] = gt[r] * (fast_exp2(fminf(csi - cb[jl], 0.0f)) * db[jl]) + Dh * df;
         }
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
-    } else {
-        // direct weights for a tile with too much decay to factorise
-        const SSD_LDS float* cb = csb + 8 * hf;
-        const SSD_LDS float* db = dtb + 8 * hf;
-        const uint32_t keep = dgb ? diag_keep_bits(l32, hf) : 0xffffu;
-        const uint32_t deq = dgb ? diag_eq_bits(l32, hf) : 0u;
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2) {
-            float v2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int r = 2 * r2 + e;
-                const int jl = 16 * (r >> 3) + (r & 7);
-                const float kf = (float)((keep >> r) & 1u);
-                const float df = (float)((deq >> r) & 1u);
-                v2[e] = gt[r] * (fast_exp2(fminf(csi - cb[jl], 0.0f)) * db[jl] * kf) + Dh * df;
-            }
-            pk[r2] = pack_bf16x2(v2[0], v2[1]);
-        }
+        pk[r2] = pack_bf16x2(v2[0], v2[1]);
     }
     gq[0] = u32x4v{pk[0], pk[1], pk[2], pk[3]};
     gq[1] = u32x4v{pk[4], pk[5], pk[6], pk[7]};
@@ -793,6 +788,13 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
                 for (int kk = 0; kk < 8; ++kk)
                     a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bs[kk]), __builtin_bit_cast(bf16x8, cf[0][kk]), a, 0, 0, 0);
             }
+            if (s == 8 || s == 7 - wave) {
+                // a diagonal block: its causal mask j <= i does not depend
+                // on the head, so it is applied here once
+                const int tcol = l32 - 8 * hf;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) a[r] = tcol >= 16 * (r >> 3) + (r & 7) ? a[r] : 0.0f;
+            }
             gt[s] = a;
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -890,10 +892,10 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
             const bool first = s < 8 - wave;
             const bool dgb = first ? (s == 7 - wave) : (s == 8);
             u32x4v gq[2];
-            rs_weights_fast(gq, gt[s], rc);
-            if (dgb || !(first ? tf[1].fact : tf[0].fact))
-                rs_weights_special(gq, gt[s], rc, css + 32 * jt, dts + 32 * jt, first ? tf[1] : tf[0],
-                                   first ? csi[1] : csi[0], Dh, dgb, hf_o, l32_o);
+            rs_weights_fact(gq, gt[s], rc, dgb, first ? tf[1].dprime : tf[0].dprime);
+            if (!(first ? tf[1].fact : tf[0].fact))
+                rs_weights_direct(gq, gt[s], css + 32 * jt, dts + 32 * jt, first ? csi[1] : csi[0], Dh,
+                                  dgb, hf_o, l32_o);
             if (first) {
                 rs_products(acc[1], xc, gq);
                 if (s == 7 - wave) rs_store(acc[1], tf[1].colf, yrs, rowbytes, t1, hf_o, l32_o);
