@@ -579,9 +579,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--workload", default="mamba2_2p7b_b4_l8192_h80_p64_n128",
-                    choices=["mamba2_2p7b_b4_l8192_h80_p64_n128", "mamba2_130m_b8_l2048_h24_p64_n128"],
-                    help="forward workload (the default is the headline one; the other prints "
-                         "the same line for the 130M-shaped layer)")
+                    choices=["mamba2_2p7b_b4_l8192_h80_p64_n128", "mamba2_130m_b8_l2048_h24_p64_n128",
+                             "long_b1_l1048576_h32_p64_n128_g8"],
+                    help="forward workload (the default is the headline one; the others print "
+                         "the same line for the 130M-shaped layer and for one 1M-token sequence, "
+                         "the latter without the block around the scan and the oracle baseline, "
+                         "whose host-side inputs or fp64 work do not fit a short run)")
     ap.add_argument("--state-passing-long", action="store_true",
                     help="only compare sequential and segmented state passing at the "
                          "long-context shape")
@@ -615,6 +618,8 @@ def main():
     import mamba_ssd_scan_02_amd as ssd
     from mamba_ssd_scan_02_amd.workloads import FORWARD_SPECS, make_forward_inputs
     spec = FORWARD_SPECS[args.workload]
+    if spec.seqlen > 65536:
+        args.no_layer = args.no_cpu_baseline = True
 
     ssd.load()
     if not torch.cuda.is_available():

@@ -109,6 +109,44 @@ def test_chunk_scan_head_runs():
         assert e < TOL["bf16"], (h, e)
 
 
+def test_chunk_scan_head_runs_strong_decay():
+    """The head-run path with step sizes that make some 32-token tiles decay
+    by far more than 2^64 (45-token windows at dt = 2.5 with A = -1, i.e.
+    3.6 log2 units per token, between windows at dt = 0.05): those tiles,
+    diagonal ones included, take the direct per-element weights and the
+    rest the factorised ones.  First and last heads of both runs against the
+    oracle over every chunk."""
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    batch, L, H, P, N, G, Q = 1, 128 * 256 - 37, 25, 64, 128, 1, 256
+    say("[stages] chunk_scan head runs, strong decay")
+    inp = _inputs(14, batch, L, H, P, N, G, "bf16")
+    t = np.arange(L)
+    win = np.where((t // 45) % 3 == 0, 2.5, 0.05).astype(np.float32)
+    shift = np.arange(H) * 7                      # each head's windows start elsewhere
+    dt = np.stack([np.roll(win, int(k)) for k in shift], axis=1)[None]
+    inp["dt"] = torch.from_numpy(np.ascontiguousarray(dt))
+    inp["A"] = torch.full((H,), -1.0, dtype=torch.float32)
+    g = to_gpu(inp)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
+    Hin, _ = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"])
+    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], Q).cpu()
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    # both kinds of tile occur: some decay by more than 2^64, most by less
+    tile_decay = (Acs[..., ::32] - Acs[..., 31::32]) * LOG2E
+    assert (tile_decay > 64).any() and (tile_decay < 64).any()
+    Hn = Hin.cpu().double().numpy()
+    for h in (0, 12, 13, 24):
+        sl = slice(h, h + 1)
+        y_ref = stages.chunk_scan(inp["x"][:, :, sl], inp["dt"][:, :, sl], inp["B"], inp["C"],
+                                  Acs[:, sl], Hn[:, sl], inp["D"][sl], Q)
+        e = max_rel_err(y[:, :, sl], y_ref)
+        say(f"  head {h}: max rel err {e:.3e}")
+        assert e < TOL["bf16"], (h, e)
+
+
 def test_stage_intermediates_deterministic():
     import mamba_ssd_scan_02_amd as ssd
     inp = _inputs(12, 1, 512, 4, 64, 128, 1, "bf16")
