@@ -106,6 +106,36 @@ __device__ __forceinline__ uint32_t diag_eq_bits(int l32, int hf) {
     return 0u;
 }
 
+// The same two sets as lane masks of one register r of a diagonal block,
+// constant for every wave (register r holds j - 8 hf = 16 (r / 8) + r % 8
+// of column i = l32): j <= i holds in lanes l32 >= jr of the first half
+// and l32 >= jr + 8 of the second; j == i in lanes r and 40 + r (r < 8) or
+// r + 8 and 48 + r (r >= 8).
+__host__ __device__ constexpr uint64_t diag_keep_lanes(int r) {
+    return ((0xffffffffull << (16 * (r >> 3) + (r & 7))) & 0xffffffffull) |
+           (((0xffffffffull << (16 * (r >> 3) + (r & 7) + 8)) & 0xffffffffull) << 32);
+}
+__host__ __device__ constexpr uint64_t diag_eq_lanes(int r) {
+    return r < 8 ? (1ull << r) | (1ull << (40 + r)) : (1ull << (r + 8)) | (1ull << (48 + r));
+}
+constexpr bool diag_lanes_match() {
+    for (int r = 0; r < 16; ++r)
+        for (int lane = 0; lane < 64; ++lane) {
+            const int t = (lane & 31) - 8 * (lane >> 5), jr = 16 * (r >> 3) + (r & 7);
+            if ((((diag_keep_lanes(r) >> lane) & 1u) != 0) != (t >= jr)) return false;
+            if ((((diag_eq_lanes(r) >> lane) & 1u) != 0) != (t == jr)) return false;
+        }
+    return true;
+}
+static_assert(diag_lanes_match(), "diagonal lane masks disagree with the register layout");
+
+// b in the lanes of mask m, a elsewhere: one select, no compare.
+__device__ __forceinline__ float lane_select(float a, float b, uint64_t m) {
+    float d;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(m));
+    return d;
+}
+
 // C fragments of the wave's own tokens (B operand of both C products).
 // Tokens past the end of the sequence re-read the last token: C_i only
 // reaches output column i, which is not stored for those tokens.
@@ -225,16 +255,13 @@ __device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const ui
                 for (int r2 = 0; r2 < 8; ++r2)
                     pk[r2] = pack_bf16x2(gacc[t][2 * r2] * rf[2 * r2], gacc[t][2 * r2 + 1] * rf[2 * r2 + 1]);
             } else {
-                // causal mask j <= i and D on j == i; with t = l32 - 8 hf,
-                // register r holds j - 8 hf = 16 (r / 8) + r % 8
-                int tcol = l32 - 8 * hf;
-                asm volatile("" : "+v"(tcol));   // compares stay inside this block
+                // causal mask j <= i and D on j == i, selects on constant
+                // lane masks
                 float v[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int jr = 16 * (r >> 3) + (r & 7);
-                    const float w = (tcol >= jr) ? gacc[t][r] * rf[r] : 0.0f;
-                    v[r] = (tcol == jr) ? w + tf[t].dprime : w;
+                    const float w = lane_select(0.0f, gacc[t][r] * rf[r], diag_keep_lanes(r));
+                    v[r] = lane_select(w, w + tf[t].dprime, diag_eq_lanes(r));
                 }
 #pragma unroll
                 for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
@@ -606,16 +633,8 @@ __device__ __forceinline__ void rs_weights_fact(u32x4v (&gq)[2], const f32x16& g
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = gt[r] * rf(r);
     if (dgb) {
-        // register r holds j == i in two fixed lanes (and only there): in
-        // lanes r and 40 + r for r < 8, in lanes r + 8 and 48 + r above;
-        // a select on that constant lane mask takes no compare
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint64_t m = r < 8 ? (1ull << r) | (1ull << (40 + r)) : (1ull << (r + 8)) | (1ull << (48 + r));
-            float d;
-            asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(v[r]), "v"(v[r] + dprime), "s"(m));
-            v[r] = d;
-        }
+        for (int r = 0; r < 16; ++r) v[r] = lane_select(v[r], v[r] + dprime, diag_eq_lanes(r));
     }
     uint32_t pk[8];
 #pragma unroll
@@ -791,9 +810,8 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
             if (s == 8 || s == 7 - wave) {
                 // a diagonal block: its causal mask j <= i does not depend
                 // on the head, so it is applied here once
-                const int tcol = l32 - 8 * hf;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] = tcol >= 16 * (r >> 3) + (r & 7) ? a[r] : 0.0f;
+                for (int r = 0; r < 16; ++r) a[r] = lane_select(0.0f, a[r], diag_keep_lanes(r));
             }
             gt[s] = a;
             __builtin_amdgcn_sched_barrier(0);
