@@ -275,9 +275,7 @@ def bench_layer(ssd, spec, steps=20, block=True):
     mb = layer_model(b, L, H, P, N, G, LAYER_K)
     for name, fn, byts in (("layer_in", run_in, mb["layer_in"]),
                            ("layer_out", run_out, mb["layer_out"])):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        settle(fn, 0.2)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
