@@ -359,6 +359,41 @@ __host__ __device__ constexpr int scan_ops_after(int NT, int jt, bool more, int 
     return n;
 }
 
+// The streaming kernel's issue order for a run of hg heads (labels: stage s
+// of head h, carried state, cs/dt rows, y stores), replayed against the
+// counts above: each step's stage, and before the next head its carried
+// state and rows, must have landed.
+constexpr bool scan_waits_hold(int NT, int W, int hg) {
+    const int DPS = 12 / W, DH = 16 / W, DC = 2, NY = 8;
+    auto stage = [](int h, int s) { return 1000 + 16 * h + s; };
+    auto hin = [](int h) { return 2000 + h; };
+    auto rows = [](int h) { return 3000 + h; };
+    VmemLog o;
+    o.push(rows(0), DC);
+    o.push(hin(0), DH);
+    for (int s = 0; s < 3; ++s) o.push(stage(0, s), DPS);
+    if (!o.wait(0)) return false;
+    for (int hi = 0; hi < hg; ++hi) {
+        const bool more = hi + 1 < hg;
+        for (int jt = 0; jt < NT; ++jt) {
+            if (!o.wait(scan_ops_after(NT, jt, more, DPS, DH, DC, NY)) || !o.landed(stage(hi, jt))) return false;
+            if (jt + 3 < NT) o.push(stage(hi, jt + 3), DPS);
+            else if (more) o.push(stage(hi + 1, jt + 3 - NT), DPS);
+            if (jt == 0 && more) {
+                o.push(hin(hi + 1), DH);
+                o.push(rows(hi + 1), DC);
+            }
+        }
+        o.push(4000 + hi, NY);
+        if (more && (!o.wait((NT - 1) * DPS + NY) || !o.landed(hin(hi + 1)) || !o.landed(rows(hi + 1))))
+            return false;
+    }
+    return true;
+}
+static_assert(scan_waits_hold(8, 4, 1) && scan_waits_hold(8, 4, 2) && scan_waits_hold(8, 4, 5) &&
+              scan_waits_hold(4, 2, 1) && scan_waits_hold(4, 2, 2) && scan_waits_hold(4, 2, 5),
+              "chunk_scan wait counts do not cover its copies");
+
 // ---------------------------------------------------------------------------
 // One workgroup per (batch, chunk, run of hg heads of one group).  The heads
 // share C, so the C fragments are loaded once; everything a head needs
@@ -546,6 +581,27 @@ constexpr int kDt = 50176;     // dt: 256 floats
 constexpr int kSlot = 51200;
 constexpr int kCopies = 14;    // LDS-copy instructions per wave per head
 constexpr int kStores = 8;     // y stores per wave per head
+constexpr int kPartCopies[4] = {4, 4, 4, 2};   // x rows 0..127, x rows 128..255, Hin, cs + dt
+static_assert(kPartCopies[0] + kPartCopies[1] + kPartCopies[2] + kPartCopies[3] == kCopies, "copy count");
+
+// The resident kernel's issue order (labels: copies of head k, y stores of
+// head k) replayed against its waits at the top of each head: head k's
+// copies must have landed.  Its tile-(7 - w) stores follow slot 3 for every
+// wave, so both store groups come after the head's copies.
+constexpr bool waits_hold(int heads) {
+    VmemLog o;
+    o.push(100, kCopies);
+    o.push(101, kCopies);
+    for (int k = 0; k < heads; ++k) {
+        const int cnt = k == 0 ? 0 : (k == 1 ? kCopies + kStores : kCopies + 2 * kStores);
+        if (!o.wait(cnt) || !o.landed(100 + k)) return false;
+        for (int part = 0; part < 4; ++part) o.push(100 + k + 2, kPartCopies[part]);
+        o.push(200 + k, kStores);
+    }
+    return true;
+}
+static_assert(waits_hold(1) && waits_hold(2) && waits_hold(3) && waits_hold(12) && waits_hold(40),
+              "resident chunk_scan wait counts do not cover its copies");
 }  // namespace rsl
 
 // Carried-state term of both of the wave's tiles, acc[q][mt] = sstate_q *

@@ -220,4 +220,32 @@ __device__ __forceinline__ void issue_bx_stage(int wave, int lane, int tokbase, 
     }
 }
 
+// Compile-time replay of one wave's vector-memory issue order, used next to
+// each pipelined kernel to check its wait counts: s_waitcnt vmcnt(n) leaves
+// at most the n newest operations pending (they complete in issue order), so
+// a wait is sound when every operation it guards is older than those n.
+struct VmemLog {
+    int lab[1024] = {};
+    int n = 0;
+    int done = 0;   // operations [0, done) are known complete
+    constexpr void push(int label, int times) {
+        for (int i = 0; i < times; ++i) lab[n++] = label;   // past 1024: not a constant expression
+    }
+    constexpr bool wait(int count) {   // false if the count does not fit the counter
+        if (count < 0 || count > 63) return false;
+        if (n - count > done) done = n - count;
+        return true;
+    }
+    // at least one operation carries the label and all of them are complete
+    constexpr bool landed(int label) const {
+        bool any = false;
+        for (int i = 0; i < n; ++i)
+            if (lab[i] == label) {
+                if (i >= done) return false;
+                any = true;
+            }
+        return any;
+    }
+};
+
 }  // namespace ssd

@@ -54,6 +54,36 @@ __host__ __device__ constexpr int sscan_ops_after(int jt) {
          : jt == 2 ? 1 + kSsDc + kSsDps
                    : 1 + kSsDps;
 }
+// The issue order replayed against those counts over a few chunks (labels:
+// B block k, x block k, rows of chunk c, Hin stores of chunk c): at step k
+// the block scaled (x k + 1) and the block multiplied (B k) must have landed,
+// and at a chunk's last step the next chunk's rows.
+constexpr bool sscan_waits_hold(int nc) {
+    auto bl = [](int k) { return 1000 + k; };
+    auto xl = [](int k) { return 2000 + k; };
+    auto rl = [](int c) { return 3000 + c; };
+    VmemLog o;
+    o.push(rl(0), kSsDc);
+    for (int k = 0; k < 7; ++k) o.push(xl(k), 1);
+    for (int k = 0; k < 3; ++k) o.push(bl(k), 2);
+    if (!o.wait(0)) return false;
+    for (int c = 0; c < nc; ++c) {
+        o.push(4000 + c, kSsNh);
+        for (int jt = 0; jt < 8; ++jt) {
+            const int k = 8 * c + jt;
+            if (!o.wait(sscan_ops_after(jt < 3 ? jt : 3)) || !o.landed(xl(k + 1)) || !o.landed(bl(k)))
+                return false;
+            if (jt == 7 && !o.landed(rl(c + 1))) return false;
+            o.push(bl(k + 3), 2);
+            o.push(xl(k + 7), 1);
+            if (jt == 0) o.push(rl(c + 1), kSsDc);
+        }
+    }
+    return true;
+}
+static_assert(kSsDps == 2 + 1, "two B copies and one x copy per step");
+static_assert(sscan_waits_hold(1) && sscan_waits_hold(2) && sscan_waits_hold(4),
+              "state_scan wait counts do not cover its copies");
 
 }  // namespace
 
