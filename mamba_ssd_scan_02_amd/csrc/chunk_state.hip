@@ -39,6 +39,22 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, const float (&w)[8]) {
 }
 
 constexpr int kStateRing = 3;
+// Stages issued after stage jt when step jt waits for it (R - 1 are issued
+// ahead, none past the last of NT).
+__host__ __device__ constexpr int state_ring_ahead(int NT, int R, int jt) {
+    return (NT - 1 - jt) < (R - 2) ? (NT - 1 - jt) : (R - 2);
+}
+// The ring's issue order (stages of DPS copies) replayed against those
+// waits: stage jt must have landed at step jt.
+constexpr bool state_ring_waits_hold(int NT, int R, int DPS) {
+    VmemLog o;
+    for (int k = 0; k < R - 1 && k < NT; ++k) o.push(k, DPS);
+    for (int jt = 0; jt < NT; ++jt) {
+        if (!o.wait(DPS * state_ring_ahead(NT, R, jt)) || !o.landed(jt)) return false;
+        if (jt + R - 1 < NT) o.push(jt + R - 1, DPS);
+    }
+    return true;
+}
 // Heads per workgroup where a group's head count allows it, else one.  At the
 // 2.7B shape: 1 head 151 us, 2 heads 134-138 us, 4 heads 139-141 us.
 constexpr int kStateHeads = 2;
@@ -59,6 +75,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
     constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
     constexpr int DPS = 12 / W;          // copies per wave per 32-token stage
     constexpr int R = kStateRing;        // ring stages (R - 1 issued ahead)
+    static_assert(state_ring_waits_hold(NT, R, DPS), "chunk_state wait counts do not cover its copies");
     __shared__ uint4 bsr[R][512];
     __shared__ uint4 xsr[R][256];
     __shared__ float wv[Q];
@@ -98,9 +115,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
     for (int jt = 0; jt < NT; ++jt) {
         uint4* bst = bsr[jt % R];
         uint4* xst = xsr[jt % R];
-        // stages issued after jt: up to R - 2 of them
-        const int ahead = (NT - 1 - jt) < (R - 2) ? (NT - 1 - jt) : (R - 2);
-        wait_vmcnt_n(DPS * ahead);   // a constant once the loop is unrolled
+        wait_vmcnt_n(DPS * state_ring_ahead(NT, R, jt));   // a constant once the loop is unrolled
         barrier_lds();
         if (jt + R - 1 < NT)
             issue_bx_stage<W>(wave, lane, tok0 + 32 * (jt + R - 1), L, xbase, xstride, bbase, bstride, bxo,
@@ -237,6 +252,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     constexpr int XR = 128 * HG;                         // bytes of a token's x row
     constexpr int DPS = 8 / W + BxhOffsets<W, HG>::XC;   // copies per wave per stage
     constexpr int R = kStateRing;
+    static_assert(state_ring_waits_hold(NT, R, DPS), "chunk_state wait counts do not cover its copies");
     __shared__ uint4 bsr[R][512];
     __shared__ uint4 xsr[R][32 * XR / 16];
     __shared__ float wv[HG][Q];
@@ -330,8 +346,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     for (int jt = 0; jt < NT; ++jt) {
         uint4* bst = bsr[jt % R];
         uint4* xst = xsr[jt % R];
-        const int ahead = (NT - 1 - jt) < (R - 2) ? (NT - 1 - jt) : (R - 2);
-        wait_vmcnt_n(DPS * ahead);   // a constant once the loop is unrolled
+        wait_vmcnt_n(DPS * state_ring_ahead(NT, R, jt));   // a constant once the loop is unrolled
         barrier_lds();
         if (jt + R - 1 < NT)
             issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * (jt + R - 1), L, xbase, xstride, bbase, bstride,
