@@ -117,7 +117,8 @@ def compulsory_bytes(b, L, H, P, N, G):
 def source_hash(kernel: str) -> str:
     p = ROOT / "mamba_ssd_scan_02_amd" / "csrc" / KERNEL_SOURCES[kernel]
     h = hashlib.sha256(p.read_bytes())
-    h.update((ROOT / "mamba_ssd_scan_02_amd" / "csrc" / "device_common.h").read_bytes())
+    for inc in ("device_common.h", "lds_pipe.h"):   # device code every kernel includes
+        h.update((ROOT / "mamba_ssd_scan_02_amd" / "csrc" / inc).read_bytes())
     return h.hexdigest()[:16]
 
 
