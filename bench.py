@@ -444,12 +444,27 @@ def summarize_trace(d: str, out: str, cmd: str):
     if not f:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(f[0])))
+    # medians from the per-dispatch trace beside the stats, when present
+    med = {}
+    t = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if t:
+        durs = {}
+        for r in csv.DictReader(open(t[0])):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in durs.items():
+            v.sort()
+            n = len(v)
+            med[k] = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
     lines = ["# rocprofv3 kernel trace summary (per-kernel dispatch durations)",
              f"command: {cmd}", "",
-             f"{'kernel':24s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_%':>8s}"]
+             f"{'kernel':24s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} "
+             f"{'max_us':>10s} {'total_%':>8s}"]
     for r in rows:
         avg = float(r["AverageNs"]) / 1e3
-        lines.append(f"{_short_kernel(r['Name']):24s} {int(r['Calls']):6d} {avg:10.2f} "
+        m = med.get(r["Name"])
+        mtxt = f"{m:10.2f}" if m is not None else f"{'-':>10s}"
+        lines.append(f"{_short_kernel(r['Name']):24s} {int(r['Calls']):6d} {avg:10.2f} {mtxt} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                      f"{float(r['Percentage']):8.2f}")
     lines.append("")
