@@ -1,19 +1,25 @@
 """End-to-end parity of ssd_forward (GPU, through the C ABI) with the fp64
 oracle, on the five workloads and on the edge cases the method has.
 
-Gate: max |gpu - oracle| / max |oracle| per output tensor, <= 1e-4 for fp32
-storage and <= 2e-2 for bf16 storage (fp32 accumulation and state).
+Gates (tests/metrics.py), per output tensor, at 1e-4 for fp32 storage and
+2e-2 for bf16 storage (fp32 accumulation and state): max |gpu - oracle| /
+max |oracle|, and max |gpu - oracle| / (|oracle| + rms(oracle)) per element.
 At full size the oracle runs on a sample of (batch, head) pairs over the
-whole sequence (first and last pair always included)."""
+whole sequence (first and last pair always included).  Every full-size
+workload is also run without the skip term (D = None): with D ~ N(0, 1) the
+D x term sets the output's peak, so only a D-free run gates the scan terms
+(the masked in-chunk product and the carried state) at their own scale.
+Outputs and the workspace are guarded and NaN-poisoned (tests/helpers.py)."""
 import math
 
 import numpy as np
 import pytest
 import torch
 
-from tests.helpers import (TOL, all_pairs, gpu_forward, oracle_forward, sample_pairs, say,
-                           select_state, select_y, to_gpu)
-from tests.metrics import max_rel_err
+from tests.helpers import (TOL, abs_inputs, all_pairs, gpu_forward, oracle_forward,
+                           oracle_forward_scaled, sample_pairs, say, select_state, select_y,
+                           to_gpu)
+from tests.metrics import gate, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -23,13 +29,17 @@ def _check(inp, chunk, dtype, bh=None, t_range=None, label=""):
     batch, L, H, P = inp["x"].shape
     if bh is None:
         bh = all_pairs(batch, H)
-    y_ref, f_ref = oracle_forward(inp, bh=bh, t_range=t_range)
-    e_y = max_rel_err(select_y(y, bh, t_range), y_ref)
-    e_f = max_rel_err(select_state(fin, bh), f_ref)
-    say(f"[forward] {label} chunk={chunk}: y {e_y:.3e} final {e_f:.3e}")
-    assert e_y <= TOL[dtype], e_y
-    assert e_f <= TOL[dtype], e_f
+    y_ref, f_ref, y_mag, f_mag = oracle_forward_scaled(inp, bh=bh, t_range=t_range)
+    say(f"[forward] {label} chunk={chunk}")
+    gate(select_y(y, bh, t_range), y_ref, TOL[dtype], "y", y_mag)
+    gate(select_state(fin, bh), f_ref, TOL[dtype], "final_state", f_mag)
     return y, fin
+
+
+def _check_with_and_without_skip(inp, chunk, dtype, bh=None, label=""):
+    """The workload as drawn, then the same inputs with D = None."""
+    _check(inp, chunk, dtype, bh=bh, label=label)
+    _check(dict(inp, D=None), chunk, dtype, bh=bh, label=label + " D=None")
 
 
 def _spec_inputs(spec):
@@ -40,27 +50,36 @@ def _spec_inputs(spec):
 # ----------------------------------------------------------------- workloads
 def test_tiny_f32():
     from mamba_ssd_scan_02_amd.workloads import TINY_F32
-    _check(_spec_inputs(TINY_F32), TINY_F32.chunk, "f32", label=TINY_F32.name)
+    _check_with_and_without_skip(_spec_inputs(TINY_F32), TINY_F32.chunk, "f32",
+                                 label=TINY_F32.name)
 
 
 def test_mamba2_130m_shape():
+    """130M-shaped layer: 24 heads per group, so chunk_scan runs the
+    streaming kernel."""
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M as s
     inp = _spec_inputs(s)
-    _check(inp, s.chunk, s.dtype, bh=sample_pairs(s.batch, s.nheads, 24, seed=2), label=s.name)
+    _check_with_and_without_skip(inp, s.chunk, s.dtype,
+                                 bh=sample_pairs(s.batch, s.nheads, 24, seed=2), label=s.name)
 
 
 def test_mamba2_2p7b_shape():
+    """2.7B-shaped layer (the bench workload): 80 heads per group, so
+    chunk_scan runs the resident kernel (runs of 40 heads)."""
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as s
     inp = _spec_inputs(s)
-    _check(inp, s.chunk, s.dtype, bh=sample_pairs(s.batch, s.nheads, 12, seed=3), label=s.name)
+    _check_with_and_without_skip(inp, s.chunk, s.dtype,
+                                 bh=sample_pairs(s.batch, s.nheads, 12, seed=3), label=s.name)
 
 
 def test_long_context_1m():
+    """One 1M-token sequence, 8 groups of 4 heads (streaming chunk_scan, 4,096
+    chained chunks).  Heads 0 and 31 (groups 0 and 7) plus two in between."""
     from mamba_ssd_scan_02_amd.workloads import LONG_1M as s
     inp = _spec_inputs(s)
     say(f"[forward] {s.name}: inputs ready")
-    # heads 0 and 31 (groups 0 and 7) plus two in between, over all 1M tokens
-    _check(inp, s.chunk, s.dtype, bh=[(0, 0), (0, 5), (0, 18), (0, 31)], label=s.name)
+    _check_with_and_without_skip(inp, s.chunk, s.dtype, bh=[(0, 0), (0, 5), (0, 18), (0, 31)],
+                                 label=s.name)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -108,7 +127,7 @@ def test_long_memory_f32():
 def test_ragged_lengths_bf16(L):
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
     inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=L, nheads=4, init_var=0.1, seed=77))
-    _check(inp, 256, "bf16", label=f"ragged L={L}")
+    _check_with_and_without_skip(inp, 256, "bf16", label=f"ragged L={L}")
 
 
 @pytest.mark.parametrize("chunk", [64, 128, 256])
@@ -116,7 +135,7 @@ def test_chunk_sweep_bf16(chunk):
     """Same inputs, three chunk sizes: all match the oracle."""
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
     inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=1024, nheads=4, init_var=0.1, seed=78))
-    _check(inp, chunk, "bf16", label="chunk sweep")
+    _check_with_and_without_skip(inp, chunk, "bf16", label="chunk sweep")
 
 
 @pytest.mark.parametrize("chunk", [1, 7, 64, 200, 256])
@@ -155,13 +174,12 @@ def test_split_sequence_handoff():
     y1, f1 = gpu_forward(first, 256)
     second["init"] = f1.cpu()
     y2, f2 = gpu_forward(second, 256)
-    y_ref, f_ref = oracle_forward(inp)
+    y_ref, f_ref, y_mag, f_mag = oracle_forward_scaled(inp)
     bh = all_pairs(2, 4)
     y_cat = torch.cat([y1.cpu(), y2.cpu()], dim=1)
-    e_y = max_rel_err(select_y(y_cat, bh), y_ref)
-    e_f = max_rel_err(select_state(f2, bh), f_ref)
-    say(f"[forward] handoff y {e_y:.3e} final {e_f:.3e}")
-    assert e_y <= TOL["bf16"] and e_f <= TOL["bf16"]
+    say("[forward] handoff")
+    gate(select_y(y_cat, bh), y_ref, TOL["bf16"], "y", y_mag)
+    gate(select_state(f2, bh), f_ref, TOL["bf16"], "final_state", f_mag)
 
 
 def test_zero_step_keeps_state():
@@ -189,8 +207,8 @@ def test_no_skip_no_init_no_final():
                              return_final_state=False)
     assert fin is None
     ref = dict(inp, D=None, init=None)
-    y_ref, _ = oracle_forward(ref)
-    assert max_rel_err(select_y(y, all_pairs(1, 2)), y_ref) <= TOL["bf16"]
+    y_ref, _, y_mag, _ = oracle_forward_scaled(ref)
+    gate(select_y(y, all_pairs(1, 2)), y_ref, TOL["bf16"], "y (no D, no init)", y_mag)
 
 
 def test_final_state_may_alias_init():
@@ -232,11 +250,10 @@ def test_zero_order_hold_forward(case):
     batch, L, H, P = inp["x"].shape
     bh = all_pairs(batch, H) if nsample is None else sample_pairs(batch, H, nsample, seed=9)
     y, fin = gpu_forward(inp, chunk, zoh=True)
-    y_ref, f_ref = oracle_forward(inp, bh=bh, zoh=True)
-    e_y = max_rel_err(select_y(y, bh), y_ref)
-    e_f = max_rel_err(select_state(fin, bh), f_ref)
-    say(f"[forward zoh] {label}: y {e_y:.3e} final {e_f:.3e}")
-    assert e_y <= TOL[spec.dtype] and e_f <= TOL[spec.dtype], (e_y, e_f)
+    y_ref, f_ref, y_mag, f_mag = oracle_forward_scaled(inp, bh=bh, zoh=True)
+    say(f"[forward zoh] {label}")
+    gate(select_y(y, bh), y_ref, TOL[spec.dtype], "y", y_mag)
+    gate(select_state(fin, bh), f_ref, TOL[spec.dtype], "final_state", f_mag)
     y_plain, _ = gpu_forward(inp, chunk)
     d = max_rel_err(select_y(y_plain, bh), y_ref)
     assert d > 10 * TOL[spec.dtype], d
@@ -278,6 +295,7 @@ def test_time_invariant_is_a_convolution(case):
     x64 = x.double().numpy()
     B64, C64 = Bv.double().numpy(), Cv.double().numpy()
     ref = np.empty_like(x64)
+    mag = np.empty_like(x64)      # the same convolution over absolute values
     k = np.arange(L, dtype=np.float64)
     for b in range(batch):
         for h in range(H):
@@ -285,7 +303,8 @@ def test_time_invariant_is_a_convolution(case):
             d, a_h = float(dt_h[b, h]), float(A[h])
             w = math.expm1(d * a_h) / a_h if zoh else d
             K = float(C64[b, g] @ B64[b, g]) * w * np.exp(d * a_h * k)
+            Km = float(np.abs(C64[b, g]) @ np.abs(B64[b, g])) * abs(w) * np.exp(d * a_h * k)
             ref[b, :, h] = fftconvolve(x64[b, :, h], K[:, None], axes=0)[:L] + float(D[h]) * x64[b, :, h]
-    e = max_rel_err(y, ref)
-    say(f"  y {e:.3e}")
-    assert e <= TOL[dtype], e
+            mag[b, :, h] = (np.abs(fftconvolve(np.abs(x64[b, :, h]), Km[:, None], axes=0)[:L]) +
+                            abs(float(D[h])) * np.abs(x64[b, :, h]))
+    gate(y, ref, TOL[dtype], "y", mag)

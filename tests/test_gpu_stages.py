@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from tests.helpers import TOL, say, to_gpu
-from tests.metrics import max_rel_err
+from tests.metrics import gate, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -57,59 +57,62 @@ def test_stages(case):
     # chunk state, from the GPU's cs/dtc
     S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
     S_ref = stages.chunk_state(inp["x"], inp["dt"], inp["B"], Acs, Q)
-    e = max_rel_err(S, S_ref)
-    say(f"  chunk_state max rel err {e:.3e}")
-    assert e < (tol if dtype == "bf16" else 1e-5)
+    S_mag = stages.chunk_state(inp["x"].abs(), inp["dt"], inp["B"].abs(), Acs, Q)
+    gate(S, S_ref, tol if dtype == "bf16" else 1e-5, "chunk_state S", S_mag)
 
     # state passing, from the GPU's S
     sd = torch.bfloat16 if dtype == "bf16" else torch.float32
     Hin, fin = ssd.state_passing(S, cs, L, Q, sd, g["init"])
     S_gpu = S.cpu().double().numpy()
     Hin_ref, fin_ref = stages.state_passing(S_gpu, Acs, inp["init"])
-    e_h = max_rel_err(Hin, Hin_ref)
-    e_f = max_rel_err(fin, fin_ref)
-    say(f"  state_passing Hin {e_h:.3e} final {e_f:.3e}")
-    assert e_h < (8e-3 if dtype == "bf16" else 1e-6)
-    assert e_f < 1e-5
+    Hin_mag, fin_mag = stages.state_passing(np.abs(S_gpu), Acs, inp["init"].abs())
+    gate(Hin, Hin_ref, 8e-3 if dtype == "bf16" else 1e-6, "state_passing Hin", Hin_mag)
+    gate(fin, fin_ref, 1e-5, "state_passing final", fin_mag)
 
-    # chunk scan, from the GPU's cs/dtc/Hin
-    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], Q)
-    y_ref = stages.chunk_scan(inp["x"], inp["dt"], inp["B"], inp["C"], Acs,
-                              Hin.cpu().double().numpy(), inp["D"], Q)
-    e_y = max_rel_err(y, y_ref)
-    say(f"  chunk_scan max rel err {e_y:.3e}")
-    assert e_y < tol
+    # chunk scan, from the GPU's cs/dtc/Hin, with and without the skip term
+    Hn = Hin.cpu().double().numpy()
+    for D_gpu, D_ref, what in ((g["D"], inp["D"], "chunk_scan y"),
+                               (None, None, "chunk_scan y (D=None)")):
+        y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, D_gpu, Q)
+        y_ref = stages.chunk_scan(inp["x"], inp["dt"], inp["B"], inp["C"], Acs, Hn, D_ref, Q)
+        y_mag = stages.chunk_scan(inp["x"].abs(), inp["dt"], inp["B"].abs(), inp["C"].abs(), Acs,
+                                  np.abs(Hn), None if D_ref is None else D_ref.abs(), Q)
+        gate(y, y_ref, tol, what, y_mag)
 
 
-def test_chunk_scan_head_runs():
+@pytest.mark.parametrize("skip", [True, False], ids=["with_D", "D_none"])
+def test_chunk_scan_head_runs(skip):
     """128 (batch, chunk, group) units of 25 heads: the launcher gives each
     workgroup a run of 13 or 12 heads of one chunk (on a 256-CU part), the
     path that keeps the C.B^T tiles in registers across a run.  The first and
     last head of both runs are checked against the oracle over every chunk,
-    including the ragged last one."""
+    including the ragged last one; with D = None the masked in-chunk product
+    and the carried state are gated at their own scale."""
     import mamba_ssd_scan_02_amd as ssd
     from oracle import stages
 
     batch, L, H, P, N, G, Q = 1, 128 * 256 - 37, 25, 64, 128, 1, 256
-    say("[stages] chunk_scan head runs")
+    say(f"[stages] chunk_scan head runs ({'with D' if skip else 'D=None'})")
     inp = _inputs(13, batch, L, H, P, N, G, "bf16")
     g = to_gpu(inp)
     cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
     S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
     Hin, _ = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"])
-    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], Q).cpu()
+    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"] if skip else None, Q).cpu()
     Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
     Hn = Hin.cpu().double().numpy()
     for h in (0, 12, 13, 24):
         sl = slice(h, h + 1)
         y_ref = stages.chunk_scan(inp["x"][:, :, sl], inp["dt"][:, :, sl], inp["B"], inp["C"],
-                                  Acs[:, sl], Hn[:, sl], inp["D"][sl], Q)
-        e = max_rel_err(y[:, :, sl], y_ref)
-        say(f"  head {h}: max rel err {e:.3e}")
-        assert e < TOL["bf16"], (h, e)
+                                  Acs[:, sl], Hn[:, sl], inp["D"][sl] if skip else None, Q)
+        y_mag = stages.chunk_scan(inp["x"][:, :, sl].abs(), inp["dt"][:, :, sl], inp["B"].abs(),
+                                  inp["C"].abs(), Acs[:, sl], np.abs(Hn[:, sl]),
+                                  inp["D"][sl].abs() if skip else None, Q)
+        gate(y[:, :, sl], y_ref, TOL["bf16"], f"head {h}", y_mag)
 
 
-def test_chunk_scan_head_runs_strong_decay():
+@pytest.mark.parametrize("skip", [True, False], ids=["with_D", "D_none"])
+def test_chunk_scan_head_runs_strong_decay(skip):
     """The head-run path with step sizes that make some 32-token tiles decay
     by far more than 2^64 (45-token windows at dt = 2.5 with A = -1, i.e.
     3.6 log2 units per token, between windows at dt = 0.05): those tiles,
@@ -120,7 +123,7 @@ def test_chunk_scan_head_runs_strong_decay():
     from oracle import stages
 
     batch, L, H, P, N, G, Q = 1, 128 * 256 - 37, 25, 64, 128, 1, 256
-    say("[stages] chunk_scan head runs, strong decay")
+    say(f"[stages] chunk_scan head runs, strong decay ({'with D' if skip else 'D=None'})")
     inp = _inputs(14, batch, L, H, P, N, G, "bf16")
     t = np.arange(L)
     win = np.where((t // 45) % 3 == 0, 2.5, 0.05).astype(np.float32)
@@ -132,7 +135,7 @@ def test_chunk_scan_head_runs_strong_decay():
     cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
     S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
     Hin, _ = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"])
-    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"], Q).cpu()
+    y = ssd.chunk_scan(g["x"], g["B"], g["C"], cs, dtc, Hin, g["D"] if skip else None, Q).cpu()
     Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
     # both kinds of tile occur: some decay by more than 2^64, most by less
     tile_decay = (Acs[..., ::32] - Acs[..., 31::32]) * LOG2E
@@ -141,10 +144,11 @@ def test_chunk_scan_head_runs_strong_decay():
     for h in (0, 12, 13, 24):
         sl = slice(h, h + 1)
         y_ref = stages.chunk_scan(inp["x"][:, :, sl], inp["dt"][:, :, sl], inp["B"], inp["C"],
-                                  Acs[:, sl], Hn[:, sl], inp["D"][sl], Q)
-        e = max_rel_err(y[:, :, sl], y_ref)
-        say(f"  head {h}: max rel err {e:.3e}")
-        assert e < TOL["bf16"], (h, e)
+                                  Acs[:, sl], Hn[:, sl], inp["D"][sl] if skip else None, Q)
+        y_mag = stages.chunk_scan(inp["x"][:, :, sl].abs(), inp["dt"][:, :, sl], inp["B"].abs(),
+                                  inp["C"].abs(), Acs[:, sl], np.abs(Hn[:, sl]),
+                                  inp["D"][sl].abs() if skip else None, Q)
+        gate(y[:, :, sl], y_ref, TOL["bf16"], f"head {h}", y_mag)
 
 
 def test_stage_intermediates_deterministic():
@@ -193,10 +197,10 @@ def test_state_scan(case):
     Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
     S_ref = stages.chunk_state(inp["x"], inp["dt"], inp["B"], Acs, Q)
     Hin_ref, fin_ref = stages.state_passing(S_ref, Acs, inp["init"] if init else None)
-    e_h = max_rel_err(Hin, Hin_ref)
-    e_f = max_rel_err(fin, fin_ref)
-    say(f"  Hin {e_h:.3e} final {e_f:.3e}")
-    assert e_h < TOL["bf16"] and e_f < TOL["bf16"]
+    S_mag = stages.chunk_state(inp["x"].abs(), inp["dt"], inp["B"].abs(), Acs, Q)
+    Hin_mag, fin_mag = stages.state_passing(S_mag, Acs, inp["init"].abs() if init else None)
+    gate(Hin, Hin_ref, TOL["bf16"], "Hin", Hin_mag)
+    gate(fin, fin_ref, TOL["bf16"], "final", fin_mag)
     # the two-kernel path on the same device intermediates
     S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
     Hin2, fin2 = ssd.state_passing(S, cs, L, Q, torch.bfloat16, g["init"] if init else None)
@@ -256,12 +260,12 @@ def test_state_passing_segmented(case):
     Hin, fin = ssd.state_passing_seg(S, cs, L, Q, sd, nseg, init_state=st,
                                      final_state=st if alias else None)
     Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
-    Hin_ref, fin_ref = stages.state_passing(S.cpu().double().numpy(), Acs,
-                                            inp["init"] if init else None)
-    e_h, e_f = max_rel_err(Hin, Hin_ref), max_rel_err(fin, fin_ref)
-    say(f"  Hin {e_h:.3e} final {e_f:.3e}")
-    assert e_h < (8e-3 if dtype == "bf16" else 1e-6)
-    assert e_f < 1e-5
+    S_gpu = S.cpu().double().numpy()
+    Hin_ref, fin_ref = stages.state_passing(S_gpu, Acs, inp["init"] if init else None)
+    Hin_mag, fin_mag = stages.state_passing(np.abs(S_gpu), Acs,
+                                            inp["init"].abs() if init else None)
+    gate(Hin, Hin_ref, 8e-3 if dtype == "bf16" else 1e-6, "Hin", Hin_mag)
+    gate(fin, fin_ref, 1e-5, "final", fin_mag)
     Hin2, fin2 = ssd.state_passing(S, cs, L, Q, sd, g["init"] if init else None)
     assert max_rel_err(fin, fin2.cpu().double().numpy()) < 1e-5
     assert max_rel_err(Hin, Hin2.cpu().double().numpy()) < (8e-3 if dtype == "bf16" else 1e-6)
