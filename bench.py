@@ -182,7 +182,7 @@ def forward_kernels(dims):
     separate cumsum launch runs; the stage timings below time the stage calls
     themselves."""
     b, L, H, P, N, G, Q = dims
-    fused = P == 64 and N == 128 and Q in (64, 128, 256) and (H // G) % 2 == 0
+    fused = P == 64 and N == 128 and Q in (128, 256) and (H // G) % 2 == 0
     return (["chunk_state"] if fused else ["chunk_cumsum", "chunk_state"]) + \
         ["state_passing", "chunk_scan"]
 

@@ -60,8 +60,9 @@
  *    be partial.
  *  - Supported shapes (ssd_forward and the stage calls): either dtype with
  *    1 <= P <= 128, 1 <= N <= 128, 1 <= Q <= 256; bf16 with P = 64, N = 128
- *    and Q in {64, 128, 256} runs on the matrix cores, everything else on the
- *    vector units.  Anything else returns SSD_ERR_UNSUPPORTED.
+ *    and Q in {128, 256} runs on the matrix cores, everything else
+ *    (chunk 64 included) on the vector units.  Anything else returns
+ *    SSD_ERR_UNSUPPORTED.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -120,9 +121,12 @@ size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
  *   init_state  may be NULL: zero initial state.  When given it is decayed by
  *               exp(dt_0 A) at the first token, like any carried state.
  *   final_state may be NULL: not written.  It may alias init_state (the
- *               state is read before it is overwritten).
- *   y           must not overlap any input or the workspace (SSD_ERR_ALIAS).
- *   workspace   at least ssd_forward_workspace_bytes(...) bytes.
+ *               state is read before it is overwritten); it must not overlap
+ *               any other input, y or the workspace (SSD_ERR_ALIAS).
+ *   y           must not overlap any input (x, dt, A, B, C, D, init_state),
+ *               final_state or the workspace (SSD_ERR_ALIAS).
+ *   workspace   at least ssd_forward_workspace_bytes(...) bytes; it must not
+ *               overlap any input or output (SSD_ERR_ALIAS).
  */
 int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                     int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,

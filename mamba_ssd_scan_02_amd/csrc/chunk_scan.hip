@@ -13,7 +13,7 @@
 // through the chunk; (iii) is the D x term of y = C h + D x (page "Puntata 205",
 // section "Cos'e' un SSM, in 30 secondi").
 //
-// Matrix-core kernel (bf16, P = 64, N = 128, Q in {64, 128, 256}); one
+// Matrix-core kernel (bf16, P = 64, N = 128, Q in {128, 256}); one
 // workgroup of Q/64 waves per (batch, chunk, head); v_mfma_f32_32x32x16_bf16.
 // Everything is computed transposed, Y^T[p][i], so that each lane owns one
 // output token i (the MFMA result column) -- that makes the masked weights

@@ -518,7 +518,6 @@ hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B,
     const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
     const int z = zoh ? 1 : 0;
     switch (d.chunk) {
-        case 64: chunk_state_mfmah_kernel<64, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
         case 128: chunk_state_mfmah_kernel<128, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
         default: chunk_state_mfmah_kernel<256, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
     }
@@ -535,14 +534,12 @@ hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const
         if ((d.nheads / d.ngroups) % kStateHeads == 0) {
             const unsigned hblocks = blocks / (unsigned)kStateHeads;
             switch (d.chunk) {
-                case 64: chunk_state_mfmah_kernel<64, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
                 case 128: chunk_state_mfmah_kernel<128, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
                 default: chunk_state_mfmah_kernel<256, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
             }
             return hipGetLastError();
         }
         switch (d.chunk) {
-            case 64: chunk_state_mfma_kernel<64><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
             case 128: chunk_state_mfma_kernel<128><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
             default: chunk_state_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
         }

@@ -279,16 +279,23 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     const size_t ybytes = tok * d.nheads * d.headdim * es;
     const size_t bcbytes = tok * d.ngroups * d.dstate * es;
     const size_t dtbytes = tok * d.nheads * 4;
+    const size_t hbytes = (size_t)d.nheads * 4;
     const size_t stbytes = (size_t)d.batch * d.nheads * d.headdim * d.dstate * 4;
-    if (overlaps(y, ybytes, x, ybytes) || overlaps(y, ybytes, B, bcbytes) ||
-        overlaps(y, ybytes, C, bcbytes) || overlaps(y, ybytes, dt, dtbytes) ||
-        overlaps(y, ybytes, workspace, lo.total) || overlaps(y, ybytes, init_state, stbytes) ||
-        overlaps(y, ybytes, final_state, stbytes) ||
-        overlaps(workspace, lo.total, x, ybytes) || overlaps(workspace, lo.total, B, bcbytes) ||
-        overlaps(workspace, lo.total, C, bcbytes) || overlaps(workspace, lo.total, dt, dtbytes) ||
-        overlaps(workspace, lo.total, init_state, stbytes) ||
-        overlaps(workspace, lo.total, final_state, stbytes))
-        return SSD_ERR_ALIAS;
+    // Every output (y, final_state, the workspace) must stay clear of every
+    // input and of the other outputs; the one permitted overlap is
+    // final_state on init_state (the state is read before it is written).
+    struct Span { const void* p; size_t n; };
+    const Span inputs[] = {{x, ybytes}, {B, bcbytes}, {C, bcbytes}, {dt, dtbytes},
+                           {A, hbytes}, {D, hbytes}, {init_state, stbytes}};
+    const Span outs[] = {{y, ybytes}, {workspace, lo.total}, {final_state, stbytes}};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 7; ++i) {
+            if (o == 2 && i == 6) continue;   // final_state may alias init_state
+            if (overlaps(outs[o].p, outs[o].n, inputs[i].p, inputs[i].n)) return SSD_ERR_ALIAS;
+        }
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlaps(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n)) return SSD_ERR_ALIAS;
+    }
 
     char* ws = static_cast<char*>(workspace);
     float* cs = reinterpret_cast<float*>(ws + lo.cs);

@@ -95,6 +95,19 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, dt=0x2002) == ALIGN
     assert _fwd(lib, y=0x1000) == ALIAS            # y on top of x
     assert _fwd(lib, ws=0x1000) == ALIAS           # workspace on top of x
+    # y or the workspace on top of A or D
+    assert _fwd(lib, y=0x3000) == ALIAS
+    assert _fwd(lib, D=0x6000, y=0x6000) == ALIAS
+    assert _fwd(lib, ws=0x3000) == ALIAS
+    assert _fwd(lib, D=0x6000, ws=0x6000) == ALIAS
+    # final_state on any input but init_state, on y or on the workspace
+    for name, addr in (("x", 0x1000), ("dt", 0x2000), ("A", 0x3000), ("B", 0x4000),
+                       ("C", 0x5000)):
+        assert _fwd(lib, final=addr) == ALIAS, name
+    assert _fwd(lib, D=0x6000, final=0x6000) == ALIAS
+    assert _fwd(lib, final=0x100000) == ALIAS      # on y
+    assert _fwd(lib, final=0x200000) == ALIAS      # on the workspace
+    # (final_state on init_state is allowed: tests/test_gpu_forward.py runs it)
 
 
 def test_step_argument_errors(lib):

@@ -26,7 +26,7 @@ CASES = [
     # (name, batch, L, H, P, N, G, chunk, dtype)
     ("mfma_q256_ragged", 2, 700, 4, 64, 128, 2, 256, "bf16"),
     ("mfma_q128", 1, 512, 2, 64, 128, 1, 128, "bf16"),
-    ("mfma_q64_ragged", 1, 333, 2, 64, 128, 2, 64, "bf16"),
+    ("bf16_q64_vector_units_ragged", 1, 333, 2, 64, 128, 2, 64, "bf16"),
     ("generic_f32", 2, 300, 3, 16, 16, 1, 64, "f32"),
     ("generic_f32_odd", 1, 77, 2, 3, 5, 1, 16, "f32"),
     ("generic_bf16", 1, 260, 2, 32, 64, 2, 128, "bf16"),

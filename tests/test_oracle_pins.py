@@ -137,35 +137,57 @@ def test_water_tank_inside_a_wide_head(oracle_mod):
 
 # --------------------------------------------------------------------------
 # Page "State Space Models (SSM)", section "Come funzionano gli SSM": for
-# time-invariant parameters the recurrence equals a convolution with kernel
-# (C Bbar, C Abar Bbar, C Abar^2 Bbar, ...), from a zero initial state.
+# time-invariant parameters the recurrence equals a causal convolution of the
+# input with the system's impulse response, from a zero initial state.  The
+# page checks this on a 64-step, 16-state diagonal system with step 0.1 and
+# the exact zero-order hold; only those sizes and its tolerance are taken
+# from it (tests/golden/conv_demo.json).  The draws are this file's own.
 # --------------------------------------------------------------------------
+def _diag_system(seed, n):
+    """Decay rates in [0.3, 2.0) (log-uniform), input and output gains
+    N(0, 1): a stable diagonal system of n states."""
+    r = _rng(seed)
+    rate = np.exp(r.uniform(math.log(0.3), math.log(2.0), n))
+    return (-rate).astype(np.float32), r.standard_normal(n), r.standard_normal(n), r
+
+
+def _impulse_response(A, gain_in, gain_out, step, L):
+    """h[k] = sum_n gain_out_n exp(k step A_n) gain_in_n, k = 0 .. L-1: the
+    output k steps after a unit input, by the closed form of each state's
+    geometric decay (no recurrence)."""
+    k = np.arange(L, dtype=np.float64)[:, None]
+    return (gain_out[None, :] * np.exp(k * step * A[None, :].astype(np.float64)) *
+            gain_in[None, :]).sum(axis=1)
+
+
+def _causal_convolution(h, x):
+    """y = T x with T the lower-triangular Toeplitz matrix of h."""
+    from scipy.linalg import toeplitz
+    T = toeplitz(h, np.zeros_like(h))
+    return T @ x
+
+
 def test_recurrence_equals_convolution_diagonal(oracle_mod):
+    """Each diagonal state becomes one head (P = N = 1, its own B/C group);
+    the scan multiplies B by dt, so the exact zero-order-hold input gain
+    (exp(step A) - 1) / A B is handed in divided by the step."""
     g = json.loads((GOLDEN / "conv_demo.json").read_text())
-    L, Ns, delta = g["seqlen"], g["state_size"], g["delta"]
-    r = _rng(7)
-    xs = r.standard_normal(L)
-    Acont = -(r.uniform(0, 1, Ns) + 0.5)
-    Bc, Cc = r.standard_normal(Ns), r.standard_normal(Ns)
-    # Each diagonal state entry becomes one head (P = N = 1, own B/C group);
-    # the scan multiplies B by dt, so B is handed in as Bbar / delta.
-    A32 = Acont.astype(np.float32)
-    d32 = np.float32(delta)
-    Abar = np.exp(np.float64(d32) * A32.astype(np.float64))
-    Bbar = (Abar - 1.0) / A32.astype(np.float64) * Bc
-    Bin = (Bbar / np.float64(d32)).astype(np.float32)
-    x = np.repeat(xs.astype(np.float32)[None, :, None, None], Ns, axis=2)        # 1 L H 1
-    dt = np.full((1, L, Ns), d32, np.float32)
+    L, Ns, step = g["seqlen"], g["state_size"], np.float32(g["delta"])
+    A32, Bc, Cc, r = _diag_system(7, Ns)
+    xs = r.standard_normal(L).astype(np.float32)
+    s64, A64 = np.float64(step), A32.astype(np.float64)
+    gain_in = np.expm1(s64 * A64) / A64 * Bc
+    Bin = (gain_in / s64).astype(np.float32)
+    x = np.repeat(xs[None, :, None, None], Ns, axis=2)                       # 1 L H 1
+    dt = np.full((1, L, Ns), step, np.float32)
     Bm = np.broadcast_to(Bin[None, None, :, None], (1, L, Ns, 1)).copy()
     Cm = np.broadcast_to(Cc.astype(np.float32)[None, None, :, None], (1, L, Ns, 1)).copy()
     y_sel, _ = oracle_mod.forward(x, dt, A32, Bm, Cm)
     y_rec = y_sel[:, :, 0].sum(axis=0)
-    # the convolution, from the values the oracle actually consumed
-    Bbar_eff = np.float64(d32) * Bin.astype(np.float64)
-    C64 = Cc.astype(np.float32).astype(np.float64)
-    K = np.array([np.sum(C64 * Abar ** k * Bbar_eff) for k in range(L)])
-    x64 = xs.astype(np.float32).astype(np.float64)
-    y_conv = np.array([np.dot(K[: t + 1][::-1], x64[: t + 1]) for t in range(L)])
+    # the convolution, from the gains the oracle actually consumed
+    h = _impulse_response(A32, s64 * Bin.astype(np.float64),
+                          Cc.astype(np.float32).astype(np.float64), s64, L)
+    y_conv = _causal_convolution(h, xs.astype(np.float64))
     assert np.allclose(y_rec, y_conv, atol=g["compared_with_atol"])          # the page's check
     np.testing.assert_allclose(y_rec, y_conv, rtol=0, atol=1e-12 * np.abs(y_conv).max())
 
@@ -429,28 +451,24 @@ def test_chunk_cumsum_definition():
 # by its recurrent-versus-convolutional demonstration.
 # --------------------------------------------------------------------------
 def test_zoh_convolution_demo(oracle_mod):
-    """The demo again, now with the oracle's own zero-order hold: B is handed
-    in as B, and the recurrence must equal the convolution with kernel
-    K_k = C . (Abar^k Bbar), Bbar = (Abar - 1) / A B, built here in fp64."""
+    """The same check with the oracle's own zero-order hold: B is handed in
+    as drawn, and the recurrence must equal the causal convolution with the
+    impulse response built from the exact hold's input gain (fp64)."""
     g = json.loads((GOLDEN / "conv_demo.json").read_text())
-    L, Ns, delta = g["seqlen"], g["state_size"], g["delta"]
-    r = _rng(17)
+    L, Ns, step = g["seqlen"], g["state_size"], np.float32(g["delta"])
+    A32, B64, C64, r = _diag_system(17, Ns)
+    B32, C32 = B64.astype(np.float32), C64.astype(np.float32)
     xs = r.standard_normal(L).astype(np.float32)
-    A32 = (-(r.uniform(0, 1, Ns) + 0.5)).astype(np.float32)
-    B32 = r.standard_normal(Ns).astype(np.float32)
-    C32 = r.standard_normal(Ns).astype(np.float32)
-    d32 = np.float32(delta)
     x = np.repeat(xs[None, :, None, None], Ns, axis=2)
-    dt = np.full((1, L, Ns), d32, np.float32)
+    dt = np.full((1, L, Ns), step, np.float32)
     Bm = np.broadcast_to(B32[None, None, :, None], (1, L, Ns, 1)).copy()
     Cm = np.broadcast_to(C32[None, None, :, None], (1, L, Ns, 1)).copy()
     y_sel, _ = oracle_mod.forward(x, dt, A32, Bm, Cm, zoh=True)
     y_rec = y_sel[:, :, 0].sum(axis=0)
-    A64, d64 = A32.astype(np.float64), np.float64(d32)
-    Abar = np.exp(d64 * A64)
-    Bbar = (Abar - 1.0) / A64 * B32.astype(np.float64)
-    K = np.array([np.sum(C32.astype(np.float64) * Abar ** k * Bbar) for k in range(L)])
-    y_conv = np.array([np.dot(K[: t + 1][::-1], xs[: t + 1].astype(np.float64)) for t in range(L)])
+    A64, s64 = A32.astype(np.float64), np.float64(step)
+    gain_in = np.expm1(s64 * A64) / A64 * B32.astype(np.float64)
+    h = _impulse_response(A32, gain_in, C32.astype(np.float64), s64, L)
+    y_conv = _causal_convolution(h, xs.astype(np.float64))
     assert np.allclose(y_rec, y_conv, atol=g["compared_with_atol"])          # the page's check
     np.testing.assert_allclose(y_rec, y_conv, rtol=0, atol=1e-12 * np.abs(y_conv).max())
 
