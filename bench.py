@@ -66,7 +66,8 @@ def log(msg):
 # --------------------------------------------------------------- byte models
 def forward_model(b, L, H, P, N, G, Q):
     """Algorithmic HBM bytes and flops of each kernel: every input read once,
-    every output written once (workspace intermediates included, Hin in bf16).
+    every output written once (workspace intermediates included, S and Hin in
+    bf16).
     state_scan does what chunk_state + state_passing do without S."""
     nc = -(-L // Q)
     tok = b * L
@@ -75,7 +76,7 @@ def forward_model(b, L, H, P, N, G, Q):
     dt = tok * H * 4
     rows = b * H * nc * Q * 4               # one of cs / dtc
     st = b * H * P * N * 4                  # init or final
-    S = b * H * nc * P * N * 4
+    S = b * H * nc * P * N * 2                # bf16, like Hin
     Hin = b * H * nc * P * N * 2
     bytes_ = {
         "chunk_cumsum": dt + 2 * rows,
@@ -137,6 +138,22 @@ def counter_traffic(kernel: str, workload: str):
     return float(m_bytes.group(1))
 
 
+def trace_average(kernel: str, workload: str):
+    """(average dispatch duration in us, file) of ``kernel`` in the committed
+    rocprofv3 kernel-trace summary of this workload's forward, or None."""
+    path = ROOT / "profiles" / f"ssd_forward_{workload}_kernel_trace.txt"
+    if not path.exists():
+        return None
+    for line in path.read_text().splitlines():
+        parts = line.split()
+        if len(parts) >= 3 and parts[0] == kernel:
+            try:
+                return float(parts[2]), str(path.relative_to(ROOT))
+            except ValueError:
+                return None
+    return None
+
+
 # -------------------------------------------------------------------- timing
 SETTLE_S = 0.3
 
@@ -176,40 +193,45 @@ def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup, zoh=False):
 
 
 def forward_kernels(dims):
-    """The stages ssd_forward runs (the one-pass state stage is timed beside
-    them but is not on the forward's path).  Where a group's head count is
-    even the forward's chunk-state kernel also forms the chunk cumsum, so no
-    separate cumsum launch runs; the stage timings below time the stage calls
-    themselves."""
+    """The kernels ssd_forward runs at these sizes, by the names of the stage
+    calls that launch the same kernels: chunk state (with the cumsum inside
+    where a group's head count is even), state passing and chunk_scan."""
     b, L, H, P, N, G, Q = dims
     fused = P == 64 and N == 128 and Q in (128, 256) and (H // G) % 2 == 0
     return (["chunk_state"] if fused else ["chunk_cumsum", "chunk_state"]) + \
         ["state_passing", "chunk_scan"]
 
 
-def time_stages(ssd, g, y, fin, ws, dims, steps):
-    """Average duration of each kernel (both state paths), from HIP events
-    recorded on the stream the stage calls are launched on (torch's current
-    stream)."""
+def time_stages(ssd, g, y, fin, dims, steps):
+    """Average duration of each kernel, from HIP events recorded on the
+    stream the stage calls are launched on (torch's current stream): the
+    forward's own kernels (through the stage calls that launch them) and the
+    two-kernel state path beside them.  Buffers of their own, not the
+    forward's workspace."""
     import ctypes
     import torch
     lib = ssd.load()
     b, L, H, P, N, G, Q = dims
-    reg = ssd.workspace_regions(b, L, H, P, N, Q, torch.bfloat16)
-    base = ws.data_ptr()
-    cs, dtc, S, Hin = (ctypes.c_void_p(base + reg[k][0]) for k in ("cs", "dtc", "S", "Hin"))
+    nc = -(-L // Q)
+    dev = g["x"].device
+    cs_t = torch.empty((b, H, nc, Q), dtype=torch.float32, device=dev)
+    dtc_t = torch.empty_like(cs_t)
+    S_t = torch.empty((b, H, nc, P, N), dtype=torch.bfloat16, device=dev)
+    Hin_t = torch.empty((b, H, nc, P, N), dtype=torch.bfloat16, device=dev)
+    cs, dtc, S, Hin = (ctypes.c_void_p(t.data_ptr()) for t in (cs_t, dtc_t, S_t, Hin_t))
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     p = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
-    names = ["chunk_cumsum", "chunk_state", "state_passing", "state_scan", "chunk_scan"]
+    names = ["chunk_cumsum", "chunk_state", "state_passing", "state_scan"]
     calls = [
         lambda: lib.ssd_chunk_cumsum(b, L, H, Q, p(g["dt"]), p(g["A"]), cs, dtc, stream),
         lambda: lib.ssd_chunk_state(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), cs, dtc, S, stream),
         lambda: lib.ssd_state_passing(b, L, H, P, N, Q, 1, S, cs, p(g["init"]), Hin, p(fin), stream),
         lambda: lib.ssd_state_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), cs, dtc,
                                    p(g["init"]), Hin, p(fin), stream),
-        lambda: lib.ssd_chunk_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["C"]), cs, dtc,
-                                   Hin, p(g["D"]), p(y), stream),
     ]
+    names.append("chunk_scan")
+    calls.append(lambda: lib.ssd_chunk_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["C"]),
+                                            cs, dtc, Hin, p(g["D"]), p(y), stream))
     for f in calls:            # warm
         assert f() == 0
     torch.cuda.synchronize()
@@ -330,12 +352,12 @@ def bench_state_passing_long(nsegs=(8, 32, 128), steps=10):
     A = -torch.exp(torch.rand(H, device="cuda", generator=gen) * spec.a_hi)
     cs, _ = ssd.chunk_cumsum(dt, A, Q)
     del dt
-    S = torch.randn(b, H, nc, P, N, device="cuda", generator=gen)
+    S = torch.randn(b, H, nc, P, N, device="cuda", generator=gen).to(torch.bfloat16)
     Hin = torch.empty(b, H, nc, P, N, dtype=torch.bfloat16, device="cuda")
     fin = torch.empty(b, H, P, N, device="cuda")
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    byts = S.numel() * 4 + Hin.numel() * 2 + fin.numel() * 4
+    byts = S.numel() * 2 + Hin.numel() * 2 + fin.numel() * 4
 
     def timed(f):
         assert f() == 0
@@ -362,6 +384,30 @@ def bench_state_passing_long(nsegs=(8, 32, 128), steps=10):
     return out
 
 
+def host_cpu():
+    """(CPU model name, physical core count) of this host from /proc/cpuinfo
+    (distinct (physical id, core id) pairs), or (None, None)."""
+    try:
+        text = Path("/proc/cpuinfo").read_text()
+    except OSError:
+        return None, None
+    model, cores, phys, core = None, set(), None, None
+    for line in text.splitlines() + [""]:
+        if ":" in line:
+            k, v = (t.strip() for t in line.split(":", 1))
+            if k == "model name" and model is None:
+                model = v
+            elif k == "physical id":
+                phys = v
+            elif k == "core id":
+                core = v
+        elif not line.strip():
+            if core is not None:
+                cores.add((phys, core))
+            phys = core = None
+    return model, (len(cores) or None)
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences of (batch, head) pairs, in batches of one pair per core,
@@ -380,7 +426,9 @@ def cpu_baseline(inp, budget_s=12.0):
         done += len(chunk)
         k = (k + len(chunk)) % len(pairs)
     tokens_equiv = done * L / H
+    model, physical = host_cpu()
     return {"value": tokens_equiv / t_total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "physical_cores": physical, "logical_cpus": os.cpu_count(),
             "sample": f"{done} (batch, head) sequences of {L} tokens of the same workload, cycling "
                       f"over its {len(pairs)} pairs (= {tokens_equiv:.0f} full-width tokens), "
                       f"in {t_total:.1f} s"}
@@ -407,7 +455,10 @@ def profile_loop(k: int):
     fin = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
     ws = torch.empty(ssd.workspace_bytes(b, L, H, P, N, G, Q, torch.bfloat16), dtype=torch.uint8,
                      device="cuda")
-    time_stages(ssd, g, y, fin, ws, dims, k)
+    for _ in range(k):   # the forward itself, so the trace holds its kernels as it runs them
+        ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], Q, g["init"], y=y,
+                        final_state=fin, workspace=ws)
+    time_stages(ssd, g, y, fin, dims, k)
     from mamba_ssd_scan_02_amd.workloads import DECODE_B256 as dspec
     from mamba_ssd_scan_02_amd.workloads import make_decode_static, make_decode_step
     st = make_decode_static(dspec)
@@ -428,7 +479,7 @@ def profile_loop(k: int):
 
 def _short_kernel(name: str) -> str:
     if "chunk_state" in name and ", true>" in name:
-        return "chunk_state+cumsum"   # the forward's chunk state with the cumsum inside
+        return "chunk_state+cumsum"   # chunk state with the cumsum inside
     for k in KERNEL_SOURCES:
         if k in name:
             return k
@@ -592,6 +643,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 130M-shaped forward printed beside the headline")
     ap.add_argument("--workload", default="mamba2_2p7b_b4_l8192_h80_p64_n128",
                     choices=["mamba2_2p7b_b4_l8192_h80_p64_n128", "mamba2_130m_b8_l2048_h24_p64_n128",
                              "long_b1_l1048576_h32_p64_n128_g8"],
@@ -663,7 +716,7 @@ def main():
     log(f"[bench] forward {ms * 1e3:.1f} us/step, {tokens_per_s:.4g} tokens/s")
 
     log("[bench] per-kernel event timing")
-    k_us = time_stages(ssd, g, y, fin, ws, dims, max(args.steps, 10))
+    k_us = time_stages(ssd, g, y, fin, dims, max(args.steps, 10))
     kbytes, kflops = forward_model(*dims)
     path = forward_kernels(dims)
     kernels = {}
@@ -680,7 +733,12 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(dom, spec.name), "kernel": dom,
-                "alg_bytes_per_launch": kbytes[dom], "avg_launch_us": round(d_us, 2)}
+                "alg_bytes_per_launch": kbytes[dom], "avg_launch_us": round(d_us, 2),
+                "timing": "HIP events on the launching stream, this run"}
+    tr = trace_average(dom, spec.name)
+    if tr is not None:
+        roofline["trace_avg_us"], roofline["trace_file"] = tr
+        roofline["trace_frac"] = round(kbytes[dom] / (tr[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     comp = compulsory_bytes(b, L, H, P, N, G)
     flops_total = sum(kflops[n] for n in path)
 
@@ -700,6 +758,23 @@ def main():
                  "algorithmic_flops": flops_total, "wall_s_timed_region": round(wall, 4)},
         "kernels": kernels,
     }
+    if headline and not args.no_extra:
+        from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M as s2
+        log(f"[bench] {s2.name} forward")
+        inp2 = make_forward_inputs(s2)
+        g2 = {k: (v.cuda() if v is not None else None) for k, v in inp2.items()}
+        y2 = torch.empty_like(g2["x"])
+        f2 = torch.empty((s2.batch, s2.nheads, s2.headdim, s2.dstate), dtype=torch.float32,
+                         device="cuda")
+        ws2 = torch.empty(ssd.workspace_bytes(s2.batch, s2.seqlen, s2.nheads, s2.headdim, s2.dstate,
+                                              s2.ngroups, s2.chunk, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        ms2, _ = time_forward(ssd, g2, y2, f2, ws2, s2.chunk, args.steps, args.warmup)
+        dims2 = (s2.batch, s2.seqlen, s2.nheads, s2.headdim, s2.dstate, s2.ngroups, s2.chunk)
+        out["forward_130m"] = {"workload": s2.name, "us_per_step": round(ms2 * 1e3, 2),
+                               "tokens_per_s": round(s2.batch * s2.seqlen / (ms2 * 1e-3), 1),
+                               "forward_kernels": forward_kernels(dims2)}
+        del g2, y2, f2, ws2
     log("[bench] zero-order-hold forward")
     ms_zoh, _ = time_forward(ssd, g, y, fin, ws, Q, args.steps, args.warmup, zoh=True)
     out["forward_zoh"] = {"us_per_step": round(ms_zoh * 1e3, 2),

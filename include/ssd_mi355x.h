@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 
@@ -103,9 +103,11 @@ const char* ssd_status_str(int32_t status);
  * 256-byte aligned and in this order:
  *     cs   fp32 [B][H][nc][Q]  log2(e) * inclusive prefix of dt*A in the chunk
  *     dtc  fp32 [B][H][nc][Q]  dt rearranged head-major (0 past the end)
- *     S    fp32 [B][H][nc][P][N]  each chunk's end state, starting from zero
- *     Hin  [B][H][nc][P][N]    state entering each chunk, in the storage type
- *                              (bf16 for bf16, fp32 for fp32)
+ *     S    [B][H][nc][P][N]    each chunk's end state, starting from zero
+ *     Hin  [B][H][nc][P][N]    state entering each chunk
+ * S and Hin are in the storage type (bf16 for bf16, fp32 for fp32): each is
+ * written once and read once, as a summand of the fp32 carried state (S) or
+ * a matrix operand (Hin); the carried state itself stays fp32.
  */
 size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
                                    int64_t headdim, int64_t dstate, int64_t ngroups,
@@ -116,7 +118,8 @@ size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
  * dt, A, B, C, D and an optional initial state, by the block algorithm with
  * chunk length `chunk` (see the block-algorithm sources above).  Runs, in
  * order on `stream`: ssd_chunk_cumsum, ssd_chunk_state, ssd_state_passing,
- * ssd_chunk_scan.
+ * ssd_chunk_scan (the cumsum inside the chunk-state launch where the
+ * paired-head matrix-core kernel applies).
  *   D           may be NULL: no skip term.
  *   init_state  may be NULL: zero initial state.  When given it is decayed by
  *               exp(dt_0 A) at the first token, like any carried state.
@@ -203,19 +206,21 @@ int32_t ssd_chunk_cumsum_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int6
                              const float* dt, const float* A, float* cs, float* dtc,
                              hipStream_t stream);
 
-/* S [B][H][nc][P][N]: each chunk's end state from a zero start,
- * S_c[p][n] = sum_j exp(Acs_last - Acs_j) dt_j x_j[p] B_j[n]
- * ("Il trucco a blocchi": only a summary state leaves a block). */
+/* S [B][H][nc][P][N] in the storage type: each chunk's end state from a
+ * zero start, S_c[p][n] = sum_j exp(Acs_last - Acs_j) dt_j x_j[p] B_j[n]
+ * ("Il trucco a blocchi": only a summary state leaves a block), accumulated
+ * in fp32 and rounded once. */
 int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                         int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                         const void* x, const void* B, const float* cs, const float* dtc,
-                        float* S, hipStream_t stream);
+                        void* S, hipStream_t stream);
 
-/* Hin (storage type of `dtype`) and final_state from S: the linear recurrence
- * between chunks, H_0 = init (or 0), Hin_c = H_c, H_{c+1} = exp(Acs_last) H_c
- * + S_c, final = H_nc.  init_state / final_state may be NULL and may alias. */
+/* Hin and final_state from S (both in the storage type of `dtype`): the
+ * linear recurrence between chunks in fp32, H_0 = init (or 0), Hin_c = H_c,
+ * H_{c+1} = exp(Acs_last) H_c + S_c, final = H_nc.  init_state /
+ * final_state may be NULL and may alias. */
 int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
-                          int64_t dstate, int64_t chunk, int32_t dtype, const float* S,
+                          int64_t dstate, int64_t chunk, int32_t dtype, const void* S,
                           const float* cs, const float* init_state, void* Hin,
                           float* final_state, hipStream_t stream);
 
@@ -238,7 +243,7 @@ size_t ssd_state_passing_seg_workspace_bytes(int64_t batch, int64_t nheads, int6
                                              int64_t dstate, int64_t nsegments);
 int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                               int64_t dstate, int64_t chunk, int64_t nsegments, int32_t dtype,
-                              const float* S, const float* cs, const float* init_state, void* Hin,
+                              const void* S, const float* cs, const float* init_state, void* Hin,
                               float* final_state, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
@@ -248,10 +253,13 @@ int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int
  * blocchi" run as the token recurrence of "Un sistema che riassume il
  * passato" with one factor per block).  Same arguments, layouts, aliasing
  * rules (init_state / final_state may be NULL and may alias) and outputs as
- * that pair.  Matrix-core path only: dtype bf16, headdim 64, dstate 128,
- * chunk 256; anything else returns SSD_ERR_UNSUPPORTED.  (ssd_forward runs
- * ssd_chunk_state and ssd_state_passing instead: on the MI355X that pair,
- * with two heads per chunk-state workgroup, measured faster.) */
+ * that pair.  One workgroup walks the whole sequence of each (batch, head
+ * pair) where the heads of a group pair up (chunk 128 or 256), of each
+ * (batch, head, half of P) otherwise (chunk 256).  Matrix-core path only:
+ * dtype bf16, headdim 64, dstate 128; anything else returns
+ * SSD_ERR_UNSUPPORTED.  (ssd_forward runs ssd_chunk_state and
+ * ssd_state_passing instead: one walk per CU cannot use the whole device's
+ * bandwidth, and that pair measured faster.) */
 int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                        const void* x, const void* B, const float* cs, const float* dtc,

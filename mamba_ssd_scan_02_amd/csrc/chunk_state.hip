@@ -38,6 +38,32 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, const float (&w)[8]) {
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// Store the two 32-row tiles acc[0..1] (MFMA result layout: register r of
+// lane (hf, l32) of wave w is row p = 32 mt + 8 (r / 4) + 4 hf + r % 4,
+// column n = 32 w + l32) of a P x N = 64 x 128 state into row-major bf16 at
+// dst.  Neighbouring lanes swap one value so that each holds two adjacent
+// columns of one row (registers r and r + 1 are rows p and p + 1) and writes
+// them as one word: even lanes row p at columns n, n + 1, odd lanes row p + 1
+// at columns n - 1, n.  Non-temporal: the state is read once, later.
+__device__ __forceinline__ void store_state_bf16(const f32x16 (&acc)[2], bf16_t* dst, int lane, int n) {
+    constexpr int N = 128;
+    const bool odd = (lane & 1) != 0;
+    const int hf = lane >> 5;
+    uint32_t* row = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float h0v = acc[mt][r], h1v = acc[mt][r + 1];
+            const float got = __shfl_xor(odd ? h0v : h1v, 1, 64);
+            const float keep = odd ? h1v : h0v;
+            const int rr = odd ? r + 1 : r;
+            const int p = 32 * mt + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+            const uint32_t w = odd ? pack_bf16x2(got, keep) : pack_bf16x2(keep, got);
+            __builtin_nontemporal_store(w, &row[(p * N + (n & ~1)) >> 1]);
+        }
+}
+
 constexpr int kStateRing = 3;
 // Stages issued after stage jt when step jt waits for it (R - 1 are issued
 // ahead, none past the last of NT).
@@ -70,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
                                                                   const bf16_t* __restrict__ Bm,
                                                                   const float* __restrict__ cs,
                                                                   const float* __restrict__ dtc,
-                                                                  float* __restrict__ S, int L, int H,
+                                                                  bf16_t* __restrict__ S, int L, int H,
                                                                   int G, int nc) {
     constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
     constexpr int DPS = 12 / W;          // copies per wave per 32-token stage
@@ -150,14 +176,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
         }
     }
 
-    float* Sp = S + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N);
-    const int n = 32 * wave + l32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int p = 8 * (r >> 2) + 4 * hf + (r & 3);
-        __builtin_nontemporal_store(acc[0][r], &Sp[p * N + n]);
-        __builtin_nontemporal_store(acc[1][r], &Sp[(32 + p) * N + n]);
-    }
+    store_state_bf16(acc, S + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), lane, 32 * wave + l32);
 }
 
 // HG (2 or 4) heads per workgroup: one workgroup per (batch, chunk, HG
@@ -233,6 +252,21 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
     }
 }
 
+// LDS of the paired-head body below.
+template <int Q, int HG>
+struct StateSmem {
+    uint4 bsr[kStateRing][512];
+    uint4 xsr[kStateRing][32 * 128 * HG / 16];
+    float wv[HG][Q];
+    double wsum[HG][4];
+    float cslast[HG];
+};
+
+// The chunk states of HG heads of one group for one (batch, chunk): acc[e][mt]
+// = S_c of head h0 + e, p tile mt, in the MFMA result layout (lane (hf, l32)
+// of wave w, register r: p = 32 mt + 8 (r / 4) + 4 hf + r % 4, n = 32 w + l32);
+// cl[e] = the chunk's summed decay (cs of its last token, log2 units).
+//
 // FUSE: the workgroup also forms its heads' chunk cumsum (what
 // chunk_cumsum_kernel computes) from dt and A instead of reading cs and dtc:
 // an fp64 inclusive prefix of dt A log2(e) over the chunk's tokens (a wave
@@ -240,44 +274,37 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
 // zero-order-hold weight) as dtc.  Both rows are written out at the end for
 // the later stages.
 template <int Q, int HG, bool FUSE>
-__global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t* __restrict__ x,
-                                                                   const bf16_t* __restrict__ Bm,
-                                                                   const float* cs, const float* dtc,
-                                                                   float* __restrict__ S, int L,
-                                                                   int H, int G, int nc,
-                                                                   const float* __restrict__ dtin,
-                                                                   const float* __restrict__ A,
-                                                                   float* csw, float* dtcw, int zoh) {
-    constexpr int P = 64, N = 128, W = 4, NT = Q / 32;
+__device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, int c, int h0,
+                                                 const bf16_t* __restrict__ x,
+                                                 const bf16_t* __restrict__ Bm, const float* cs,
+                                                 const float* dtc, int L, int H, int G, int nc,
+                                                 const float* __restrict__ dtin,
+                                                 const float* __restrict__ A, float* csw,
+                                                 float* dtcw, int zoh, f32x16 (&acc)[HG][2],
+                                                 float (&cl)[HG]) {
+    constexpr int W = 4, NT = Q / 32;
     constexpr int XR = 128 * HG;                         // bytes of a token's x row
     constexpr int DPS = 8 / W + BxhOffsets<W, HG>::XC;   // copies per wave per stage
     constexpr int R = kStateRing;
     static_assert(state_ring_waits_hold(NT, R, DPS), "chunk_state wait counts do not cover its copies");
-    __shared__ uint4 bsr[R][512];
-    __shared__ uint4 xsr[R][32 * XR / 16];
-    __shared__ float wv[HG][Q];
+    auto& bsr = sm.bsr;
+    auto& xsr = sm.xsr;
+    auto& wv = sm.wv;
 
-    const int HP = H / HG;
-    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int h0 = HG * (int)(wg % (uint32_t)HP);
-    const int bc = (int)(wg / (uint32_t)HP);
-    const int c = bc % nc, b = bc / nc;
     const int g = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hf = lane >> 5, l32 = lane & 31;
+    const int hf = lane >> 5;
     const int64_t row0 = (((int64_t)b * H + h0) * nc + c) * Q;   // head h0 + e: + e * nc * Q
     const int tok0 = c * Q;
-    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
-    const bf16_t* xbase = x + ((int64_t)b * L * H + h0) * P;
-    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
+    const int64_t xstride = (int64_t)H * 64, bstride = (int64_t)G * 128;
+    const bf16_t* xbase = x + ((int64_t)b * L * H + h0) * 64;
+    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * 128;
 
     // ordinary loads first (their values are used, so waited for, before the
     // copies are issued): w_j = exp2(cs_last - cs_j) dt_j for each head
     float wreg[HG];
     float csv[HG], dcv[HG];    // FUSE: this thread's token's cs and dtc
-    __shared__ double wsum[HG][4];
-    __shared__ float cslast[HG];
     double v[HG];              // FUSE: dt A log2(e) of this thread's token, then its prefix
     if constexpr (FUSE) {
         float dl[HG];
@@ -299,6 +326,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
         for (int e = 0; e < HG; ++e) {
             const int64_t row = row0 + (int64_t)e * nc * Q;
             wreg[e] = tid < Q ? fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid] : 0.0f;
+            cl[e] = cs[row + Q - 1];
         }
     }
     asm volatile("" ::: "memory");
@@ -316,19 +344,22 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
                 const double o = __shfl_up(v[e], off2, 64);
                 if (lane >= off2) v[e] += o;
             }
-            if (lane == 63) wsum[e][wave] = v[e];
+            if (lane == 63) sm.wsum[e][wave] = v[e];
         }
         barrier_lds();
 #pragma unroll
         for (int e = 0; e < HG; ++e) {
             double base = 0.0;
-            for (int w2 = 0; w2 < wave; ++w2) base += wsum[e][w2];
+            for (int w2 = 0; w2 < wave; ++w2) base += sm.wsum[e][w2];
             csv[e] = (float)(base + v[e]);
-            if (tid == Q - 1) cslast[e] = csv[e];
+            if (tid == Q - 1) sm.cslast[e] = csv[e];
         }
         barrier_lds();
 #pragma unroll
-        for (int e = 0; e < HG; ++e) wreg[e] = tid < Q ? fast_exp2(cslast[e] - csv[e]) * dcv[e] : 0.0f;
+        for (int e = 0; e < HG; ++e) {
+            cl[e] = sm.cslast[e];
+            wreg[e] = tid < Q ? fast_exp2(cl[e] - csv[e]) * dcv[e] : 0.0f;
+        }
     }
     if (tid < Q) {
 #pragma unroll
@@ -339,7 +370,6 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     const int trow0 = 8 * (grp >> 1) + (rr >> 2);
     const int qcol = 16 * (grp & 1) + 4 * (rr & 3);
 
-    f32x16 acc[HG][2];   // [head][p tile]
 #pragma unroll
     for (int e = 0; e < HG; ++e) acc[e][0] = acc[e][1] = f32x16{};
 #pragma unroll
@@ -393,16 +423,230 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
             }
         }
     }
-    const int n = 32 * wave + l32;
+}
+
+// One workgroup (4 waves) per (batch, chunk, HG heads of one group); each
+// writes its heads' S_c (and, with FUSE, their cumsum rows).
+template <int Q, int HG, bool FUSE>
+__global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t* __restrict__ x,
+                                                                   const bf16_t* __restrict__ Bm,
+                                                                   const float* cs, const float* dtc,
+                                                                   bf16_t* __restrict__ S, int L,
+                                                                   int H, int G, int nc,
+                                                                   const float* __restrict__ dtin,
+                                                                   const float* __restrict__ A,
+                                                                   float* csw, float* dtcw, int zoh) {
+    constexpr int P = 64, N = 128;
+    __shared__ StateSmem<Q, HG> sm;
+    const int HP = H / HG;
+    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int h0 = HG * (int)(wg % (uint32_t)HP);
+    const int bc = (int)(wg / (uint32_t)HP);
+    const int c = bc % nc, b = bc / nc;
+    f32x16 acc[HG][2];
+    float cl[HG];
+    chunk_state_pair<Q, HG, FUSE>(sm, b, c, h0, x, Bm, cs, dtc, L, H, G, nc, dtin, A, csw, dtcw, zoh,
+                                  acc, cl);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int e = 0; e < HG; ++e) {
-        float* Sp = S + (((int64_t)b * H + h0 + e) * nc + c) * (int64_t)(P * N);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = 8 * (r >> 2) + 4 * hf + (r & 3);
-            __builtin_nontemporal_store(acc[e][0][r], &Sp[p * N + n]);
-            __builtin_nontemporal_store(acc[e][1][r], &Sp[(32 + p) * N + n]);
+    for (int e = 0; e < HG; ++e)
+        store_state_bf16(acc[e], S + (((int64_t)b * H + h0 + e) * nc + c) * (int64_t)(P * N), lane,
+                         32 * wave + (lane & 31));
+}
+
+// ---------------------------------------------------------------------------
+// Walked chunk state: chunk state and the recurrence between chunks in one
+// pass per (batch, head pair), so that no chunk's S reaches memory.  Only
+// the summary state crosses from one block to the next (page "Mamba-2
+// (2024): SSM e attention sono la stessa cosa", section "Il trucco a
+// blocchi"): one workgroup (4 waves, one per CU) walks the whole sequence of
+// its two heads in 32-token blocks, keeping the running state in the MFMA
+// accumulators (the layout of the paired-head chunk state above: wave w owns
+// state columns n in [32w, 32w + 32) of both heads).  At each chunk's start
+// it writes the state entering the chunk (Hin, bf16) and scales the state by
+// the chunk's decay, H <- exp2(cs_last) H; the chunk's products, weighted
+// w_j = exp2(cs_last - cs_j) dt_j as in S_c, then accumulate onto it, which
+// leaves exp2(cs_last) H_c + S_c = H_{c+1}.  After the last chunk the state
+// is the final state.
+//
+// B and the two heads' x rows stream through an 8-stage LDS ring (16 KB a
+// stage, seven stages ahead: the walk of one chain is paced by how much is
+// in flight, not by the CU's throughput), and each chunk's cs/dt rows arrive
+// one chunk ahead.  Blocks past the end re-read the last token (their
+// weights are zero) and rows past the last chunk read as zeros, so every
+// wave issues the same operations at every step and every wait is a
+// constant (checked at compile time below).
+constexpr int kWalkRing = 8;                           // ring stages (7 ahead)
+constexpr int kWalkDps = 4;                            // copies per wave per stage (B 2, x 2)
+constexpr int kWalkRows = 4;                           // row copies per wave per chunk
+constexpr int kWalkHin = 32;                           // Hin stores per wave per chunk
+
+// Operations issued after stage k = c NT + jt when step jt of chunk c waits
+// for it: the stages issued ahead of it, plus chunk c's Hin stores and the
+// next chunk's row copies when they came after stage k's copies.
+__host__ __device__ constexpr int walk_ops_after(int NT, int jt) {
+    return (kWalkRing - 2) * kWalkDps + (jt < kWalkRing - 1 ? kWalkHin + kWalkRows : 0);
+}
+// The issue order replayed against those waits over a few chunks (labels:
+// stage k, rows of chunk c, Hin stores of chunk c): at each step its stage,
+// and at each chunk's start (after a wait that leaves only the previous
+// chunk's NT stages pending) its rows, must have landed.
+constexpr bool walk_waits_hold(int NT, int nc) {
+    auto stl = [](int k) { return 1000 + k; };
+    auto rwl = [](int c) { return 5000 + c; };
+    VmemLog o;
+    o.push(rwl(0), kWalkRows);
+    for (int k = 0; k < kWalkRing - 1; ++k) o.push(stl(k), kWalkDps);
+    if (!o.wait((kWalkRing - 1) * kWalkDps) || !o.landed(rwl(0))) return false;
+    for (int c = 0; c < nc; ++c) {
+        if (c > 0 && (!o.wait(NT * kWalkDps) || !o.landed(rwl(c)))) return false;
+        o.push(6000 + c, kWalkHin);
+        o.push(rwl(c + 1), kWalkRows);
+        for (int jt = 0; jt < NT; ++jt) {
+            const int k = c * NT + jt;
+            if (!o.wait(walk_ops_after(NT, jt)) || !o.landed(stl(k))) return false;
+            o.push(stl(k + kWalkRing - 1), kWalkDps);
         }
+    }
+    return true;
+}
+static_assert(walk_waits_hold(8, 1) && walk_waits_hold(8, 3) && walk_waits_hold(4, 1) &&
+              walk_waits_hold(4, 4), "state walk wait counts do not cover its copies");
+
+template <int NT>
+__global__ __launch_bounds__(256, 1) void state_walk_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const float* __restrict__ cs,
+    const float* __restrict__ dtc, const float* init, bf16_t* __restrict__ Hin, float* fin, int L,
+    int H, int G, int nc) {
+    constexpr int Q = 32 * NT, HG = 2, W = 4, P = 64, N = 128, R = kWalkRing;
+    constexpr int XR = 128 * HG;
+    static_assert(BxhOffsets<W, HG>::XC + 8 / W == kWalkDps, "copies per stage");
+    __shared__ uint4 bsr[R][512];            // B blocks: 32 x 256 B
+    __shared__ uint4 xsr[R][32 * XR / 16];   // x blocks: 32 x (2 heads x 128 B)
+    __shared__ float rows[2][HG][2][Q];      // cs and dt rows by chunk parity
+    __shared__ float wv[HG][Q];
+
+    const int HP = H / HG;
+    const int b = (int)blockIdx.x / HP, h0 = HG * ((int)blockIdx.x % HP);
+    const int g = h0 / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int n = 32 * wave + l32;
+    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+    const bf16_t* xbase = x + ((int64_t)b * L * H + h0) * P;
+    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
+    const int64_t rowbase = ((int64_t)b * H + h0) * nc;   // (b, h0, chunk 0) row; head h0 + e at + e nc
+    const BxhOffsets<W, HG> off = bxh_offsets<W, HG>(wave, lane, xstride, bstride);
+
+    // cs / dt rows of chunk c (records empty past the last chunk): wave w
+    // copies row e = w / 2, array w % 2, 256 floats in 4 copies
+    const int re = wave >> 1, ra = wave & 1;
+    const float* rsrc = (ra == 0 ? cs : dtc) + (rowbase + (int64_t)re * nc) * Q;
+    auto issue_rows = [&](int c) {
+        const __amdgpu_buffer_rsrc_t rr = make_rs(rsrc + (int64_t)c * Q, c < nc ? Q * 4 : 0);
+#pragma unroll
+        for (int i = 0; i < kWalkRows; ++i)
+            dma4_rs(rr, 4u * (uint32_t)(64 * i + lane) % (4u * Q), lds(&rows[c & 1][re][ra][0]) + (64 * i) % Q);
+    };
+    auto issue_stage = [&](int k) {
+        issue_bxh_stage<W, HG>(wave, lane, 32 * k, L, xbase, xstride, bbase, bstride, off, bsr[k % R],
+                               xsr[k % R]);
+    };
+
+    // running state, from init or zero
+    f32x16 acc[HG][2];
+#pragma unroll
+    for (int e = 0; e < HG; ++e)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int p = 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                acc[e][mt][r] = init ? init[(((int64_t)b * H + h0 + e) * P + p) * N + n] : 0.0f;
+            }
+    asm volatile("" ::: "memory");
+    issue_rows(0);
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) issue_stage(k);
+    wait_vmcnt<(R - 1) * kWalkDps>();   // rows of chunk 0
+
+    const int grp = lane >> 4, rr4 = lane & 15;
+    const int trow0 = 8 * (grp >> 1) + (rr4 >> 2);
+    const int qcol = 16 * (grp & 1) + 4 * (rr4 & 3);
+    const bool odd = (lane & 1) != 0;
+
+    for (int c = 0; c < nc; ++c) {
+        // chunk c's rows were copied at chunk c - 1's start, before its NT stages
+        if (c > 0) wait_vmcnt<NT * kWalkDps>();
+        barrier_lds();   // chunk c's rows are visible; every wave is done with chunk c - 1's weights
+        float cl[HG];
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const float* rc = rows[c & 1][e][0];
+            cl[e] = rc[Q - 1];
+            if (tid < Q) wv[e][tid] = fast_exp2(cl[e] - rc[tid]) * rows[c & 1][e][1][tid];
+        }
+        // the state entering chunk c (bf16), then its decay
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            store_state_bf16(acc[e], Hin + (rowbase + (int64_t)e * nc + c) * (int64_t)(P * N), lane, n);
+            const float a = fast_exp2(cl[e]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[e][mt][r] *= a;
+        }
+        issue_rows(c + 1);
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+            const int k = c * NT + jt;
+            wait_vmcnt_n(walk_ops_after(NT, jt));   // a constant once the loop is unrolled
+            barrier_lds();                          // stage k (and, at jt = 0, the weights) visible
+            issue_stage(k + R - 1);
+            const SSD_LDS char* xb = (const SSD_LDS char*)lds(xsr[k % R]);
+            const SSD_LDS char* bb = (const SSD_LDS char*)lds(bsr[k % R]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r0 = 16 * u + trow0, r1 = r0 + 4;
+                uint4 bq;
+                {
+                    const int nc4 = 32 * wave + qcol;
+                    const int chk = nc4 >> 3, sub = (nc4 & 7) * 2;
+                    const uint2 lo = tr16(bb + r0 * 256 + ((chk ^ swz_b(r0)) << 4) + sub);
+                    const uint2 hi = tr16(bb + r1 * 256 + ((chk ^ swz_b(r1)) << 4) + sub);
+                    bq = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+#pragma unroll
+                for (int e = 0; e < HG; ++e) {
+                    float wj[8];
+#pragma unroll
+                    for (int sidx = 0; sidx < 8; ++sidx) wj[sidx] = wv[e][32 * jt + 16 * u + 8 * hf + sidx];
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, scale_bf16x8(bq, wj));
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const int pc = 64 * e + 32 * mt + qcol;
+                        const int chk = pc >> 3, sub = (pc & 7) * 2;
+                        const uint2 lo = tr16(xb + r0 * XR + ((chk ^ swz_b(r0)) << 4) + sub);
+                        const uint2 hi = tr16(xb + r1 * XR + ((chk ^ swz_b(r1)) << 4) + sub);
+                        const bf16x8 xq = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                        acc[e][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, bw, acc[e][mt], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();   // prefetches past the end land before the workgroup's LDS goes away
+    if (fin) {
+#pragma unroll
+        for (int e = 0; e < HG; ++e)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int p = 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    fin[(((int64_t)b * H + h0 + e) * P + p) * N + n] = acc[e][mt][r];
+                }
     }
 }
 
@@ -412,7 +656,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
 template <typename T, int MAXO>
 __global__ __launch_bounds__(256) void chunk_state_generic_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ cs,
-    const float* __restrict__ dtc, float* __restrict__ S, int L, int H, int P, int N, int G,
+    const float* __restrict__ dtc, T* __restrict__ S, int L, int H, int P, int N, int G,
     int Q, int nc) {
     extern __shared__ float smem[];
     float* xs = smem;              // [32][P]
@@ -461,28 +705,28 @@ __global__ __launch_bounds__(256) void chunk_state_generic_kernel(
         }
         __syncthreads();
     }
-    float* Sp = S + (((int64_t)b * H + h) * nc + c) * (int64_t)PN;
+    T* Sp = S + (((int64_t)b * H + h) * nc + c) * (int64_t)PN;
 #pragma unroll
     for (int k = 0; k < MAXO; ++k) {
         const int o = tid + 256 * k;
-        if (o < PN) Sp[o] = acc[k];
+        if (o < PN) Elem<T>::store(Sp, o, acc[k]);
     }
 }
 
 template <typename T, int MAXO>
 static void launch_generic(const Dims& d, const void* x, const void* B, const float* cs,
-                           const float* dtc, float* S, hipStream_t stream) {
+                           const float* dtc, void* S, hipStream_t stream) {
     const size_t shmem = sizeof(float) * (32 * (d.headdim + d.dstate) + 32);
     const unsigned blocks = (unsigned)(d.batch * d.nchunks * d.nheads);
     chunk_state_generic_kernel<T, MAXO><<<blocks, 256, shmem, stream>>>(
-        static_cast<const T*>(x), static_cast<const T*>(B), cs, dtc, S, (int)d.seqlen,
+        static_cast<const T*>(x), static_cast<const T*>(B), cs, dtc, static_cast<T*>(S), (int)d.seqlen,
         (int)d.nheads, (int)d.headdim, (int)d.dstate, (int)d.ngroups, (int)d.chunk,
         (int)d.nchunks);
 }
 
 template <typename T>
 static void launch_generic_t(const Dims& d, const void* x, const void* B, const float* cs,
-                             const float* dtc, float* S, hipStream_t stream) {
+                             const float* dtc, void* S, hipStream_t stream) {
     const int64_t per = (d.headdim * d.dstate + 255) / 256;
     if (per <= 1) launch_generic<T, 1>(d, x, B, cs, dtc, S, stream);
     else if (per <= 2) launch_generic<T, 2>(d, x, B, cs, dtc, S, stream);
@@ -510,8 +754,9 @@ bool chunk_state_fuses_cumsum(int32_t dtype, const Dims& d) {
 }
 
 hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B, const float* dt,
-                                    const float* A, bool zoh, float* cs, float* dtc, float* S,
+                                    const float* A, bool zoh, float* cs, float* dtc, void* Sv,
                                     hipStream_t stream) {
+    bf16_t* S = static_cast<bf16_t*>(Sv);
     const unsigned hblocks = (unsigned)(d.batch * d.nchunks * d.nheads / kStateHeads);
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* bb = static_cast<const bf16_t*>(B);
@@ -524,9 +769,29 @@ hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B,
     return hipGetLastError();
 }
 
+bool state_walk_applies(int32_t dtype, const Dims& d) {
+    return mfma_path(dtype, d) && (d.nheads / d.ngroups) % 2 == 0;
+}
+
+hipError_t launch_state_walk(const Dims& d, const void* x, const void* B, const float* cs,
+                             const float* dtc, const float* init, void* Hin, float* final_state,
+                             hipStream_t stream) {
+    const unsigned blocks = (unsigned)(d.batch * (d.nheads / 2));
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* bb = static_cast<const bf16_t*>(B);
+    bf16_t* hb = static_cast<bf16_t*>(Hin);
+    const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
+    if (d.chunk == 128)
+        state_walk_kernel<4><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, init, hb, final_state, L, H, G, nc);
+    else
+        state_walk_kernel<8><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, init, hb, final_state, L, H, G, nc);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const void* B,
-                              const float* cs, const float* dtc, float* S, hipStream_t stream) {
+                              const float* cs, const float* dtc, void* Sv, hipStream_t stream) {
     if (mfma_path(dtype, d)) {
+        bf16_t* S = static_cast<bf16_t*>(Sv);
         const unsigned blocks = (unsigned)(d.batch * d.nchunks * d.nheads);
         const bf16_t* xb = static_cast<const bf16_t*>(x);
         const bf16_t* bb = static_cast<const bf16_t*>(B);
@@ -544,9 +809,9 @@ hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const
             default: chunk_state_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
         }
     } else if (dtype == 1) {
-        launch_generic_t<bf16_t>(d, x, B, cs, dtc, S, stream);
+        launch_generic_t<bf16_t>(d, x, B, cs, dtc, Sv, stream);
     } else {
-        launch_generic_t<float>(d, x, B, cs, dtc, S, stream);
+        launch_generic_t<float>(d, x, B, cs, dtc, Sv, stream);
     }
     return hipGetLastError();
 }

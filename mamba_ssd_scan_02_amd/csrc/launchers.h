@@ -21,17 +21,18 @@ bool generic_path(const Dims& d);
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* cs,
                                float* dtc, hipStream_t stream, bool zoh = false);
 
+// S in the storage type (bf16 for the matrix-core path).
 hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const void* B,
-                              const float* cs, const float* dtc, float* S, hipStream_t stream);
+                              const float* cs, const float* dtc, void* S, hipStream_t stream);
 
 // Chunk state that also forms the chunk cumsum (cs, dtc written for the
 // later stages), where the paired-head matrix-core kernel applies.
 bool chunk_state_fuses_cumsum(int32_t dtype, const Dims& d);
 hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B, const float* dt,
-                                    const float* A, bool zoh, float* cs, float* dtc, float* S,
+                                    const float* A, bool zoh, float* cs, float* dtc, void* S,
                                     hipStream_t stream);
 
-hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, const float* cs,
+hipError_t launch_state_passing(const Dims& d, int32_t dtype, const void* S, const float* cs,
                                 const float* init, void* Hin, float* final_state,
                                 hipStream_t stream);
 
@@ -40,13 +41,20 @@ hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, co
 void state_passing_segments(int64_t nc, int64_t nseg_req, int64_t* seg, int64_t* nseg);
 size_t state_passing_seg_workspace_bytes(int64_t batch, int64_t H, int64_t P, int64_t N,
                                          int64_t nseg);
-hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_req, const float* S,
+hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_req, const void* S,
                                     const float* cs, const float* init, void* Hin,
                                     float* final_state, void* workspace, hipStream_t stream);
 
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream);
+
+// Chunk state and state passing walked per (batch, head pair) in one pass
+// (bf16 matrix-core path, chunk 128 or 256, an even head count per group).
+bool state_walk_applies(int32_t dtype, const Dims& d);
+hipError_t launch_state_walk(const Dims& d, const void* x, const void* B, const float* cs,
+                             const float* dtc, const float* init, void* Hin, float* final_state,
+                             hipStream_t stream);
 
 // Chunk state and state passing in one pass (bf16 matrix-core path, chunk 256).
 hipError_t launch_state_scan(const Dims& d, const void* x, const void* B, const float* cs,

@@ -64,6 +64,8 @@ int32_t check_supported(int32_t dtype, const Dims& d) {
     return SSD_ERR_UNSUPPORTED;
 }
 
+// Workspace of ssd_forward (layout documented at ssd_forward_workspace_bytes):
+// cs, dtc, S and Hin, the last two in the storage type.
 struct Layout {
     size_t cs, dtc, S, Hin, total;
 };
@@ -78,13 +80,13 @@ bool workspace_layout(const Dims& d, int32_t dtype, Layout* lo) {
     size_t per_chunk_state = (size_t)d.headdim * (size_t)d.dstate;
     if (!mul_ok((size_t)d.batch * (size_t)d.nheads, (size_t)d.nchunks, &t)) return false;
     if (!mul_ok(t, per_chunk_state, &states)) return false;
-    size_t b_cs, b_S, b_H;
-    if (!mul_ok(rows, 4, &b_cs) || !mul_ok(states, 4, &b_S) || !mul_ok(states, es, &b_H)) return false;
+    size_t b_cs, b_st;
+    if (!mul_ok(rows, 4, &b_cs) || !mul_ok(states, es, &b_st)) return false;
     lo->cs = 0;
     lo->dtc = align_up(b_cs);
     lo->S = lo->dtc + align_up(b_cs);
-    lo->Hin = lo->S + align_up(b_S);
-    lo->total = lo->Hin + align_up(b_H);
+    lo->Hin = lo->S + align_up(b_st);
+    lo->total = lo->Hin + align_up(b_st);
     return true;
 }
 
@@ -155,7 +157,7 @@ int32_t ssd_chunk_cumsum_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int6
 int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                         int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                         const void* x, const void* B, const float* cs, const float* dtc,
-                        float* S, hipStream_t stream) {
+                        void* S, hipStream_t stream) {
     Dims d;
     int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
     if (st != SSD_OK) return st;
@@ -167,7 +169,7 @@ int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
 }
 
 int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
-                          int64_t dstate, int64_t chunk, int32_t dtype, const float* S,
+                          int64_t dstate, int64_t chunk, int32_t dtype, const void* S,
                           const float* cs, const float* init_state, void* Hin,
                           float* final_state, hipStream_t stream) {
     Dims d;
@@ -191,7 +193,7 @@ size_t ssd_state_passing_seg_workspace_bytes(int64_t batch, int64_t nheads, int6
 
 int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                               int64_t dstate, int64_t chunk, int64_t nsegments, int32_t dtype,
-                              const float* S, const float* cs, const float* init_state, void* Hin,
+                              const void* S, const float* cs, const float* init_state, void* Hin,
                               float* final_state, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
     Dims d;
@@ -222,12 +224,15 @@ int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     if (st != SSD_OK) return st;
     size_t es;
     if (!elem_size(dtype, &es)) return SSD_ERR_UNSUPPORTED;
-    if (!ssd::mfma_path(dtype, d) || d.chunk != 256) return SSD_ERR_UNSUPPORTED;
+    const bool walk = ssd::state_walk_applies(dtype, d);
+    if (!walk && (!ssd::mfma_path(dtype, d) || d.chunk != 256)) return SSD_ERR_UNSUPPORTED;
     if (!x || !B || !cs || !dtc || !Hin) return SSD_ERR_NULL;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(Hin, 16) || !aligned(cs, 4) ||
         !aligned(dtc, 4) || (init_state && !aligned(init_state, 16)) ||
         (final_state && !aligned(final_state, 16)))
         return SSD_ERR_ALIGN;
+    if (walk)
+        return hip_status(ssd::launch_state_walk(d, x, B, cs, dtc, init_state, Hin, final_state, stream));
     return hip_status(ssd::launch_state_scan(d, x, B, cs, dtc, init_state, Hin, final_state, stream));
 }
 
@@ -300,13 +305,13 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     char* ws = static_cast<char*>(workspace);
     float* cs = reinterpret_cast<float*>(ws + lo.cs);
     float* dtc = reinterpret_cast<float*>(ws + lo.dtc);
-    float* S = reinterpret_cast<float*>(ws + lo.S);
+    void* S = ws + lo.S;
     void* Hin = ws + lo.Hin;
 
+    hipError_t e;
     // chunk cumsum and chunk states (one launch where the paired-head kernel
     // applies), then the recurrence between chunks (the one-pass
     // ssd_state_scan measured slower than this pair at every shape tried)
-    hipError_t e;
     if (ssd::chunk_state_fuses_cumsum(dtype, d)) {
         e = ssd::launch_chunk_state_fused(d, x, B, dt, A, zoh, cs, dtc, S, stream);
         if (e != hipSuccess) return SSD_ERR_HIP;

@@ -1,6 +1,9 @@
 // state_passing.hip -- the linear recurrence between chunks, sequential and
 // segmented.
 //
+// S and Hin are in the storage type (bf16 on the matrix-core path); the
+// carried state itself is fp32.
+//
 // Only the summary state travels from one block to the next (page "Mamba-2
 // (2024): SSM e attention sono la stessa cosa", section "Il trucco a blocchi"),
 // and the update has the general linear form h_t = A_t h_{t-1} + b_t of page
@@ -42,6 +45,22 @@ __device__ __forceinline__ Vec<VW> load_vec(const float* p, int64_t i) {
     return r;
 }
 
+// S in bf16 (the matrix-core path stores it in the storage type).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int VW>
+__device__ __forceinline__ Vec<VW> load_vec(const bf16_t* p, int64_t i) {
+    Vec<VW> r;
+    if constexpr (VW == 4) {
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + i);
+        r.v[0] = bf16_bits_to_f32(t[0] & 0xffffu); r.v[1] = bf16_bits_to_f32(t[0] >> 16);
+        r.v[2] = bf16_bits_to_f32(t[1] & 0xffffu); r.v[3] = bf16_bits_to_f32(t[1] >> 16);
+    } else {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) r.v[e] = bf16_bits_to_f32(p[i * VW + e].bits);
+    }
+    return r;
+}
+
 template <int VW>
 __device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r) {
     if constexpr (VW >= 4) {
@@ -72,7 +91,7 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
 
 // Walks n >= 1 chunks of one thread's VW state elements:
 //     [store h at hp], h <- exp2(lg_c) h + S_c,   c = 0 .. n - 1,
-// where S_c sits at src + c * sstep (floats) and lg_c, the chunk's decay in
+// where S_c sits at src + c * sstep (elements of ST) and lg_c, the chunk's decay in
 // log2 units, at dec[c * dstep].  kStore writes the entering state of every
 // chunk (hp advances by sstep); kSum adds the lg_c into *lsum.
 //
@@ -82,8 +101,8 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
 // beyond the group; the last 1..PF chunks run from the ring with no further
 // loads.  (A load or store under a branch makes the compiler wait for the
 // ring's loads at the join, which serialises it.)
-template <typename HT, int PF, int VW, bool kStore, bool kSum>
-__device__ __forceinline__ void walk_chunks(const float* __restrict__ src, int64_t sstep,
+template <typename ST, typename HT, int PF, int VW, bool kStore, bool kSum>
+__device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t sstep,
                                             const float* __restrict__ dec, int64_t dstep, int n,
                                             HT* hp, Vec<VW>& h, float* lsum) {
     Vec<VW> buf[PF];
@@ -148,7 +167,7 @@ __device__ __forceinline__ Vec<VW> start_state(const float* init, int64_t idx) {
 // (batch, head) on x, so the decays are uniform across a workgroup and come
 // from scalar loads, off the vector memory counter that paces the S ring.
 template <typename HT, int PF, int VW>
-__global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ S,
+__global__ __launch_bounds__(256) void state_passing_kernel(const HT* __restrict__ S,
                                                             const float* __restrict__ cs,
                                                             const float* init, HT* __restrict__ Hin,
                                                             float* fin, int pnv, int nc, int Q) {
@@ -158,8 +177,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
     const int64_t idx = bh * pnv + off;
     Vec<VW> h = start_state<VW>(init, idx);
     const int64_t base = (bh * nc * (int64_t)pnv + off) * VW;
-    walk_chunks<HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW, cs + bh * nc * (int64_t)Q + (Q - 1),
-                                         Q, nc, Hin + base, h, nullptr);
+    walk_chunks<HT, HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW, cs + bh * nc * (int64_t)Q + (Q - 1),
+                                             Q, nc, Hin + base, h, nullptr);
     if (fin) store_vec<VW>(fin, idx, h);
 }
 
@@ -176,8 +195,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
 //   3. seg_down:   each segment again from Hs_s, writing Hin (all in parallel).
 // Depth nc / nseg + nseg instead of nc, for 1.5x the S reads.
 
-template <int PF, int VW>
-__global__ __launch_bounds__(256) void sp_seg_reduce_kernel(const float* __restrict__ S,
+template <typename ST, int PF, int VW>
+__global__ __launch_bounds__(256) void sp_seg_reduce_kernel(const ST* __restrict__ S,
                                                             const float* __restrict__ cs,
                                                             float* __restrict__ E,
                                                             float* __restrict__ Dseg, int pnv,
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(256) void sp_seg_reduce_kernel(const float* __restr
 #pragma unroll
     for (int e = 0; e < VW; ++e) h.v[e] = 0.0f;
     float ls = 0.0f;
-    walk_chunks<float, PF, VW, false, true>(S + ((bh * nc + c0) * (int64_t)pnv + off) * VW,
+    walk_chunks<ST, float, PF, VW, false, true>(S + ((bh * nc + c0) * (int64_t)pnv + off) * VW,
                                             (int64_t)pnv * VW,
                                             cs + (bh * nc + c0) * (int64_t)Q + (Q - 1), Q, n,
                                             (float*)nullptr, h, &ls);
@@ -211,13 +230,13 @@ __global__ __launch_bounds__(256) void sp_seg_carry_kernel(const float* __restri
     const int64_t idx = bh * pnv + off;
     Vec<VW> h = start_state<VW>(init, idx);
     const int64_t base = (bh * nseg * (int64_t)pnv + off) * VW;
-    walk_chunks<float, PF, VW, true, false>(E + base, (int64_t)pnv * VW, Dseg + bh * nseg, 1, nseg,
-                                            Hs + base, h, nullptr);
+    walk_chunks<float, float, PF, VW, true, false>(E + base, (int64_t)pnv * VW, Dseg + bh * nseg, 1, nseg,
+                                                   Hs + base, h, nullptr);
     if (fin) store_vec<VW>(fin, idx, h);
 }
 
 template <typename HT, int PF, int VW>
-__global__ __launch_bounds__(256) void sp_seg_down_kernel(const float* __restrict__ S,
+__global__ __launch_bounds__(256) void sp_seg_down_kernel(const HT* __restrict__ S,
                                                           const float* __restrict__ cs,
                                                           const float* __restrict__ Hs,
                                                           HT* __restrict__ Hin, int pnv, int nc,
@@ -229,18 +248,18 @@ __global__ __launch_bounds__(256) void sp_seg_down_kernel(const float* __restric
     const int c0 = s * seg, n = min(seg, nc - c0);
     Vec<VW> h = load_vec<VW>(Hs, (bh * nseg + s) * (int64_t)pnv + off);
     const int64_t base = ((bh * nc + c0) * (int64_t)pnv + off) * VW;
-    walk_chunks<HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW,
-                                         cs + (bh * nc + c0) * (int64_t)Q + (Q - 1), Q, n, Hin + base,
-                                         h, nullptr);
+    walk_chunks<HT, HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW,
+                                             cs + (bh * nc + c0) * (int64_t)Q + (Q - 1), Q, n, Hin + base,
+                                             h, nullptr);
 }
 
 template <typename HT, int PF, int VW>
-static void launch_sp_vw(const Dims& d, const float* S, const float* cs, const float* init,
+static void launch_sp_vw(const Dims& d, const void* S, const float* cs, const float* init,
                          void* Hin, float* fin, hipStream_t stream) {
     const int pnv = (int)(d.headdim * d.dstate / VW);
     const dim3 grid((unsigned)(d.batch * d.nheads), (unsigned)((pnv + 255) / 256));
     state_passing_kernel<HT, PF, VW><<<grid, 256, 0, stream>>>(
-        S, cs, init, reinterpret_cast<HT*>(Hin), fin, pnv, (int)d.nchunks, (int)d.chunk);
+        static_cast<const HT*>(S), cs, init, reinterpret_cast<HT*>(Hin), fin, pnv, (int)d.nchunks, (int)d.chunk);
 }
 
 // Four elements per thread where P * N allows (measured best at the
@@ -250,7 +269,7 @@ static void launch_sp_vw(const Dims& d, const float* S, const float* cs, const f
 // chains of 4,096 chunks: 2.32 ms with the old branchy ring, 1.28 ms now, the
 // same at depths 16 to 48).
 template <typename HT>
-static void launch_sp(const Dims& d, const float* S, const float* cs, const float* init,
+static void launch_sp(const Dims& d, const void* S, const float* cs, const float* init,
                       void* Hin, float* fin, hipStream_t stream) {
     const bool longseq = d.nchunks >= 64;
     if ((d.headdim * d.dstate) % 4 == 0) {
@@ -285,8 +304,9 @@ size_t state_passing_seg_workspace_bytes(int64_t batch, int64_t H, int64_t P, in
 }
 
 template <typename HT, int VW>
-static void launch_seg_vw(const Dims& d, int64_t seg, int64_t nseg, const float* S, const float* cs,
+static void launch_seg_vw(const Dims& d, int64_t seg, int64_t nseg, const void* Sv, const float* cs,
                           const float* init, void* Hin, float* fin, char* ws, hipStream_t stream) {
+    const HT* S = static_cast<const HT*>(Sv);
     const int pnv = (int)(d.headdim * d.dstate / VW);
     const int64_t states = d.batch * d.nheads * nseg * d.headdim * d.dstate * 4;
     float* E = reinterpret_cast<float*>(ws);
@@ -295,7 +315,7 @@ static void launch_seg_vw(const Dims& d, int64_t seg, int64_t nseg, const float*
     const unsigned bh = (unsigned)(d.batch * d.nheads), eb = (unsigned)((pnv + 255) / 256);
     const dim3 g3(bh, (unsigned)nseg, eb), g2(bh, eb);
     constexpr int PFS = VW == 4 ? 8 : 16;   // segment walks: many waves hide the latency
-    sp_seg_reduce_kernel<PFS, VW><<<g3, 256, 0, stream>>>(S, cs, E, Dseg, pnv, (int)d.nchunks,
+    sp_seg_reduce_kernel<HT, PFS, VW><<<g3, 256, 0, stream>>>(S, cs, E, Dseg, pnv, (int)d.nchunks,
                                                           (int)d.chunk, (int)seg, (int)nseg);
     sp_seg_carry_kernel<16, VW><<<g2, 256, 0, stream>>>(E, Dseg, init, Hs, fin, pnv, (int)nseg);
     sp_seg_down_kernel<HT, PFS, VW><<<g3, 256, 0, stream>>>(S, cs, Hs, reinterpret_cast<HT*>(Hin), pnv,
@@ -303,7 +323,7 @@ static void launch_seg_vw(const Dims& d, int64_t seg, int64_t nseg, const float*
                                                             (int)nseg);
 }
 
-hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_req, const float* S,
+hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_req, const void* S,
                                     const float* cs, const float* init, void* Hin,
                                     float* final_state, void* workspace, hipStream_t stream) {
     int64_t seg, nseg;
@@ -320,7 +340,7 @@ hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_r
     return hipGetLastError();
 }
 
-hipError_t launch_state_passing(const Dims& d, int32_t dtype, const float* S, const float* cs,
+hipError_t launch_state_passing(const Dims& d, int32_t dtype, const void* S, const float* cs,
                                 const float* init, void* Hin, float* final_state,
                                 hipStream_t stream) {
     if (dtype == 1)

@@ -21,7 +21,7 @@ DTYPE_BF16 = 1
 
 # The SSD_ABI_VERSION this binding was written against; load() refuses a
 # library that reports another one (a stale build).
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _STATUS_OK = 0
 
@@ -85,6 +85,7 @@ def load():
     lib.ssd_layer_in.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp]
     lib.ssd_layer_out.restype = i32
     lib.ssd_layer_out.argtypes = [i64, i32, vp, vp, vp, vp]
+
     got = int(lib.ssd_abi_version())
     if got != ABI_VERSION:
         raise RuntimeError(f"{_LIB_PATH} reports ABI version {got}, this binding needs "
@@ -153,7 +154,8 @@ def workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtyp
 
 def workspace_regions(batch, seqlen, nheads, headdim, dstate, chunk, dtype):
     """Byte offsets and element counts of cs, dtc, S, Hin inside the workspace
-    (the layout documented at ssd_forward_workspace_bytes)."""
+    (the layout documented at ssd_forward_workspace_bytes; S and Hin in the
+    storage type)."""
     nc = n_chunks(seqlen, chunk)
     es = 2 if dtype == torch.bfloat16 else 4
     up = lambda v: (v + 255) // 256 * 256
@@ -161,7 +163,7 @@ def workspace_regions(batch, seqlen, nheads, headdim, dstate, chunk, dtype):
     states = batch * nheads * nc * headdim * dstate
     off_dtc = up(rows * 4)
     off_S = off_dtc + up(rows * 4)
-    off_H = off_S + up(states * 4)
+    off_H = off_S + up(states * es)
     return dict(cs=(0, rows), dtc=(off_dtc, rows), S=(off_S, states), Hin=(off_H, states),
                 total=off_H + up(states * es))
 
@@ -255,7 +257,7 @@ def chunk_cumsum(dt, A, chunk, zoh=False):
 
 
 def chunk_state(x, B, cs, dtc, chunk):
-    """S [batch, H, nc, P, N] fp32 -- see ssd_chunk_state."""
+    """S [batch, H, nc, P, N] in x's dtype -- see ssd_chunk_state."""
     lib = load()
     x = _dev(x, "x")
     batch, L, H, P = x.shape
@@ -264,7 +266,7 @@ def chunk_state(x, B, cs, dtc, chunk):
     _dev(B, "B", x.dtype, (batch, L, G, N), x.device)
     _dev(cs, "cs", torch.float32, (batch, H, nc, chunk), x.device)
     _dev(dtc, "dtc", torch.float32, (batch, H, nc, chunk), x.device)
-    S = torch.empty((batch, H, nc, P, N), dtype=torch.float32, device=x.device)
+    S = torch.empty((batch, H, nc, P, N), dtype=x.dtype, device=x.device)
     _check("ssd_chunk_state", lib.ssd_chunk_state(batch, L, H, P, N, G, chunk, _dtype_code(x),
                                                   _p(x), _p(B), _p(cs), _p(dtc), _p(S),
                                                   _stream(x.device)))
@@ -272,9 +274,10 @@ def chunk_state(x, B, cs, dtc, chunk):
 
 
 def state_passing(S, cs, seqlen, chunk, dtype, init_state=None, final_state=None):
-    """(Hin [batch, H, nc, P, N] in ``dtype``, final [batch, H, P, N] fp32)."""
+    """(Hin [batch, H, nc, P, N] in ``dtype``, final [batch, H, P, N] fp32)
+    from S in ``dtype``."""
     lib = load()
-    S = _dev(S, "S", torch.float32)
+    S = _dev(S, "S", dtype)
     batch, H, nc, P, N = S.shape
     _dev(cs, "cs", torch.float32, (batch, H, nc, chunk), S.device)
     _dev(init_state, "init_state", torch.float32, (batch, H, P, N), S.device)
@@ -292,9 +295,10 @@ def state_passing(S, cs, seqlen, chunk, dtype, init_state=None, final_state=None
 def state_passing_seg(S, cs, seqlen, chunk, dtype, nsegments, init_state=None, final_state=None,
                       workspace=None):
     """(Hin, final) as state_passing, by the two-level associative scan over
-    ``nsegments`` segments of chunks -- see ssd_state_passing_seg."""
+    ``nsegments`` segments of chunks -- see ssd_state_passing_seg (S in
+    ``dtype``)."""
     lib = load()
-    S = _dev(S, "S", torch.float32)
+    S = _dev(S, "S", dtype)
     batch, H, nc, P, N = S.shape
     _dev(cs, "cs", torch.float32, (batch, H, nc, chunk), S.device)
     _dev(init_state, "init_state", torch.float32, (batch, H, P, N), S.device)

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 4
+    assert lib.ssd_abi_version() == 5
     for s in range(8):
         assert lib.ssd_status_str(s)
     assert lib.ssd_status_str(99) == b"unknown status"
@@ -55,11 +55,15 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_bytes(lib):
     import mamba_ssd_scan_02_amd as ssd
+    import torch
     n = lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 1, 256, 1)
-    regions = ssd.workspace_regions(4, 8192, 80, 64, 128, 256, __import__("torch").bfloat16)
+    regions = ssd.workspace_regions(4, 8192, 80, 64, 128, 256, torch.bfloat16)
     assert n == regions["total"]
     nc = 32
-    assert n >= 4 * 80 * nc * 256 * 4 * 2 + 4 * 80 * nc * 64 * 128 * (4 + 2)
+    # cs, dtc fp32; S and Hin in the storage type (bf16)
+    assert n >= 4 * 80 * nc * 256 * 4 * 2 + 4 * 80 * nc * 64 * 128 * 2 * 2
+    n = lib.ssd_forward_workspace_bytes(1, 256, 1, 16, 16, 1, 64, 0)
+    assert n == ssd.workspace_regions(1, 256, 1, 16, 16, 64, torch.float32)["total"]
     assert lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 3, 256, 1) == 0   # H % G
     assert lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 1, 512, 1) == 0   # chunk
     assert lib.ssd_forward_workspace_bytes(1, 8, 1, 256, 16, 1, 8, 0) == 0         # P too big
@@ -139,8 +143,12 @@ def test_stage_argument_errors(lib):
                                P(0x4000), None) == NULL
     assert lib.ssd_state_passing(1, 64, 2, 64, 128, 64, 1, P(0x1000), P(0x2000), None, P(0x3008),
                                  None, None) == ALIGN
-    # the one-pass state stage exists for bf16, P = 64, N = 128, chunk 256 only
-    assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 128, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
+    # the one-pass state stage exists for bf16, P = 64, N = 128, chunk 128 or
+    # 256 with heads that pair up in a group, else chunk 256 (no call below
+    # passes its checks: none may reach a launch)
+    assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 64, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
+                              None, P(0x4000), None, None) == UNSUP
+    assert lib.ssd_state_scan(1, 64, 3, 64, 128, 1, 128, 1, P(0x1000), P(0x2000), P(0x10), P(0x20),
                               None, P(0x4000), None, None) == UNSUP
     assert lib.ssd_state_scan(1, 64, 2, 64, 128, 1, 256, 0, P(0x1000), P(0x2000), P(0x10), P(0x20),
                               None, P(0x4000), None, None) == UNSUP

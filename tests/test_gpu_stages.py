@@ -167,26 +167,33 @@ def test_stage_intermediates_deterministic():
 
 
 SCAN_CASES = [
-    # (name, batch, L, H, G, init, alias init/final)
-    ("one_chunk", 1, 256, 2, 1, True, False),
-    ("ragged", 2, 700, 4, 2, True, False),
-    ("one_token_tail", 1, 513, 3, 1, False, False),
-    ("many_chunks", 1, 2600, 2, 2, True, False),
-    ("short", 1, 40, 2, 1, True, False),
-    ("aliased_state", 1, 600, 2, 1, True, True),
-    ("head_pairs_two_groups", 2, 1000, 8, 2, True, False),
+    # (name, batch, L, H, G, chunk, init, alias init/final); an even head
+    # count per group takes the walked (head-pair) kernel, an odd one the
+    # per-head kernel
+    ("one_chunk", 1, 256, 2, 1, 256, True, False),
+    ("ragged", 2, 700, 4, 2, 256, True, False),
+    ("one_token_tail", 1, 513, 3, 1, 256, False, False),
+    ("many_chunks", 1, 2600, 2, 2, 256, True, False),
+    ("short", 1, 40, 2, 1, 256, True, False),
+    ("aliased_state", 1, 600, 2, 1, 256, True, True),
+    ("head_pairs_two_groups", 2, 1000, 8, 2, 256, True, False),
+    ("walk_many_chunks", 1, 40 * 256 + 77, 4, 1, 256, True, False),
+    ("walk_chunk128_ragged", 2, 1000, 4, 1, 128, True, False),
+    ("walk_chunk128_one_chunk", 1, 100, 2, 1, 128, False, False),
+    ("walk_chunk128_aliased", 1, 33 * 128, 6, 3, 128, True, True),
 ]
 
 
 @pytest.mark.parametrize("case", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
 def test_state_scan(case):
-    """The one-pass chunk-state + state-passing kernel against the fp64 stage
-    definitions (Hin and final state), and against the two-kernel GPU path."""
+    """The one-pass chunk-state + state-passing kernels against the fp64
+    stage definitions (Hin and final state), and against the two-kernel GPU
+    path."""
     import mamba_ssd_scan_02_amd as ssd
     from oracle import stages
 
-    name, batch, L, H, G, init, alias = case
-    P, N, Q = 64, 128, 256
+    name, batch, L, H, G, Q, init, alias = case
+    P, N = 64, 128
     say(f"[state_scan] {name}")
     inp = _inputs(21, batch, L, H, P, N, G, "bf16", init=init)
     g = to_gpu(inp)
@@ -302,7 +309,7 @@ def test_state_passing_segmented_long_context():
     A = -torch.exp(torch.rand(H, device="cuda", generator=gen))
     cs, _ = ssd.chunk_cumsum(dt, A, Q)
     del dt
-    S = torch.randn(b, H, nc, P, N, device="cuda", generator=gen) * 0.1
+    S = (torch.randn(b, H, nc, P, N, device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
     init = torch.randn(b, H, P, N, device="cuda", generator=gen) * 0.3
     Hin, fin = ssd.state_passing(S, cs, L, Q, torch.bfloat16, init)
     Hin2, fin2 = ssd.state_passing_seg(S, cs, L, Q, torch.bfloat16, 64, init_state=init)
@@ -323,3 +330,4 @@ def test_state_passing_segmented_deterministic():
     r1 = ssd.state_passing_seg(S, cs, 1000, 64, torch.bfloat16, 5, init_state=g["init"])
     r2 = ssd.state_passing_seg(S, cs, 1000, 64, torch.bfloat16, 5, init_state=g["init"])
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
