@@ -139,6 +139,27 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
                     hipStream_t stream);
 
 /*
+ * ssd_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation, arguments and errors without the workspace arguments.  The
+ * workspace is a device array of SSD_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends; the call itself
+ * allocates nothing.  Sizes whose workspace (ssd_forward_workspace_bytes)
+ * exceeds it return SSD_ERR_WORKSPACE before any launch: 64 MiB holds, for
+ * example, the Mamba-2-130M-shaped layer (batch 8, 2,048 tokens, 24 heads of
+ * 64, N = 128, chunk 256).  Every call on one device shares that device's
+ * array: calls whose executions overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * has to start at zero; it keeps whatever the last call left there.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t ssd_forward_noalloc(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                            const void* x, const float* dt, const float* A, const void* B,
+                            const void* C, const float* D, const float* init_state, void* y,
+                            float* final_state, hipStream_t stream);
+
+/*
  * ssd_forward with the exact zero-order hold for the input term: the step
  * adds expm1(dt A) / A * x (outer) B instead of dt * x (outer) B (dt itself
  * where A = 0), i.e. Bbar = (Abar - 1) / A B, the discretisation of the

@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "launchers.h"
 
@@ -98,6 +99,37 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+// Workspace of ssd_forward_noalloc: one array per device, resident from the
+// library's load until the process ends.  Host code never uses the array's
+// name as an address: its device address is looked up once per device
+// (scratch_address) and that pointer is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call made with that device current).
+int32_t scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SSD_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
 
 }  // namespace
 
@@ -336,6 +368,26 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
     return forward_impl(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, x, dt, A,
                         B, C, D, init_state, y, final_state, workspace, workspace_bytes, stream,
                         false);
+}
+
+int32_t ssd_forward_noalloc(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                            const void* x, const float* dt, const float* A, const void* B,
+                            const void* C, const float* D, const float* init_state, void* y,
+                            float* final_state, hipStream_t stream) {
+    Dims d;
+    int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
+    if (st != SSD_OK) return st;
+    if ((st = check_supported(dtype, d)) != SSD_OK) return st;
+    Layout lo;
+    if (!workspace_layout(d, dtype, &lo)) return SSD_ERR_SHAPE;
+    if (lo.total > (size_t)SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != SSD_OK) return st;
+    return forward_impl(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, x, dt, A,
+                        B, C, D, init_state, y, final_state, ws, (size_t)SSD_NOALLOC_SCRATCH_BYTES,
+                        stream, false);
 }
 
 int32_t ssd_forward_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,

@@ -61,6 +61,8 @@ def load():
     lib.ssd_forward.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp, sz, vp]
     lib.ssd_forward_zoh.restype = i32
     lib.ssd_forward_zoh.argtypes = lib.ssd_forward.argtypes
+    lib.ssd_forward_noalloc.restype = i32
+    lib.ssd_forward_noalloc.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp]
     lib.ssm_step.restype = i32
     lib.ssm_step.argtypes = [i64] * 5 + [i32] + [vp] * 8 + [vp]
     lib.ssm_step_zoh.restype = i32

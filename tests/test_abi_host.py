@@ -114,6 +114,22 @@ def test_forward_argument_errors(lib):
     # (final_state on init_state is allowed: tests/test_gpu_forward.py runs it)
 
 
+def test_noalloc_rejects_before_any_call(lib):
+    """ssd_forward_noalloc refuses sizes whose workspace exceeds its scratch
+    array, bad sizes and missing pointers before any GPU call."""
+    P = ctypes.c_void_p
+    p = P(0x10000)
+    assert lib.ssd_forward_workspace_bytes(4, 8192, 80, 64, 128, 1, 256, 1) > 64 << 20
+    assert lib.ssd_forward_noalloc(4, 8192, 80, 64, 128, 1, 256, 1, p, p, p, p, p, None, None, p,
+                                   None, None) == WS
+    assert lib.ssd_forward_noalloc(0, 64, 2, 64, 128, 1, 256, 1, p, p, p, p, p, None, None, p,
+                                   None, None) == SHAPE
+    assert lib.ssd_forward_noalloc(1, 64, 2, 64, 128, 1, 512, 1, p, p, p, p, p, None, None, p,
+                                   None, None) == UNSUP
+    assert lib.ssd_forward_noalloc(1, 64, 2, 64, 128, 1, 256, 1, None, p, p, p, p, None, None, p,
+                                   None, None) == NULL
+
+
 def test_step_argument_errors(lib):
     P = ctypes.c_void_p
 
