@@ -38,7 +38,8 @@
  *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major
  *    array; the caller allocates and owns all memory, including the
  *    workspace.  The library allocates nothing and keeps no pointer after a
- *    call returns; it has no mutable global state, so calls are reentrant.
+ *    call returns; apart from ssd_forward_noalloc's per-device array (see
+ *    there) it has no mutable global state, so calls are reentrant.
  *  - Work is enqueued on `stream` (NULL = the null stream) and the call
  *    returns at once.  SSD_OK means every kernel was launched; results are
  *    valid once the stream has completed.  No call synchronises.

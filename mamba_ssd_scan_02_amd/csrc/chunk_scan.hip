@@ -33,11 +33,17 @@
 //     of its token: two 16-byte stores per tile.
 //   * Term (ii) first: Y^T = Hin C^T (K = N), then each column scaled by
 //     exp2(cs_i).
-// Wave w owns i tiles {w, 2W-1-w} so that every wave has the same number of
-// causal (j <= i) tiles.  C fragments of the wave's own tokens stay in
-// registers for the whole kernel; the carried state and the j blocks of B
-// (32 rows) and x (32 rows) are copied straight into LDS (lds_pipe.h) through
-// a 3-buffer ring, two blocks ahead, and x is read back transposed with tr16.
+// Two kernels share these steps:
+//   * the streaming kernel (Q in {128, 256}): wave w owns i tiles
+//     {w, 2W-1-w} so that every wave has the same number of causal (j <= i)
+//     tiles; C fragments of the wave's own tokens stay in registers; the
+//     carried state and the j blocks of B (32 rows) and x (32 rows) are
+//     copied straight into LDS (lds_pipe.h) through a 3-buffer ring, two
+//     blocks ahead, and x is read back transposed with tr16;
+//   * the resident kernel (Q = 256, long runs of heads sharing one B/C
+//     group): G^T does not depend on the head, so it is formed once per
+//     chunk and kept in registers across the run, two waves per SIMD (see
+//     its own description below).
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
@@ -129,11 +135,23 @@ constexpr bool diag_lanes_match() {
 }
 static_assert(diag_lanes_match(), "diagonal lane masks disagree with the register layout");
 
-// b in the lanes of mask m, a elsewhere: one select, no compare.
+// b in the lanes of mask m, a elsewhere: one select, no compare.  Its
+// operands must not come straight from a matrix-core product: the compiler
+// does not see inside the asm, so it would not insert the wait states that
+// reading an MFMA result needs (mask_causal below is the form for those).
 __device__ __forceinline__ float lane_select(float a, float b, uint64_t m) {
     float d;
     asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(m));
     return d;
+}
+
+// The causal mask j <= i of a diagonal block's G^T tile, applied to the
+// MFMA result itself with plain selects (the compiler then waits for the
+// product before reading it): lane (l32, hf) keeps register r iff
+// l32 >= gt_row(r, hf).
+__device__ __forceinline__ void mask_causal(f32x16& a, int l32, int hf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = l32 >= gt_row(r, hf) ? a[r] : 0.0f;
 }
 
 // C fragments of the wave's own tokens (B operand of both C products).
@@ -560,86 +578,10 @@ __global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Resident kernel (Q = 256): one workgroup of 4 waves per CU and per (batch,
-// chunk, group, run of heads).  G^T = B_j C_i^T does not depend on the head,
-// so each wave forms its 9 causal G^T tiles once (8 products each, operands
-// loaded straight into registers) and keeps them in registers for all of the
-// run's heads; per head only the decay weights, the Y^T products and the
-// carried-state product remain.  A head's x rows, carried state and cs/dt
-// rows (50 KB) are copied into one of three LDS slots two heads ahead, so
-// the workgroup meets once per head.
-//   per wave and head, in issue order: copies for head k + 2 (x 8, Hin 4,
-//   cs 1, dt 1), then the y stores of its two tiles (4 each).
-// Wave w owns i tiles t1 = 7 - w (blocks 0..7-w, processed first) and
-// t0 = w (blocks 0..w): slot s < 8 - w is (t1, s), slot s >= 8 - w is
-// (t0, s - 8 + w).
-namespace rsl {
-constexpr int kX = 0;          // x: 256 rows x 128 B
-constexpr int kH = 32768;      // Hin: 64 rows x 256 B
-constexpr int kCs = 49152;     // cs: 256 floats
-constexpr int kDt = 50176;     // dt: 256 floats
-constexpr int kSlot = 51200;
-constexpr int kCopies = 14;    // LDS-copy instructions per wave per head
-constexpr int kStores = 8;     // y stores per wave per head
-constexpr int kPartCopies[4] = {4, 4, 4, 2};   // x rows 0..127, x rows 128..255, Hin, cs + dt
-static_assert(kPartCopies[0] + kPartCopies[1] + kPartCopies[2] + kPartCopies[3] == kCopies, "copy count");
-
-// The resident kernel's issue order (labels: copies of head k, y stores of
-// head k) replayed against its waits at the top of each head: head k's
-// copies must have landed.  Its tile-(7 - w) stores follow slot 3 for every
-// wave, so both store groups come after the head's copies.
-constexpr bool waits_hold(int heads) {
-    VmemLog o;
-    o.push(100, kCopies);
-    o.push(101, kCopies);
-    for (int k = 0; k < heads; ++k) {
-        const int cnt = k == 0 ? 0 : (k == 1 ? kCopies + kStores : kCopies + 2 * kStores);
-        if (!o.wait(cnt) || !o.landed(100 + k)) return false;
-        for (int part = 0; part < 4; ++part) o.push(100 + k + 2, kPartCopies[part]);
-        o.push(200 + k, kStores);
-    }
-    return true;
-}
-static_assert(waits_hold(1) && waits_hold(2) && waits_hold(3) && waits_hold(12) && waits_hold(40),
-              "resident chunk_scan wait counts do not cover its copies");
-}  // namespace rsl
-
-// Carried-state term of both of the wave's tiles, acc[q][mt] = sstate_q *
-// Hin C_q^T (q = 0: t0, 1: t1).  The 16 Hin fragments are read at the top
-// of the head (rs_hin_read), ahead of the head's other LDS work: with one
-// wave per SIMD nothing else would cover their latency.
+// Pieces of the resident kernel below (Q = 256): per-slot LDS operands, the
+// slot's weights and its products.
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void rs_hin_read(u32x4v (&a)[8][2], const SSD_LDS uint4* hs, int hf, int l32) {
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int pr = 32 * mt + perm_sigma(l32);
-            const int ch = 2 * kk + hf;
-            a[kk][mt] = *reinterpret_cast<const SSD_LDS u32x4v*>(hs + pr * 16 + (ch ^ swz_h(pr)));
-        }
-}
-__device__ __forceinline__ void rs_state_terms(f32x16 (&acc)[2][2], const u32x4v (&a)[8][2],
-                                               const uint4 (&cf)[2][8], const TileF (&tf)[2]) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[q][mt] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kk][mt]), __builtin_bit_cast(bf16x8, cf[q][kk]), acc[q][mt], 0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[q][mt][r] *= tf[q].sstate;
-}
 
 // LDS operands of one slot: the rf values of the lane's 16 block tokens
 // (rs_fetch_rf) and the X^T fragments of the block (rs_fetch_x, xq[mt][u]).
@@ -698,26 +640,28 @@ __device__ __forceinline__ void rs_weights_fact(u32x4v (&gq)[2], const f32x16& g
     gq[0] = u32x4v{pk[0], pk[1], pk[2], pk[3]};
     gq[1] = u32x4v{pk[4], pk[5], pk[6], pk[7]};
 }
+// Direct weights, exp2(cs_i - cs_j) dt_j per element, with D added on the
+// diagonal by constant lane masks (no per-lane flag values that the
+// compiler would keep live across the head loop).
 __device__ __forceinline__ void rs_weights_direct(u32x4v (&gq)[2], const f32x16& gt,
                                                   const SSD_LDS float* csb, const SSD_LDS float* dtb,
-                                                  float csi, float Dh, bool dgb, int hf, int l32) {
+                                                  float csi, float Dh, bool dgb, int hf) {
     // gt is zero above the diagonal of a diagonal block
     const SSD_LDS float* cb = csb + 8 * hf;
     const SSD_LDS float* db = dtb + 8 * hf;
-    const uint32_t deq = dgb ? diag_eq_bits(l32, hf) : 0u;
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int jl = 16 * (r >> 3) + (r & 7);
+        v[r] = gt[r] * (fast_exp2(fminf(csi - cb[jl], 0.0f)) * db[jl]);
+    }
+    if (dgb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = lane_select(v[r], v[r] + Dh, diag_eq_lanes(r));
+    }
     uint32_t pk[8];
 #pragma unroll
-    for (int r2 = 0; r2 < 8; ++r2) {
-        float v2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int r = 2 * r2 + e;
-            const int jl = 16 * (r >> 3) + (r & 7);
-            const float df = (float)((deq >> r) & 1u);
-            v2[e] = gt[r] * (fast_exp2(fminf(csi - cb[jl], 0.0f)) * db[jl]) + Dh * df;
-        }
-        pk[r2] = pack_bf16x2(v2[0], v2[1]);
-    }
+    for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
     gq[0] = u32x4v{pk[0], pk[1], pk[2], pk[3]};
     gq[1] = u32x4v{pk[4], pk[5], pk[6], pk[7]};
 }
@@ -733,33 +677,354 @@ __device__ __forceinline__ void rs_products(f32x16 (&acc)[2], const SlotX& x, co
                                                               __builtin_bit_cast(bf16x8, gq[u]), acc[mt], 0, 0, 0);
 }
 
-// y rows of tile t (lane owns token 32 t + l32, channels 32 mt + 16 hf +
-// 0..15) after the final column scale; 4 buffer stores, dropped past the end.
-__device__ __forceinline__ void rs_store(const f32x16 (&acc)[2], float colf, __amdgpu_buffer_rsrc_t yrs,
-                                         int rowbytes, int t, int hf, int l32) {
-    const int off = (32 * t + l32) * rowbytes + 32 * hf;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        uint32_t w8[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) w8[k] = pack_bf16x2(acc[mt][2 * k] * colf, acc[mt][2 * k + 1] * colf);
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 v0 = {w8[0], w8[1], w8[2], w8[3]};
-        const u32x4 v1 = {w8[4], w8[5], w8[6], w8[7]};
-        __builtin_amdgcn_raw_buffer_store_b128(v0, yrs, off + 64 * mt, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(v1, yrs, off + 64 * mt + 16, 0, 0);
+// ---------------------------------------------------------------------------
+// Paired resident kernel (Q = 256): one workgroup of 8 waves per CU and per
+// (batch, chunk, group, run of heads), two waves per SIMD, so that one
+// wave's vector work (the decay weights) overlaps the other's matrix-core
+// products and LDS reads.  The chunk's 36 causal 32 x 32 blocks and 8
+// carried-state terms are split over 4 pairs of waves: pair p owns output
+// tiles 7 - p and p (9 blocks).  Its lead wave (waves 0..3) takes blocks
+// 0..4 of tile 7 - p and that tile's state term; its helper wave (waves
+// 4..7) takes blocks 5..7 - p of tile 7 - p, all of tile p and tile p's
+// state term.  The helper's partial sums of tile 7 - p reach the lead through
+// LDS.  Each wave keeps the G^T tiles of its own 5 or 4 blocks in registers
+// for the whole run of heads.  A head's x rows, carried state and cs/dt rows
+// are copied into one of two LDS slots one head ahead, spread over the
+// previous head's blocks.  Every wave stores its tile of head k after the
+// barrier that opens head k + 1 (the lead of pairs 0..2 once it has added
+// the helper's partial sums), so the workgroup still meets once per head:
+// it writes the tile as bf16 rows into the four 1 KB pieces of head k's
+// slot that it will itself fill with head k + 2's x rows, and stores them
+// back as whole 128-byte token rows (8 lanes per row) -- the y traffic
+// then leaves the CU as full-line writes rather than 16-byte pieces.
+namespace rpl {
+constexpr int kX = 0;          // x: 256 rows x 128 B
+constexpr int kH = 32768;      // Hin: 64 rows x 256 B
+constexpr int kCs = 49152;     // cs: 256 floats
+constexpr int kDt = 50176;     // dt: 256 floats
+constexpr int kSlot = 51200;
+constexpr int kRedTile = 8192;                 // one tile's partial sums: 32 tokens x 64 channels fp32
+constexpr int kRed = 2 * kSlot;                // [head parity][pair 0..2] partial tiles
+constexpr int kRf = kRed + 2 * 3 * kRedTile;   // [wave][160] rf rows of the wave's blocks
+constexpr int kBytes = kRf + 8 * 160 * 4;
+static_assert(kBytes <= 160 * 1024, "paired chunk_scan LDS");
+constexpr int kCopies = 7;     // LDS-copy instructions per wave per head: x 4, Hin 2, cs or dt 1
+constexpr int kStores = 4;     // y stores of one tile (8 token rows each)
+
+// The issue order of one wave (labels: copies of head k, y stores of head
+// k) replayed against its wait at the top of each head, vmcnt(0): head k's
+// copies must have landed (trivially: nothing may be outstanding).
+constexpr bool waits_hold(int heads) {
+    VmemLog o;
+    o.push(100, kCopies);
+    for (int k = 0; k < heads; ++k) {
+        if (!o.wait(0) || !o.landed(100 + k)) return false;
+        if (k > 0) o.push(1000 + k - 1, kStores);
+        if (k + 1 < heads) o.push(100 + k + 1, kCopies);
     }
+    return true;
+}
+static_assert(waits_hold(1) && waits_hold(2) && waits_hold(40), "paired chunk_scan waits");
+
+// Byte offset of 16-byte chunk c of token row r (0..31) of a staged y tile
+// within its 1 KB piece (rows 8 m .. 8 m + 7 in piece m): the chunk index
+// is XORed with (r / 2) % 8 so that the 16 lanes of one LDS cycle -- one
+// chunk of 16 rows when the tile is written, 8 chunks of 2 rows when it is
+// read back -- reach 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int stage_off(int r, int c) {
+    return (r & 7) * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+}  // namespace rpl
+
+// One wave of the paired kernel; ROLE 0 = lead, 1 = helper.
+template <int ROLE>
+__device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm,
+                                           const bf16_t* __restrict__ Cm, const float* __restrict__ cs,
+                                           const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
+                                           const float* __restrict__ D, bf16_t* __restrict__ y, int L,
+                                           int H, int G, int nc, int b, int c, int g, int h0, int cnt,
+                                           int wave, int lane, SSD_LDS char* sm) {
+    using namespace rpl;
+    constexpr int Q = 256, P = 64, N = 128;
+    constexpr int NB = ROLE == 0 ? 5 : 4;       // blocks of this wave
+    const int p = wave & 3;
+    const int thi = 7 - p, tlo = p;
+    const int nh = ROLE == 0 ? NB : 3 - p;      // its blocks 0..nh-1 belong to tile thi
+    const int own = ROLE == 0 ? thi : tlo;      // the tile whose state term and store it makes
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int tok0 = c * Q;
+    const int rowbytes = H * P * 2;
+    // end of the chunk's last valid row, for x and y (Q rows fit 31 bits)
+    const int xrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
+    // block i: output tile bt(i), j block bs(i)
+    auto bt = [&](int i) { return i < nh ? thi : tlo; };
+    auto bs = [&](int i) { return ROLE == 0 ? i : (i < nh ? 5 + i : i - nh); };
+
+    // Copy offsets.  x copy m covers rows 8 q .. 8 q + 7 and Hin copy m rows
+    // 4 q .. 4 q + 3, q = wave + 8 m; cs (waves 0..3) or dt (4..7) a quarter
+    // row each.
+    const uint32_t xo0 = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)rowbytes +
+                         16u * (uint32_t)((lane & 7) ^ swz_x(lane >> 3));
+    const uint32_t xstep = 64u * (uint32_t)rowbytes;
+    uint32_t ho[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int r = 4 * (wave + 8 * m) + (lane >> 4);
+        ho[m] = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ swz_h(r)));
+    }
+    // copy instruction m (0..6) of head k into the slot at s: x parts 0..3,
+    // Hin parts 4 and 5, the cs or dt quarter 6.  The seven are spread over
+    // the previous head's blocks so that a wave held at issue by a full
+    // memory pipeline leaves its SIMD to the other wave.
+    auto issue_part = [&](int k, SSD_LDS char* s, int m) {
+        const int h = h0 + k;
+        if (m < 4) {
+            const __amdgpu_buffer_rsrc_t rx = make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, xrecord);
+            dma16_rs(rx, xo0 + (uint32_t)m * xstep, s + kX + (wave + 8 * m) * 1024);
+        } else if (m < 6) {
+            const __amdgpu_buffer_rsrc_t rh =
+                make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), P * N * 2);
+            dma16_rs(rh, ho[m - 4], s + kH + (wave + 8 * (m - 4)) * 1024);
+        } else {
+            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+            const int part = wave & 3;
+            dma4_rs(make_rs((wave < 4 ? cs : dtc) + row, Q * 4), 4u * (uint32_t)(64 * part + lane),
+                    s + (wave < 4 ? kCs : kDt) + 256 * part);
+        }
+    };
+    auto issue = [&](int k, SSD_LDS char* s) {
+#pragma unroll
+        for (int m = 0; m < kCopies; ++m) issue_part(k, s, m);
+    };
+    auto yrs_of = [&](int k) {
+        return __builtin_amdgcn_make_buffer_rsrc(y + (((int64_t)b * L + tok0) * H + h0 + k) * P, (short)0,
+                                                 xrecord, 0x00020000);
+    };
+
+    issue(0, sm);
+
+    // C fragments of the tile(s) of this wave's blocks and the resident G^T
+    // tiles of its blocks (the diagonal block's causal mask applied once).
+    uint4 cfo[8];   // tile own
+    uint4 cfh[8];   // tile thi (helper, prologue only)
+    auto load_cf = [&](uint4 (&cf)[8], int t) {
+        const int tok = min(tok0 + 32 * t + l32, L - 1);
+        const bf16_t* crow = Cm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) cf[kk] = *reinterpret_cast<const uint4*>(crow + 16 * kk);
+    };
+    load_cf(cfo, own);
+    if (ROLE == 1 && nh > 0) load_cf(cfh, thi);
+    f32x16 gt[NB];
+    {
+        const int jr = perm_pi(l32);
+        uint4 bq[3][8];
+        auto load_b = [&](int i, uint4 (&dst)[8]) {
+            const int tok = min(tok0 + 32 * bs(i) + jr, L - 1);
+            const bf16_t* brow = Bm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) dst[kk] = *reinterpret_cast<const uint4*>(brow + 16 * kk);
+        };
+        load_b(0, bq[0]);
+        load_b(1, bq[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (i + 2 < NB) load_b(i + 2, bq[(i + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 (&bv)[8] = bq[i % 3];
+            f32x16 a = {};
+            if (ROLE == 1 && i < nh) {
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bv[kk]), __builtin_bit_cast(bf16x8, cfh[kk]), a, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bv[kk]), __builtin_bit_cast(bf16x8, cfo[kk]), a, 0, 0, 0);
+            }
+            if (bs(i) == bt(i)) {
+                mask_causal(a, l32, hf);
+            }
+            gt[i] = a;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // The wave's tile of head k - 1 (before its column scale), stored at the
+    // top of head k: the lead of pairs 0..2 first adds the helper's partial
+    // sums; then the tile goes as bf16 rows into this wave's pieces of head
+    // k - 1's slot (the pieces its own copies of head k + 1's x rows will
+    // fill next) and out as whole token rows.
+    f32x16 keep[2];
+    float keep_colf = 1.0f;
+    auto store_kept = [&](int k) {
+        if (ROLE == 0 && p < 3) {
+            const SSD_LDS f32x4* red = (const SSD_LDS f32x4*)(sm + kRed + ((k & 1) * 3 + p) * kRedTile);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = red[(4 * mt + q) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) keep[mt][4 * q + e] += v[e];
+                }
+        }
+        SSD_LDS char* const sb = sm + (k & 1) * kSlot + kX;
+        // lane (l32, hf) holds token row l32, channels 32 mt + 16 hf + 8 q
+        // + 0..7 in keep[mt][8 q ..]: chunk 4 mt + 2 hf + q of the row
+        SSD_LDS char* const wrow = sb + (wave + 8 * (l32 >> 3)) * 1024;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                u32x4v w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16x2(keep[mt][8 * q + 2 * e] * keep_colf, keep[mt][8 * q + 2 * e + 1] * keep_colf);
+                *reinterpret_cast<SSD_LDS u32x4v*>(wrow + stage_off(l32, 4 * mt + 2 * hf + q)) = w;
+            }
+        // lane l: row 8 m + l / 8 of the tile, chunk l % 8; rows past the
+        // sequence end fall outside the record and are dropped
+        const __amdgpu_buffer_rsrc_t yrs = yrs_of(k);
+        const int tr = lane >> 3, tc = lane & 7;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 8 * m + tr;
+            const u32x4v v = *reinterpret_cast<const SSD_LDS u32x4v*>(sb + (wave + 8 * m) * 1024 + stage_off(r, tc));
+            __builtin_amdgcn_raw_buffer_store_b128(v, yrs, (32 * own + r) * rowbytes + 16 * tc, 0, 0);
+        }
+    };
+
+    const XtAddr xa = xt_addr(lane);
+    SSD_LDS float* const rfo = (SSD_LDS float*)(sm + kRf) + 160 * wave;
+    for (int k = 0; k < cnt; ++k) {
+        wait_vmcnt<0>();
+        barrier_lds();
+        // every wave is past head k - 1: its slot takes this wave's tile of
+        // head k - 1 on its way out, then head k + 1, copied during this
+        // head's blocks (the staged rows have been read back by then: the
+        // stores consume them before the first copy is issued)
+        if (k > 0) store_kept(k - 1);
+        const bool next = k + 1 < cnt;
+        SSD_LDS char* const snext = sm + ((k + 1) & 1) * kSlot;
+
+        const SSD_LDS char* S = sm + (k & 1) * kSlot;
+        const SSD_LDS float* css = (const SSD_LDS float*)(S + kCs);
+        const SSD_LDS float* dts = (const SSD_LDS float*)(S + kDt);
+        const float Dh = D ? D[h0 + k] : 0.0f;
+        auto tile_f = [&](int t, float& csi) {
+            const float cref = css[32 * t], ctail = css[32 * t + 31];
+            csi = css[32 * t + l32];
+            TileF f;
+            f.fact = uniform_f(cref - ctail) <= kMaxTileDecayLog2;
+            if (f.fact) {
+                f.colf = fast_exp2(csi - cref);
+                f.sstate = fast_exp2(cref);
+                f.dprime = Dh * fast_exp2(cref - csi);
+            } else {
+                f.colf = 1.0f;
+                f.sstate = fast_exp2(csi);
+                f.dprime = 0.0f;
+            }
+            return f;
+        };
+        float csi_h = 0.0f, csi_l = 0.0f;
+        const TileF tfh = tile_f(thi, csi_h);
+        TileF tfl = tfh;
+        if (ROLE == 1) tfl = tile_f(tlo, csi_l);
+        // rf rows of the wave's blocks: rfo[32 i + j] = exp2(cref - cs_j) dt_j
+        // for token j of block i against its tile's first token
+#pragma unroll
+        for (int q = 0; q < (32 * NB + 63) / 64; ++q) {
+            const int e = lane + 64 * q;
+            if (e < 32 * NB) {
+                const int i = e >> 5, j = e & 31;
+                const int jj = 32 * bs(i) + j;
+                rfo[e] = fast_exp2(fminf(css[32 * bt(i)] - css[jj], kMaxTileDecayLog2)) * dts[jj];
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (ROLE == 1 && i == nh && nh > 0) {
+                // the helper's blocks of tile thi are done: hand them over
+                SSD_LDS f32x4* red = (SSD_LDS f32x4*)(sm + kRed + ((k & 1) * 3 + p) * kRedTile);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        red[(4 * mt + q) * 64 + lane] =
+                            f32x4{acc[mt][4 * q], acc[mt][4 * q + 1], acc[mt][4 * q + 2], acc[mt][4 * q + 3]};
+                    }
+                acc[0] = f32x16{};
+                acc[1] = f32x16{};
+            }
+            if (next) issue_part(k + 1, snext, i);
+            const bool hi = i < nh;
+            const int s = bs(i);
+            SlotRf rf;
+            rs_fetch_rf(rf, rfo + 32 * i, hf);
+            SlotX xs;
+            rs_fetch_x(xs, S + kX + s * 4096, xa);
+            const bool dg = s == bt(i);
+            u32x4v gq[2];
+            if (hi ? tfh.fact : tfl.fact)
+                rs_weights_fact(gq, gt[i], rf, dg, hi ? tfh.dprime : tfl.dprime);
+            else
+                rs_weights_direct(gq, gt[i], css + 32 * s, dts + 32 * s, hi ? csi_h : csi_l, Dh, dg, hf);
+            rs_products(acc, xs, gq);
+        }
+        if (next) {
+#pragma unroll
+            for (int m = NB; m < kCopies; ++m) issue_part(k + 1, snext, m);
+        }
+
+        // (ii) for tile own: accS = Hin C_own^T, added as sstate * accS
+        {
+            const SSD_LDS uint4* hs = (const SSD_LDS uint4*)(S + kH);
+            f32x16 accS[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                u32x4v ha[4][2];
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const int pr = 32 * mt + perm_sigma(l32);
+                        const int ch = 2 * (4 * kh + kq) + hf;
+                        ha[kq][mt] = *reinterpret_cast<const SSD_LDS u32x4v*>(hs + pr * 16 + (ch ^ swz_h(pr)));
+                    }
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        accS[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ha[kq][mt]), __builtin_bit_cast(bf16x8, cfo[4 * kh + kq]), accS[mt], 0, 0, 0);
+            }
+            const TileF& tfo = ROLE == 0 ? tfh : tfl;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mt][r] = fmaf(tfo.sstate, accS[mt][r], acc[mt][r]);
+            keep[0] = acc[0];
+            keep[1] = acc[1];
+            keep_colf = tfo.colf;
+        }
+    }
+    // the last head's tiles (and the helpers' last partial sums)
+    barrier_lds();
+    store_kept(cnt - 1);
+    wait_vmcnt<0>();
 }
 
-__global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
+__global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
     const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg,
     int nsplit) {
-    constexpr int Q = 256, P = 64, N = 128;
-    __shared__ __align__(16) char slots[3 * rsl::kSlot];
-    __shared__ __align__(16) float rfw[4][288];
-
+    __shared__ __align__(16) char smem[rpl::kBytes];
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = (int)(wg % (uint32_t)nsplit);
     const uint32_t bcg = wg / (uint32_t)nsplit;
@@ -769,227 +1034,14 @@ __global__ __launch_bounds__(256, 1) void chunk_scan_resident_kernel(
     const int hpg = H / G;
     const int h0 = g * hpg + split * hg;
     const int cnt = min(hg, hpg - split * hg);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(wave >= 0 && wave < 4);
-    const int hf = lane >> 5, l32 = lane & 31;
-    const int tok0 = c * Q;
-    const int rowbytes = H * P * 2;
-    // end of the chunk's last valid row, for x and y (within the chunk: Q
-    // rows of a token row's bytes fit 31 bits)
-    const int xrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
-    const int t0 = wave, t1 = 7 - wave;
-    SSD_LDS char* const sl0 = (SSD_LDS char*)lds(slots);
-
-    // Per-lane copy offsets.  x copy i covers rows 32 i + 8 w .. + 7; Hin
-    // copy i rows 16 i + 4 w .. + 3.
-    const uint32_t xo0 = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)rowbytes +
-                         16u * (uint32_t)((lane & 7) ^ swz_x(lane >> 3));
-    const uint32_t xstep = 32u * (uint32_t)rowbytes;
-    uint32_t ho[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * i + 4 * wave + (lane >> 4);
-        ho[i] = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ swz_h(r)));
-    }
-    // Copies of head k into the slot at byte offset so, in four parts (x
-    // rows 0..127, x rows 128..255, Hin, cs/dt); past the run's last head
-    // they read empty records (zeros, no memory traffic), which keeps every
-    // wait count fixed.  (Non-temporal x copies were 1% faster alone and made
-    // the whole forward 1-2% slower.)
-    auto issue_part = [&](int k, uint32_t so, int part) {
-        const bool real = k < cnt;
-        const int h = h0 + (real ? k : 0);
-        SSD_LDS char* s = sl0 + so;
-        if (part < 2) {
-            const __amdgpu_buffer_rsrc_t rx =
-                make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, real ? xrecord : 0);
-#pragma unroll
-            for (int i = 4 * part; i < 4 * part + 4; ++i)
-                dma16_rs(rx, xo0 + (uint32_t)i * xstep, s + rsl::kX + (4 * i + wave) * 1024);
-        } else if (part == 2) {
-            const __amdgpu_buffer_rsrc_t rh =
-                make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), real ? P * N * 2 : 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dma16_rs(rh, ho[i], s + rsl::kH + (4 * i + wave) * 1024);
-        } else {
-            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-            dma4_rs(make_rs(cs + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kCs + 256 * wave);
-            dma4_rs(make_rs(dtc + row, real ? Q * 4 : 0), 4u * (uint32_t)tid, s + rsl::kDt + 256 * wave);
-        }
-    };
-    auto issue_head = [&](int k, uint32_t so) {
-#pragma unroll
-        for (int part = 0; part < 4; ++part) issue_part(k, so, part);
-    };
-
-    issue_head(0, 0);
-    issue_head(1, rsl::kSlot);
-
-    // C fragments of the wave's tiles (cf[0]: t0, cf[1]: t1) and the
-    // resident G^T tiles.
-    const int it_[2] = {t0, t1};
-    uint4 cf[2][8];
-    load_c_frags(cf, Cm, b, L, G, g, tok0, it_, hf, l32);
-    f32x16 gt[9];
-    {
-        // B rows of slot s's block in registers, two slots ahead of the
-        // products (the scheduler would otherwise pull each load down to its
-        // use and wait out the latency slot by slot)
-        const int jr = perm_pi(l32);
-        uint4 bq[3][8];
-        auto load_b = [&](int s, uint4 (&dst)[8]) {
-            const int jt = s < 8 - wave ? s : s - (8 - wave);
-            const int tok = min(tok0 + 32 * jt + jr, L - 1);
-            const bf16_t* brow = Bm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) dst[kk] = *reinterpret_cast<const uint4*>(brow + 16 * kk);
-        };
-        load_b(0, bq[0]);
-        load_b(1, bq[1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < 9; ++s) {
-            if (s + 2 < 9) load_b(s + 2, bq[(s + 2) % 3]);
-            __builtin_amdgcn_sched_barrier(0);
-            const uint4 (&bs)[8] = bq[s % 3];
-            f32x16 a = {};
-            if (s < 8 - wave) {
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bs[kk]), __builtin_bit_cast(bf16x8, cf[1][kk]), a, 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bs[kk]), __builtin_bit_cast(bf16x8, cf[0][kk]), a, 0, 0, 0);
-            }
-            if (s == 8 || s == 7 - wave) {
-                // a diagonal block: its causal mask j <= i does not depend
-                // on the head, so it is applied here once
-#pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] = lane_select(0.0f, a[r], diag_keep_lanes(r));
-            }
-            gt[s] = a;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    uint32_t so = 0;   // slot of head k
-    for (int k = 0; k < cnt; ++k) {
-        // head k's copies have landed once only those issued after them are
-        // outstanding: (k >= 2) y stores of k - 2, copies of k + 1, y
-        // stores of k - 1
-        if (k == 0) wait_vmcnt<0>();
-        else if (k == 1) wait_vmcnt<rsl::kCopies + rsl::kStores>();
-        else wait_vmcnt<rsl::kCopies + 2 * rsl::kStores>();
-        barrier_lds();
-        // every wave is past head k - 1: its slot takes head k + 2, copied in
-        // parts during slots 0..3 (all before this head's first y stores:
-        // the wait counts above hold)
-        const uint32_t so2 = so >= (uint32_t)rsl::kSlot ? so - rsl::kSlot : so + 2 * rsl::kSlot;
-
-        const int h = h0 + k;
-        const SSD_LDS char* S = sl0 + so;
-        const SSD_LDS float* css = (const SSD_LDS float*)(S + rsl::kCs);
-        const SSD_LDS float* dts = (const SSD_LDS float*)(S + rsl::kDt);
-        const float Dh = D ? D[h] : 0.0f;
-        int lane_o = lane;
-        asm volatile("" : "+v"(lane_o));
-        const int hf_o = lane_o >> 5, l32_o = lane_o & 31;
-        const XtAddr xa = xt_addr(lane_o);
-        u32x4v ha[8][2];
-        rs_hin_read(ha, (const SSD_LDS uint4*)(S + rsl::kH), hf_o, l32_o);
-
-        // the head's cs/dt reads all at once: the tile factors' (tf[0]: t0,
-        // tf[1]: t1) and those of the rf rows of the wave's 9 slots,
-        // rfw[s][j] = exp2(cref_t - cs_j) dt_j (row entries e = lane + 64 q)
-        float cref[2], ctail[2], csi[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int i0 = 32 * it_[q];
-            cref[q] = css[i0];
-            ctail[q] = css[i0 + 31];
-            csi[q] = css[i0 + l32_o];
-        }
-        float rft[5], rfc[5], rfd[5];
-#pragma unroll
-        for (int q = 0; q < 5; ++q) {
-            const int e = min(lane_o + 64 * q, 287);
-            const int s = e >> 5, j = e & 31;
-            const bool first = s < 8 - wave;
-            const int t = first ? t1 : t0;
-            const int jt = first ? s : s - (8 - wave);
-            rft[q] = css[32 * t];
-            rfc[q] = css[32 * jt + j];
-            rfd[q] = dts[32 * jt + j];
-        }
-        TileF tf[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            tf[q].fact = uniform_f(cref[q] - ctail[q]) <= kMaxTileDecayLog2;
-            if (tf[q].fact) {
-                tf[q].colf = fast_exp2(csi[q] - cref[q]);
-                tf[q].sstate = fast_exp2(cref[q]);
-                tf[q].dprime = Dh * fast_exp2(cref[q] - csi[q]);
-            } else {
-                tf[q].colf = 1.0f;
-                tf[q].sstate = fast_exp2(csi[q]);
-                tf[q].dprime = 0.0f;
-            }
-        }
-        SSD_LDS float* rfo = lds(&rfw[wave][0]);
-#pragma unroll
-        for (int q = 0; q < 5; ++q) {
-            const int e = lane_o + 64 * q;
-            if (q < 4 || e < 288) rfo[e] = fast_exp2(fminf(rft[q] - rfc[q], kMaxTileDecayLog2)) * rfd[q];
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
-            y + (((int64_t)b * L + tok0) * H + h) * P, (short)0, xrecord, 0x00020000);
-        f32x16 acc[2][2];
-        rs_state_terms(acc, ha, cf, tf);
-        // slot s's LDS operands are read while slot s - 1 computes
-        auto slot_jt = [&](int s) { return s < 8 - wave ? s : s - (8 - wave); };
-        SlotRf rc, rn;
-        SlotX xc, xn;
-        rs_fetch_rf(rc, rfo, hf_o);
-        rs_fetch_x(xc, S + rsl::kX + slot_jt(0) * 4096, xa);
-#pragma unroll
-        for (int s = 0; s < 9; ++s) {
-            if (s + 1 < 9) {
-                rs_fetch_rf(rn, rfo + 32 * (s + 1), hf_o);
-                rs_fetch_x(xn, S + rsl::kX + slot_jt(s + 1) * 4096, xa);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const int jt = slot_jt(s);
-            const bool first = s < 8 - wave;
-            const bool dgb = first ? (s == 7 - wave) : (s == 8);
-            u32x4v gq[2];
-            rs_weights_fact(gq, gt[s], rc, dgb, first ? tf[1].dprime : tf[0].dprime);
-            if (!(first ? tf[1].fact : tf[0].fact))
-                rs_weights_direct(gq, gt[s], css + 32 * jt, dts + 32 * jt, first ? csi[1] : csi[0], Dh,
-                                  dgb, hf_o, l32_o);
-            if (first) {
-                rs_products(acc[1], xc, gq);
-                if (s == 7 - wave) rs_store(acc[1], tf[1].colf, yrs, rowbytes, t1, hf_o, l32_o);
-            } else {
-                rs_products(acc[0], xc, gq);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (s < 4) {
-                issue_part(k + 2, so2, s);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            rc = rn;
-            xc = xn;
-        }
-        rs_store(acc[0], tf[0].colf, yrs, rowbytes, t0, hf_o, l32_o);
-        so = so + rsl::kSlot == 3 * rsl::kSlot ? 0 : so + rsl::kSlot;
-    }
-    // the copies of the two heads past the end read empty records; nothing
-    // in flight may outlive the workgroup's LDS
-    wait_vmcnt<0>();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    __builtin_assume(wave >= 0 && wave < 8);
+    SSD_LDS char* const sm = (SSD_LDS char*)lds(smem);
+    if (wave < 4)
+        paired_run<0>(x, Bm, Cm, cs, dtc, Hin, D, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
+    else
+        paired_run<1>(x, Bm, Cm, cs, dtc, Hin, D, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1182,14 +1234,14 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         bf16_t* yb = static_cast<bf16_t*>(y);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
         if (d.chunk == 256) {
-            // the resident kernel pays for its start-up (9 tiles' products
-            // and a pipeline fill) once per run of heads: worth it for long
-            // runs only
+            // the resident kernel pays for its start-up (each wave's 5 or 4
+            // G^T tiles and the first head's copies) once per run of heads:
+            // worth it for long runs only
             int hg = 0, nsplit = 0;
             scan_resident_split(d, &hg, &nsplit);
             if (hg >= kResidentMinHeads) {
                 const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
-                chunk_scan_resident_kernel<<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg, nsplit);
+                chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg, nsplit);
                 return hipGetLastError();
             }
         }

@@ -1,6 +1,7 @@
 // ssd_api.cpp -- the C ABI declared in include/ssd_mi355x.h: argument
-// validation, workspace carving and the launch order.  No allocation, no
-// synchronisation, no global mutable state.
+// validation, workspace carving and the launch order.  No allocation and no
+// synchronisation; the only global state is ssd_forward_noalloc's per-device
+// array and the cache of its device addresses.
 #include "ssd_mi355x.h"
 
 #include <hip/hip_runtime.h>
@@ -52,7 +53,7 @@ int32_t check_dims(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
     d->dstate = dstate;
     d->ngroups = ngroups;
     d->chunk = chunk;
-    d->nchunks = (seqlen + chunk - 1) / chunk;
+    d->nchunks = (seqlen - 1) / chunk + 1;   // seqlen >= 1: no overflow for any chunk
     // grid sizes (one workgroup per batch * chunk * head) must fit 32 bits
     if ((double)batch * (double)d->nchunks * (double)nheads > 2147483647.0) return SSD_ERR_SHAPE;
     return SSD_OK;
