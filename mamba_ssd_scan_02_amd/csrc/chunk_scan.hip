@@ -727,13 +727,19 @@ constexpr bool waits_hold(int heads) {
 static_assert(waits_hold(1) && waits_hold(2) && waits_hold(40), "paired chunk_scan waits");
 
 // Byte offset of 16-byte chunk c of token row r (0..31) of a staged y tile
-// within its 1 KB piece (rows 8 m .. 8 m + 7 in piece m): the chunk index
-// is XORed with (r / 2) % 8 so that the 16 lanes of one LDS cycle -- one
-// chunk of 16 rows when the tile is written, 8 chunks of 2 rows when it is
-// read back -- reach 16 distinct 16-byte bank groups.
+// within its 1 KB piece (rows 8 m .. 8 m + 7 in piece m).  The chunk index
+// is XORed with f(r) = ((r / 2) % 8) ^ ((r / 16) % 2): the lanes that share
+// an LDS cycle then reach distinct 16-byte bank groups whether the LDS
+// serves 16 or 32 lanes of a 16-byte access per cycle -- one chunk of 16 or
+// 32 rows when the tile is written (f is one-to-one on the rows of equal
+// r % 2 among 16 and of equal r % 4 among 32), 8 chunks of 2 or 4 rows
+// when it is read back.
 __device__ __forceinline__ int stage_off(int r, int c) {
-    return (r & 7) * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    return (r & 7) * 128 + ((c ^ ((r >> 1) & 7) ^ ((r >> 4) & 1)) << 4);
 }
+// Order in which a wave issues its 7 copy instructions of the next head,
+// two per block from the first block on: cs or dt (needed first), x, Hin.
+constexpr int kIssueOrder[kCopies] = {6, 0, 1, 2, 3, 4, 5};
 }  // namespace rpl
 
 // One wave of the paired kernel; ROLE 0 = lead, 1 = helper.
@@ -774,8 +780,9 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
     }
     // copy instruction m (0..6) of head k into the slot at s: x parts 0..3,
     // Hin parts 4 and 5, the cs or dt quarter 6.  The seven are spread over
-    // the previous head's blocks so that a wave held at issue by a full
-    // memory pipeline leaves its SIMD to the other wave.
+    // the first four blocks of the previous head (kIssueOrder), so that a
+    // wave held at issue by a full memory pipeline leaves its SIMD to the
+    // other wave and the last copy still has most of a head to land.
     auto issue_part = [&](int k, SSD_LDS char* s, int m) {
         const int h = h0 + k;
         if (m < 4) {
@@ -903,8 +910,8 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
         barrier_lds();
         // every wave is past head k - 1: its slot takes this wave's tile of
         // head k - 1 on its way out, then head k + 1, copied during this
-        // head's blocks (the staged rows have been read back by then: the
-        // stores consume them before the first copy is issued)
+        // head's first four blocks (the staged rows have been read back by
+        // then: the stores consume them before the first copy is issued)
         if (k > 0) store_kept(k - 1);
         const bool next = k + 1 < cnt;
         SSD_LDS char* const snext = sm + ((k + 1) & 1) * kSlot;
@@ -962,7 +969,10 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
                 acc[0] = f32x16{};
                 acc[1] = f32x16{};
             }
-            if (next) issue_part(k + 1, snext, i);
+            if (next && i < 4) {
+                issue_part(k + 1, snext, kIssueOrder[2 * i]);
+                if (2 * i + 1 < kCopies) issue_part(k + 1, snext, kIssueOrder[2 * i + 1]);
+            }
             const bool hi = i < nh;
             const int s = bs(i);
             SlotRf rf;
@@ -976,10 +986,6 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
             else
                 rs_weights_direct(gq, gt[i], css + 32 * s, dts + 32 * s, hi ? csi_h : csi_l, Dh, dg, hf);
             rs_products(acc, xs, gq);
-        }
-        if (next) {
-#pragma unroll
-            for (int m = NB; m < kCopies; ++m) issue_part(k + 1, snext, m);
         }
 
         // (ii) for tile own: accS = Hin C_own^T, added as sstate * accS
