@@ -48,6 +48,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 KERNEL_SOURCES = {
     "chunk_cumsum": "chunk_cumsum.hip",
     "chunk_state": "chunk_state.hip",
+    "chunk_state_cumsum": "chunk_state.hip",
     "state_passing": "state_passing.hip",
     "chunk_scan": "chunk_scan.hip",
     "state_scan": "state_scan.hip",
@@ -81,6 +82,7 @@ def forward_model(b, L, H, P, N, G, Q):
     bytes_ = {
         "chunk_cumsum": dt + 2 * rows,
         "chunk_state": x + bc + 2 * rows + S,
+        "chunk_state_cumsum": x + bc + dt + 2 * rows + S,
         "state_passing": S + b * H * nc * 4 + st + Hin + st,
         "chunk_scan": x + 2 * bc + 2 * rows + Hin + x,
         "state_scan": x + bc + 2 * rows + st + Hin + st,
@@ -89,6 +91,7 @@ def forward_model(b, L, H, P, N, G, Q):
     flops = {
         "chunk_cumsum": 2 * th,
         "chunk_state": 2 * P * N * th,                               # sum_j w_j x_j B_j^T
+        "chunk_state_cumsum": 2 * P * N * th + 2 * th,
         "state_passing": 2 * b * H * nc * P * N,
         "chunk_scan": ((Q + 1) * P + 2 * N * P) * th + (Q + 1) * N * tok * G,  # causal-exact
         "state_scan": 2 * P * N * th + 2 * b * H * nc * P * N,
@@ -194,20 +197,24 @@ def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup, zoh=False):
 
 def forward_kernels(dims):
     """The kernels ssd_forward runs at these sizes, by the names of the stage
-    calls that launch the same kernels: chunk state (with the cumsum inside
-    where a group's head count is even), state passing and chunk_scan."""
+    calls that launch the same kernels: chunk state with the cumsum inside
+    (ssd_chunk_cumsum_state, one launch where a group's head count is even),
+    state passing and chunk_scan."""
     b, L, H, P, N, G, Q = dims
     fused = P == 64 and N == 128 and Q in (128, 256) and (H // G) % 2 == 0
-    return (["chunk_state"] if fused else ["chunk_cumsum", "chunk_state"]) + \
+    return (["chunk_state_cumsum"] if fused else ["chunk_cumsum", "chunk_state"]) + \
         ["state_passing", "chunk_scan"]
 
 
 def time_stages(ssd, g, y, fin, dims, steps):
     """Average duration of each kernel, from HIP events recorded on the
-    stream the stage calls are launched on (torch's current stream): the
-    forward's own kernels (through the stage calls that launch them) and the
-    two-kernel state path beside them.  Buffers of their own, not the
-    forward's workspace."""
+    stream the stage calls are launched on (torch's current stream): first
+    the forward's own kernels in the forward's order (chunk state with the
+    cumsum inside, state passing, chunk scan -- each launched by the stage
+    call that runs the same kernel, so each one follows what it follows in
+    the forward), then the stand-alone cumsum and chunk state and the
+    one-pass state stage.  Buffers of their own, not the forward's
+    workspace."""
     import ctypes
     import torch
     lib = ssd.load()
@@ -221,17 +228,19 @@ def time_stages(ssd, g, y, fin, dims, steps):
     cs, dtc, S, Hin = (ctypes.c_void_p(t.data_ptr()) for t in (cs_t, dtc_t, S_t, Hin_t))
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     p = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
-    names = ["chunk_cumsum", "chunk_state", "state_passing", "state_scan"]
+    names = ["chunk_state_cumsum", "state_passing", "chunk_scan", "chunk_cumsum", "chunk_state",
+             "state_scan"]
     calls = [
+        lambda: lib.ssd_chunk_cumsum_state(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["dt"]),
+                                           p(g["A"]), cs, dtc, S, stream),
+        lambda: lib.ssd_state_passing(b, L, H, P, N, Q, 1, S, cs, p(g["init"]), Hin, p(fin), stream),
+        lambda: lib.ssd_chunk_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["C"]),
+                                   cs, dtc, Hin, p(g["D"]), p(y), stream),
         lambda: lib.ssd_chunk_cumsum(b, L, H, Q, p(g["dt"]), p(g["A"]), cs, dtc, stream),
         lambda: lib.ssd_chunk_state(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), cs, dtc, S, stream),
-        lambda: lib.ssd_state_passing(b, L, H, P, N, Q, 1, S, cs, p(g["init"]), Hin, p(fin), stream),
         lambda: lib.ssd_state_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), cs, dtc,
                                    p(g["init"]), Hin, p(fin), stream),
     ]
-    names.append("chunk_scan")
-    calls.append(lambda: lib.ssd_chunk_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["C"]),
-                                            cs, dtc, Hin, p(g["D"]), p(y), stream))
     for f in calls:            # warm
         assert f() == 0
     torch.cuda.synchronize()
@@ -479,7 +488,9 @@ def profile_loop(k: int):
 
 def _short_kernel(name: str) -> str:
     if "chunk_state" in name and ", true>" in name:
-        return "chunk_state+cumsum"   # chunk state with the cumsum inside
+        return "chunk_state_cumsum"   # chunk state with the cumsum inside
+    if "state_walk" in name:
+        return "state_scan"           # what ssd_state_scan launches for chunk 128 / 256
     for k in KERNEL_SOURCES:
         if k in name:
             return k
@@ -526,10 +537,16 @@ def summarize_trace(d: str, out: str, cmd: str):
     print("\n".join(lines))
 
 
-def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str, cmd_write: str):
+def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str, cmd_write: str,
+                       xcheck=None, cmd_rd: str = "", cmd_wr: str = ""):
     """Per-kernel HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE (KiB
     per dispatch), each scaled by the ratio known bytes / counter value of the
-    calibration copy (COPY_BYTES read and written)."""
+    calibration copy (COPY_BYTES read and written).  With ``xcheck`` = (dir of
+    a TCC_EA0_RDREQ{,_32B,_64B,_128B} pass, dir of a TCC_EA0_WRREQ{,_64B}
+    pass), the same bytes are also counted request by request at their
+    sizes, which needs no calibration: FETCH_SIZE counts each read request
+    that is not 32 bytes as 64 bytes, while the reads here are 128-byte
+    requests -- the copy's factor of 2."""
     import csv
     import glob
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B, DECODE_B256
@@ -555,6 +572,17 @@ def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str,
 
     fetch = load(d_fetch, "FETCH_SIZE")
     write = load(d_write, "WRITE_SIZE")
+    xr = xw = None
+    if xcheck:
+        rq = {c: load(xcheck[0], c) for c in ("TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B",
+                                               "TCC_EA0_RDREQ_128B")}
+        wq = {c: load(xcheck[1], c) for c in ("TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")}
+        avg = lambda v: sum(v) / len(v)
+        xr = {k: 32 * avg(rq["TCC_EA0_RDREQ_32B"][k]) + 64 * avg(rq["TCC_EA0_RDREQ_64B"][k]) +
+              128 * avg(rq["TCC_EA0_RDREQ_128B"][k]) for k in rq["TCC_EA0_RDREQ_128B"]}
+        xw = {k: 64 * avg(wq["TCC_EA0_WRREQ_64B"][k]) +
+              32 * (avg(wq["TCC_EA0_WRREQ"][k]) - avg(wq["TCC_EA0_WRREQ_64B"][k]))
+              for k in wq["TCC_EA0_WRREQ"]}
     if "copy" not in fetch or "copy" not in write:
         raise SystemExit("calibration copy missing from the counters")
     cf = COPY_BYTES / (sum(fetch["copy"]) / len(fetch["copy"]) * 1024)
@@ -586,6 +614,17 @@ def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str,
             f"hbm_bytes_per_dispatch: {fk + wk:.6g}",
             f"algorithmic_bytes_per_dispatch: {alg[k]}",
             f"traffic_over_algorithmic: {(fk + wk) / alg[k]:.4f}",
+        ] + ([
+            f"command_read_requests: {cmd_rd}",
+            f"command_write_requests: {cmd_wr}",
+            "read_bytes_by_request_size: 32 x TCC_EA0_RDREQ_32B + 64 x TCC_EA0_RDREQ_64B + "
+            "128 x TCC_EA0_RDREQ_128B (no calibration)",
+            f"xcheck_copy_read_bytes: {xr['copy']:.6g} (copy reads {COPY_BYTES})",
+            f"xcheck_read_bytes_per_dispatch: {xr[k]:.6g}",
+            "write_bytes_by_request_size: 64 x TCC_EA0_WRREQ_64B + 32 x the rest",
+            f"xcheck_copy_write_bytes: {xw['copy']:.6g} (copy writes {COPY_BYTES})",
+            f"xcheck_write_bytes_per_dispatch: {xw[k]:.6g}",
+        ] if xr is not None and k in xr and k in xw and "copy" in xr and "copy" in xw else []) + [
             f"source_sha256_16: {source_hash(k)}",
         ]) + "\n"
         outp = Path(out_dir) / f"{k}_{wl}_counters.txt"
@@ -611,7 +650,7 @@ def summarize_sq(d: str, out_dir: str, cmd: str):
     acc = {}
     for r in csv.DictReader(open(f[0])):
         k = _short_kernel(r["Kernel_Name"])
-        if k not in KERNEL_SOURCES and k != "chunk_state+cumsum":
+        if k not in KERNEL_SOURCES:
             continue
         acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     for k, cnt in acc.items():
@@ -629,8 +668,7 @@ def summarize_sq(d: str, out_dir: str, cmd: str):
                          ("SQ_ACTIVE_INST_VMEM", "issuing VMEM")):
             if c in avg:
                 lines.append(f"share_of_wave_cycles_{label.replace(' ', '_')}: {avg[c] / wc:.4f}")
-        name = "chunk_state_cumsum" if k == "chunk_state+cumsum" else k
-        Path(out_dir, f"{name}_{wl}_issue.txt").write_text("\n".join(lines) + "\n")
+        Path(out_dir, f"{k}_{wl}_issue.txt").write_text("\n".join(lines) + "\n")
         print("\n".join(lines))
 
 
@@ -663,6 +701,11 @@ def main():
     ap.add_argument("--out-dir", default="profiles")
     ap.add_argument("--cmd", default="", help="command recorded in a summary")
     ap.add_argument("--cmd2", default="", help="second command recorded in a summary")
+    ap.add_argument("--xcheck", nargs=2, default=None,
+                    help="with --summarize-counters: dirs of the TCC_EA0_RDREQ* and TCC_EA0_WRREQ* "
+                         "passes (bytes counted per request size)")
+    ap.add_argument("--cmd3", default="", help="read-request command recorded in a summary")
+    ap.add_argument("--cmd4", default="", help="write-request command recorded in a summary")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.cmd)
@@ -672,7 +715,7 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.out_dir,
-                           args.cmd, args.cmd2)
+                           args.cmd, args.cmd2, args.xcheck, args.cmd3, args.cmd4)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

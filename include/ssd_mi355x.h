@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 
@@ -236,6 +236,16 @@ int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
                         int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                         const void* x, const void* B, const float* cs, const float* dtc,
                         void* S, hipStream_t stream);
+
+/* cs, dtc and S from dt, A, x and B: ssd_chunk_cumsum followed by
+ * ssd_chunk_state, as ssd_forward runs them -- one launch where the bf16
+ * matrix-core chunk-state kernel takes two heads per workgroup (the cumsum
+ * then runs in its prologue and writes the same cs and dtc), two launches
+ * otherwise.  Same layouts and checks as the two calls. */
+int32_t ssd_chunk_cumsum_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                               const void* x, const void* B, const float* dt, const float* A,
+                               float* cs, float* dtc, void* S, hipStream_t stream);
 
 /* Hin and final_state from S (both in the storage type of `dtype`): the
  * linear recurrence between chunks in fp32, H_0 = init (or 0), Hin_c = H_c,

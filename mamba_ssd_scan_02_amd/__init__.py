@@ -12,6 +12,7 @@ from .ssd import (  # noqa: F401
     SSDError,
     abi_version,
     chunk_cumsum,
+    chunk_cumsum_state,
     chunk_scan,
     chunk_state,
     layer_in,
@@ -32,7 +33,7 @@ from .ssd import (  # noqa: F401
 
 __all__ = [
     "ssd_forward", "ssm_step", "workspace_bytes", "workspace_regions", "chunk_cumsum",
-    "chunk_state", "state_passing", "state_scan", "chunk_scan", "load", "library_path", "abi_version",
+    "chunk_cumsum_state", "chunk_state", "state_passing", "state_scan", "chunk_scan", "load", "library_path", "abi_version",
     "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16", "ABI_VERSION", "layer_in",
     "layer_out", "ssd_layer", "state_passing_seg",
 ]

@@ -201,6 +201,25 @@ int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
     return hip_status(ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream));
 }
 
+int32_t ssd_chunk_cumsum_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                               const void* x, const void* B, const float* dt, const float* A,
+                               float* cs, float* dtc, void* S, hipStream_t stream) {
+    Dims d;
+    int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
+    if (st != SSD_OK) return st;
+    if ((st = check_supported(dtype, d)) != SSD_OK) return st;
+    if (!x || !B || !dt || !A || !cs || !dtc || !S) return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(S, 16) || !aligned(dt, 4) || !aligned(A, 4) ||
+        !aligned(cs, 4) || !aligned(dtc, 4))
+        return SSD_ERR_ALIGN;
+    if (ssd::chunk_state_fuses_cumsum(dtype, d))
+        return hip_status(ssd::launch_chunk_state_fused(d, x, B, dt, A, 0, cs, dtc, S, stream));
+    hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, 0);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    return hip_status(ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream));
+}
+
 int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                           int64_t dstate, int64_t chunk, int32_t dtype, const void* S,
                           const float* cs, const float* init_state, void* Hin,

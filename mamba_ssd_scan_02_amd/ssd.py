@@ -21,7 +21,7 @@ DTYPE_BF16 = 1
 
 # The SSD_ABI_VERSION this binding was written against; load() refuses a
 # library that reports another one (a stale build).
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _STATUS_OK = 0
 
@@ -73,6 +73,8 @@ def load():
     lib.ssd_chunk_cumsum_zoh.argtypes = lib.ssd_chunk_cumsum.argtypes
     lib.ssd_chunk_state.restype = i32
     lib.ssd_chunk_state.argtypes = [i64] * 7 + [i32] + [vp] * 5 + [vp]
+    lib.ssd_chunk_cumsum_state.restype = i32
+    lib.ssd_chunk_cumsum_state.argtypes = [i64] * 7 + [i32] + [vp] * 7 + [vp]
     lib.ssd_state_passing.restype = i32
     lib.ssd_state_passing.argtypes = [i64] * 6 + [i32] + [vp] * 5 + [vp]
     lib.ssd_state_scan.restype = i32
@@ -273,6 +275,25 @@ def chunk_state(x, B, cs, dtc, chunk):
                                                   _p(x), _p(B), _p(cs), _p(dtc), _p(S),
                                                   _stream(x.device)))
     return S
+
+
+def chunk_cumsum_state(x, B, dt, A, chunk):
+    """(cs, dtc, S) -- see ssd_chunk_cumsum_state (the forward's first launch)."""
+    lib = load()
+    x = _dev(x, "x")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = n_chunks(L, chunk)
+    _dev(B, "B", x.dtype, (batch, L, G, N), x.device)
+    _dev(dt, "dt", torch.float32, (batch, L, H), x.device)
+    _dev(A, "A", torch.float32, (H,), x.device)
+    cs = torch.empty((batch, H, nc, chunk), dtype=torch.float32, device=x.device)
+    dtc = torch.empty_like(cs)
+    S = torch.empty((batch, H, nc, P, N), dtype=x.dtype, device=x.device)
+    _check("ssd_chunk_cumsum_state",
+           lib.ssd_chunk_cumsum_state(batch, L, H, P, N, G, chunk, _dtype_code(x), _p(x), _p(B),
+                                      _p(dt), _p(A), _p(cs), _p(dtc), _p(S), _stream(x.device)))
+    return cs, dtc, S
 
 
 def state_passing(S, cs, seqlen, chunk, dtype, init_state=None, final_state=None):

@@ -107,6 +107,8 @@ static void library_checks(void) {
     CHECK(ssd_chunk_cumsum_zoh(b, L, H, Q, dt, A, NULL, (float*)y, NULL) == SSD_ERR_NULL);
     CHECK(ssd_chunk_state(b, L, H, P, N, G, Q, f32, NULL, B, dt, A, ws, NULL) == SSD_ERR_NULL);
     CHECK(ssd_chunk_state(b, L, H, P, N, G, Q, 9, x, B, dt, A, ws, NULL) == SSD_ERR_UNSUPPORTED);
+    CHECK(ssd_chunk_cumsum_state(b, L, H, P, N, G, Q, f32, x, B, NULL, A, (float*)ws, (float*)y, C, NULL) == SSD_ERR_NULL);
+    CHECK(ssd_chunk_cumsum_state(b, L, 3, P, N, 2, Q, f32, x, B, dt, A, (float*)ws, (float*)y, C, NULL) == SSD_ERR_SHAPE);
     CHECK(ssd_state_passing(b, L, H, P, N, Q, f32, NULL, dt, init, y, fin, NULL) == SSD_ERR_NULL);
     CHECK(ssd_state_passing(b, 0, H, P, N, Q, f32, ws, dt, init, y, fin, NULL) == SSD_ERR_SHAPE);
     CHECK(ssd_state_passing_seg(b, L, H, P, N, Q, 2, f32, ws, dt, init, y, fin, NULL, 0, NULL) == SSD_ERR_WORKSPACE);

@@ -60,6 +60,12 @@ def test_stages(case):
     S_mag = stages.chunk_state(inp["x"].abs(), inp["dt"], inp["B"].abs(), Acs, Q)
     gate(S, S_ref, tol if dtype == "bf16" else 1e-5, "chunk_state S", S_mag)
 
+    # the forward's first launch (the cumsum inside the chunk-state kernel
+    # where that applies) gives the same cs, dtc and S, bit for bit
+    cs2, dtc2, S2 = ssd.chunk_cumsum_state(g["x"], g["B"], g["dt"], g["A"], Q)
+    assert torch.equal(cs2, cs) and torch.equal(dtc2, dtc), "cs / dtc of the fused launch"
+    assert torch.equal(S2, S), "S of the fused launch"
+
     # state passing, from the GPU's S
     sd = torch.bfloat16 if dtype == "bf16" else torch.float32
     Hin, fin = ssd.state_passing(S, cs, L, Q, sd, g["init"])
