@@ -34,16 +34,16 @@
 //   * Term (ii) first: Y^T = Hin C^T (K = N), then each column scaled by
 //     exp2(cs_i).
 // Two kernels share these steps:
-//   * the streaming kernel (Q in {128, 256}): wave w owns i tiles
+//   * the streaming kernel (Q = 128): wave w owns i tiles
 //     {w, 2W-1-w} so that every wave has the same number of causal (j <= i)
 //     tiles; C fragments of the wave's own tokens stay in registers; the
 //     carried state and the j blocks of B (32 rows) and x (32 rows) are
 //     copied straight into LDS (lds_pipe.h) through a 3-buffer ring, two
 //     blocks ahead, and x is read back transposed with tr16;
-//   * the resident kernel (Q = 256, long runs of heads sharing one B/C
-//     group): G^T does not depend on the head, so it is formed once per
-//     chunk and kept in registers across the run, two waves per SIMD (see
-//     its own description below).
+//   * the resident kernel (Q = 256, runs of heads sharing one B/C group):
+//     G^T does not depend on the head, so it is formed once per chunk and
+//     kept in registers across the run, two waves per SIMD (see its own
+//     description below).
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
@@ -1202,10 +1202,6 @@ static int scan_heads_per_workgroup(const Dims& d) {
     return best;
 }
 
-// Shortest run of heads for which the resident kernel beats the streaming
-// one (measured on the MI355X: 40-head runs gain, 4- and 6-head runs lose).
-constexpr int kResidentMinHeads = 12;
-
 // Heads per workgroup of the resident kernel (one workgroup per CU): a run
 // of hg heads of one group, the group's heads split into nsplit runs, with
 // a start-up charge (the resident tiles, the first copies) of 1.5 heads.
@@ -1241,22 +1237,19 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
         if (d.chunk == 256) {
             // the resident kernel pays for its start-up (each wave's 5 or 4
-            // G^T tiles and the first head's copies) once per run of heads:
-            // worth it for long runs only
+            // G^T tiles and the first head's copies) once per run of heads;
+            // measured on the MI355X it beats the streaming kernel from runs
+            // of 4 heads on (the long-context shape) and at 6 (130M-shaped)
             int hg = 0, nsplit = 0;
             scan_resident_split(d, &hg, &nsplit);
-            if (hg >= kResidentMinHeads) {
-                const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
-                chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg, nsplit);
-                return hipGetLastError();
-            }
+            const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
+            chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg, nsplit);
+            return hipGetLastError();
         }
+        // 128-token chunks: the streaming kernel
         const int hg = scan_heads_per_workgroup(d);
         const unsigned blocks = (unsigned)(d.batch * nc * (d.nheads / hg));
-        switch (d.chunk) {
-            case 128: chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg); break;
-            default: chunk_scan_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg); break;
-        }
+        chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg);
     } else if (dtype == 1) {
         launch_generic_t<bf16_t>(d, x, B, C, cs, dtc, Hin, D, y, stream);
     } else {

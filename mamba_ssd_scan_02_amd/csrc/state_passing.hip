@@ -61,6 +61,51 @@ __device__ __forceinline__ Vec<VW> load_vec(const bf16_t* p, int64_t i) {
     return r;
 }
 
+// The ring's slots hold S as loaded (bf16 pairs stay packed) and are widened
+// to fp32 only when the chain consumes them.  Widening at the load would make
+// the compiler wait for each load right after issuing it, and the ring would
+// hold nothing in flight.
+template <typename ST, int VW>
+struct RingSlot;
+template <int VW>
+struct RingSlot<float, VW> {
+    Vec<VW> v;
+    __device__ __forceinline__ void load(const float* p) { v = load_vec<VW>(p, 0); }
+    __device__ __forceinline__ Vec<VW> widen() const { return v; }
+};
+template <int VW>
+struct RingSlot<bf16_t, VW> {
+    static constexpr int kWords = VW == 1 ? 1 : VW / 2;
+    uint32_t w[kWords];
+    __device__ __forceinline__ void load(const bf16_t* p) {
+        if constexpr (VW == 4) {
+            const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+            w[0] = t[0];
+            w[1] = t[1];
+        } else if constexpr (VW == 2) {
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        } else if constexpr (VW == 1) {
+            w[0] = p[0].bits;
+        } else {
+#pragma unroll
+            for (int q = 0; q < kWords; ++q) w[q] = reinterpret_cast<const uint32_t*>(p)[q];
+        }
+    }
+    __device__ __forceinline__ Vec<VW> widen() const {
+        Vec<VW> r;
+        if constexpr (VW == 1) {
+            r.v[0] = bf16_bits_to_f32(w[0] & 0xffffu);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kWords; ++q) {
+                r.v[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+                r.v[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+            }
+        }
+        return r;
+    }
+};
+
 template <int VW>
 __device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r) {
     if constexpr (VW >= 4) {
@@ -105,12 +150,12 @@ template <typename ST, typename HT, int PF, int VW, bool kStore, bool kSum>
 __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t sstep,
                                             const float* __restrict__ dec, int64_t dstep, int n,
                                             HT* hp, Vec<VW>& h, float* lsum) {
-    Vec<VW> buf[PF];
+    RingSlot<ST, VW> buf[PF];
     float lg[PF];
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
         const int cl = min(k, n - 1);
-        buf[k] = load_vec<VW>(src + (int64_t)cl * sstep, 0);
+        buf[k].load(src + (int64_t)cl * sstep);
         lg[k] = dec[(int64_t)cl * dstep];
     }
     float ls = 0.0f;
@@ -127,11 +172,12 @@ __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t 
                 store_vec<VW>(hp, 0, h);
                 hp += sstep;
             }
+            const Vec<VW> sv = buf[k].widen();
 #pragma unroll
-            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
+            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + sv.v[e];
             __builtin_amdgcn_sched_barrier(0);
             const int cn = min(c0 + k + PF, n - 1);
-            buf[k] = load_vec<VW>(src + (int64_t)cn * sstep, 0);
+            buf[k].load(src + (int64_t)cn * sstep);
             lg[k] = dec[(int64_t)cn * dstep];
         }
     }
@@ -144,8 +190,9 @@ __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t 
                 store_vec<VW>(hp, 0, h);
                 hp += sstep;
             }
+            const Vec<VW> sv = buf[k].widen();
 #pragma unroll
-            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + buf[k].v[e];
+            for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + sv.v[e];
         }
     }
     if (kSum) *lsum = ls;
