@@ -16,12 +16,14 @@ storage, 2e-2 for bf16 storage unless a test states a tighter one):
   absolute values of the terms of r_i.  Each element is judged at the scale
   of its own terms, so an error in a term that is small next to the tensor's
   peak, or in one token among large ones, is seen.  A bound follows from the
-  arithmetic: every term reaches the result through at most two roundings
-  to the storage type before an fp32 accumulation (the weighted operand of a
-  chunk product, and the carried state as a matrix operand), and the result
-  is rounded once more, so |g_i - r_i| <= (3 u + O(fp32)) m_i with
-  u = 2^-9 for bf16 (about 5.9e-3) and u = 2^-24 for fp32.  Without a
-  magnitude the scale is |r_i| + rms(r).
+  arithmetic: every term reaches the result through at most three roundings
+  to the storage type with fp32 accumulation in between (the weighted
+  operand of the chunk-state product, the chunk state S, the carried state
+  as a matrix operand), and the result is rounded once more, so
+  |g_i - r_i| <= (4 u + O(fp32)) m_i with u = 2^-9 for bf16 (about 7.8e-3)
+  and u = 2^-24 for fp32.  The block around the scan rounds x, B and C once
+  more before the scan (about 2 u more).  Without a magnitude the scale is
+  |r_i| + rms(r).
 
 The ratio against |r_i| + 1e-3 rms(r) is printed beside them for
 information only: with bf16 operands it is dominated by entries near zero
