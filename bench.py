@@ -333,15 +333,23 @@ def bench_layer(ssd, spec, steps=20, block=True):
         ssd.ssd_forward(x, dt, A, Bm, Cm, D, spec.chunk, init, y=y, final_state=fin, workspace=ws)
         ssd.layer_out(y, li["z"], out=y)
 
-    settle(block, 0.1)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        block()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
-    res["block"] = {"us": round(us, 2), "tokens_per_s": round(b * L / (us * 1e-6), 1)}
+    # the same block with the gate inside the chunk scan's store
+    # (ssd_forward_gated): layer_in -> ssd_forward_gated
+    def block_gated():
+        run_in()
+        ssd.ssd_forward(x, dt, A, Bm, Cm, D, spec.chunk, init, y=y, final_state=fin, workspace=ws,
+                        z=li["z"])
+
+    for name, fn in (("block", block), ("block_gated", block_gated)):
+        settle(fn, 0.1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        res[name] = {"us": round(us, 2), "tokens_per_s": round(b * L / (us * 1e-6), 1)}
     return res
 
 

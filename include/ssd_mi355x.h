@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 6
+#define SSD_ABI_VERSION 7
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 
@@ -138,6 +138,25 @@ int32_t ssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
                     const void* C, const float* D, const float* init_state, void* y,
                     float* final_state, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * ssd_forward followed by the gate of the block around the scan: y receives
+ * (C h + D x) * silu(z), z [B][L][H][P] in the storage type -- the output
+ * gate of a Mamba block (page "State Space Models (SSM)", section "Da S4 a
+ * Mamba"; ssd_layer_out computes the same).  Where the 256-token matrix-core
+ * chunk scan runs, the gate is applied inside its store (y is never stored
+ * ungated; z is read there instead of a separate pass over y, z and out),
+ * elsewhere by the gate kernel in place after the scan.  Either way the
+ * result is what ssd_forward then ssd_layer_out(y, z, out = y) give, bit for
+ * bit.  z must not overlap y, final_state or the workspace (SSD_ERR_ALIAS);
+ * z NULL is SSD_ERR_NULL.  Everything else as ssd_forward.
+ */
+int32_t ssd_forward_gated(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                          int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                          const void* x, const float* dt, const float* A, const void* B,
+                          const void* C, const float* D, const float* init_state, const void* z,
+                          void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * ssd_forward for callers that cannot allocate (code under HIP graph

@@ -747,9 +747,10 @@ template <int ROLE>
 __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm,
                                            const bf16_t* __restrict__ Cm, const float* __restrict__ cs,
                                            const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
-                                           const float* __restrict__ D, bf16_t* __restrict__ y, int L,
-                                           int H, int G, int nc, int b, int c, int g, int h0, int cnt,
-                                           int wave, int lane, SSD_LDS char* sm) {
+                                           const float* __restrict__ D, const bf16_t* __restrict__ z,
+                                           bf16_t* __restrict__ y, int L, int H, int G, int nc, int b,
+                                           int c, int g, int h0, int cnt, int wave, int lane,
+                                           SSD_LDS char* sm) {
     using namespace rpl;
     constexpr int Q = 256, P = 64, N = 128;
     constexpr int NB = ROLE == 0 ? 5 : 4;       // blocks of this wave
@@ -866,6 +867,18 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
     f32x16 keep[2];
     float keep_colf = 1.0f;
     auto store_kept = [&](int k) {
+        // the gate's z rows (same layout and record as y), loaded first so
+        // that the staging below covers their latency
+        const int tr = lane >> 3, tc = lane & 7;
+        u32x4v zr[4];
+        if (z) {
+            const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16_t*>(z) + (((int64_t)b * L + tok0) * H + h0 + k) * P, (short)0, xrecord, 0x00020000);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                zr[m] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       zrs, (32 * own + 8 * m + tr) * rowbytes + 16 * tc, 0, 0));
+        }
         if (ROLE == 0 && p < 3) {
             const SSD_LDS f32x4* red = (const SSD_LDS f32x4*)(sm + kRed + ((k & 1) * 3 + p) * kRedTile);
 #pragma unroll
@@ -892,13 +905,22 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
                 *reinterpret_cast<SSD_LDS u32x4v*>(wrow + stage_off(l32, 4 * mt + 2 * hf + q)) = w;
             }
         // lane l: row 8 m + l / 8 of the tile, chunk l % 8; rows past the
-        // sequence end fall outside the record and are dropped
+        // sequence end fall outside the record and are dropped.  With the
+        // gate, out = y silu(z) on the bf16 y, rounded once more: what the
+        // separate gate kernel computes from the stored y.
         const __amdgpu_buffer_rsrc_t yrs = yrs_of(k);
-        const int tr = lane >> 3, tc = lane & 7;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int r = 8 * m + tr;
-            const u32x4v v = *reinterpret_cast<const SSD_LDS u32x4v*>(sb + (wave + 8 * m) * 1024 + stage_off(r, tc));
+            u32x4v v = *reinterpret_cast<const SSD_LDS u32x4v*>(sb + (wave + 8 * m) * 1024 + stage_off(r, tc));
+            if (z) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y0 = bf16_bits_to_f32(v[e] & 0xffffu), y1 = bf16_bits_to_f32(v[e] >> 16);
+                    const float z0 = bf16_bits_to_f32(zr[m][e] & 0xffffu), z1 = bf16_bits_to_f32(zr[m][e] >> 16);
+                    v[e] = pack_bf16x2(y0 * silu_f(z0), y1 * silu_f(z1));
+                }
+            }
             __builtin_amdgcn_raw_buffer_store_b128(v, yrs, (32 * own + r) * rowbytes + 16 * tc, 0, 0);
         }
     };
@@ -1028,8 +1050,8 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
 __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
-    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg,
-    int nsplit) {
+    const float* __restrict__ D, const bf16_t* __restrict__ z, bf16_t* __restrict__ y, int L, int H,
+    int G, int nc, int hg, int nsplit) {
     __shared__ __align__(16) char smem[rpl::kBytes];
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = (int)(wg % (uint32_t)nsplit);
@@ -1045,9 +1067,9 @@ __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     __builtin_assume(wave >= 0 && wave < 8);
     SSD_LDS char* const sm = (SSD_LDS char*)lds(smem);
     if (wave < 4)
-        paired_run<0>(x, Bm, Cm, cs, dtc, Hin, D, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
+        paired_run<0>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
     else
-        paired_run<1>(x, Bm, Cm, cs, dtc, Hin, D, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
+        paired_run<1>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1227,7 +1249,7 @@ static void scan_resident_split(const Dims& d, int* hg_out, int* nsplit_out) {
 
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
-                             const float* D, void* y, hipStream_t stream) {
+                             const float* D, void* y, hipStream_t stream, const void* z) {
     if (mfma_path(dtype, d)) {
         const bf16_t* xb = static_cast<const bf16_t*>(x);
         const bf16_t* bb = static_cast<const bf16_t*>(B);
@@ -1243,8 +1265,10 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
             int hg = 0, nsplit = 0;
             scan_resident_split(d, &hg, &nsplit);
             const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
-            chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg, nsplit);
-            return hipGetLastError();
+            chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D,
+                                                                 static_cast<const bf16_t*>(z), yb, L, H, G,
+                                                                 nc, hg, nsplit);
+            return hipGetLastError();   // the gate, if any, is inside
         }
         // 128-token chunks: the streaming kernel
         const int hg = scan_heads_per_workgroup(d);
@@ -1255,7 +1279,11 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
     } else {
         launch_generic_t<float>(d, x, B, C, cs, dtc, Hin, D, y, stream);
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    // the other kernels store y first; the gate then runs in place
+    if (e == hipSuccess && z)
+        e = launch_layer_out(d.batch * d.seqlen * d.nheads * d.headdim, dtype, y, z, y, stream);
+    return e;
 }
 
 }  // namespace ssd

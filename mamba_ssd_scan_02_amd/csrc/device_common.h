@@ -57,6 +57,13 @@ struct Elem<bf16_t> {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// silu(v) = v / (1 + e^-v), with the hardware exp2 and reciprocal (about 1
+// ulp each): the gate out = y silu(z) of the block around the scan, in its own
+// kernel and inside chunk_scan's store, and the convolution's activation.
+__device__ __forceinline__ float silu_f(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
+}
+
 // Exact zero-order-hold input weight (exp(dt a) - 1) / a, dt where a = 0
 // (page "State Space Models (SSM)", ultralytics.com glossary, section "Come
 // funzionano gli SSM": Bbar = (Abar - 1) / A B).  expm1 keeps the small-step

@@ -45,9 +45,12 @@ hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_r
                                     const float* cs, const float* init, void* Hin,
                                     float* final_state, void* workspace, hipStream_t stream);
 
+// With z, y receives y * silu(z) (the gate of the block around the scan):
+// inside the store of the 256-token matrix-core kernel, else by the gate
+// kernel in place after the chunk scan.
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
-                             const float* D, void* y, hipStream_t stream);
+                             const float* D, void* y, hipStream_t stream, const void* z = nullptr);
 
 // Chunk state and state passing walked per (batch, head pair) in one pass
 // (bf16 matrix-core path, chunk 128 or 256, an even head count per group).

@@ -25,11 +25,8 @@ namespace ssd {
 
 namespace {
 
-// v / (1 + e^-v) with the hardware exp2 and reciprocal (about 1 ulp each):
-// e^-v overflows to +inf for v < -88, and rcp(inf) = 0 gives -0.
-__device__ __forceinline__ float silu_f(float v) {
-    return v * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
-}
+// silu_f (device_common.h): e^-v overflows to +inf for v < -88, and
+// rcp(inf) = 0 gives -0.
 // log(1 + e^v) without overflow: max(v, 0) + log1p(e^-|v|)
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
 

@@ -316,7 +316,7 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
                             const void* x, const float* dt, const float* A, const void* B,
                             const void* C, const float* D, const float* init_state, void* y,
                             float* final_state, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream, bool zoh) {
+                            hipStream_t stream, bool zoh, const void* z = nullptr) {
     Dims d;
     int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
     if (st != SSD_OK) return st;
@@ -327,7 +327,8 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     if (!workspace || workspace_bytes < lo.total) return SSD_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
         !aligned(workspace, 16) || !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
-        (init_state && !aligned(init_state, 16)) || (final_state && !aligned(final_state, 16)))
+        (init_state && !aligned(init_state, 16)) || (final_state && !aligned(final_state, 16)) ||
+        (z && !aligned(z, 16)))
         return SSD_ERR_ALIGN;
 
     size_t es;
@@ -339,14 +340,15 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     const size_t hbytes = (size_t)d.nheads * 4;
     const size_t stbytes = (size_t)d.batch * d.nheads * d.headdim * d.dstate * 4;
     // Every output (y, final_state, the workspace) must stay clear of every
-    // input and of the other outputs; the one permitted overlap is
-    // final_state on init_state (the state is read before it is written).
+    // input (the gate's z included) and of the other outputs; the one
+    // permitted overlap is final_state on init_state (the state is read
+    // before it is written).
     struct Span { const void* p; size_t n; };
     const Span inputs[] = {{x, ybytes}, {B, bcbytes}, {C, bcbytes}, {dt, dtbytes},
-                           {A, hbytes}, {D, hbytes}, {init_state, stbytes}};
+                           {A, hbytes}, {D, hbytes}, {init_state, stbytes}, {z, ybytes}};
     const Span outs[] = {{y, ybytes}, {workspace, lo.total}, {final_state, stbytes}};
     for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 7; ++i) {
+        for (int i = 0; i < 8; ++i) {
             if (o == 2 && i == 6) continue;   // final_state may alias init_state
             if (overlaps(outs[o].p, outs[o].n, inputs[i].p, inputs[i].n)) return SSD_ERR_ALIAS;
         }
@@ -375,7 +377,7 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     }
     e = ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream);
     if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_chunk_scan(d, dtype, x, B, C, cs, dtc, Hin, D, y, stream);
+    e = ssd::launch_chunk_scan(d, dtype, x, B, C, cs, dtc, Hin, D, y, stream, z);
     return hip_status(e);
 }
 
@@ -408,6 +410,22 @@ int32_t ssd_forward_noalloc(int64_t batch, int64_t seqlen, int64_t nheads, int64
     return forward_impl(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, x, dt, A,
                         B, C, D, init_state, y, final_state, ws, (size_t)SSD_NOALLOC_SCRATCH_BYTES,
                         stream, false);
+}
+
+int32_t ssd_forward_gated(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                          int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                          const void* x, const float* dt, const float* A, const void* B,
+                          const void* C, const float* D, const float* init_state, const void* z,
+                          void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (!z) {
+        Dims d;
+        const int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d);
+        return st != SSD_OK ? st : SSD_ERR_NULL;
+    }
+    return forward_impl(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, x, dt, A,
+                        B, C, D, init_state, y, final_state, workspace, workspace_bytes, stream,
+                        false, z);
 }
 
 int32_t ssd_forward_zoh(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,

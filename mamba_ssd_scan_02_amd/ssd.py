@@ -21,7 +21,7 @@ DTYPE_BF16 = 1
 
 # The SSD_ABI_VERSION this binding was written against; load() refuses a
 # library that reports another one (a stale build).
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _STATUS_OK = 0
 
@@ -61,6 +61,8 @@ def load():
     lib.ssd_forward.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp, sz, vp]
     lib.ssd_forward_zoh.restype = i32
     lib.ssd_forward_zoh.argtypes = lib.ssd_forward.argtypes
+    lib.ssd_forward_gated.restype = i32
+    lib.ssd_forward_gated.argtypes = [i64] * 7 + [i32] + [vp] * 10 + [vp, sz, vp]
     lib.ssd_forward_noalloc.restype = i32
     lib.ssd_forward_noalloc.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp]
     lib.ssm_step.restype = i32
@@ -173,7 +175,7 @@ def workspace_regions(batch, seqlen, nheads, headdim, dstate, chunk, dtype):
 
 
 def ssd_forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, *, y=None,
-                final_state=None, workspace=None, return_final_state=True, zoh=False):
+                final_state=None, workspace=None, return_final_state=True, zoh=False, z=None):
     """Whole-sequence SSD forward on the GPU.
 
     x [batch, L, H, P] (bf16 | fp32); dt [batch, L, H] fp32; A [H] fp32;
@@ -182,7 +184,9 @@ def ssd_forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, *, y=None,
     Returns (y [batch, L, H, P] in x's dtype, final_state [batch, H, P, N] fp32
     or None).  ``y``, ``final_state`` and ``workspace`` (uint8, at least
     workspace_bytes(...)) may be passed in to avoid allocation.  ``zoh``
-    selects the exact zero-order-hold input weight (ssd_forward_zoh).
+    selects the exact zero-order-hold input weight (ssd_forward_zoh); ``z``
+    [batch, L, H, P] (x's dtype) gates the output, y * silu(z)
+    (ssd_forward_gated; not with ``zoh``).
     """
     lib = load()
     x = _dev(x, "x")
@@ -208,6 +212,15 @@ def ssd_forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, *, y=None,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace", torch.uint8, None, dev)
+    if z is not None:
+        if zoh:
+            raise ValueError("the gated forward has no zero-order-hold variant")
+        _dev(z, "z", x.dtype, x.shape, dev)
+        st = lib.ssd_forward_gated(batch, L, H, P, N, G, chunk, code, _p(x), _p(dt), _p(A), _p(B),
+                                   _p(C), _p(D), _p(init_state), _p(z), _p(y), _p(final_state),
+                                   _p(workspace), workspace.numel(), _stream(dev))
+        _check("ssd_forward_gated", st)
+        return y, final_state
     fn = lib.ssd_forward_zoh if zoh else lib.ssd_forward
     st = fn(batch, L, H, P, N, G, chunk, code, _p(x), _p(dt), _p(A), _p(B), _p(C),
             _p(D), _p(init_state), _p(y), _p(final_state), _p(workspace),
@@ -439,8 +452,12 @@ def layer_out(y, z, out=None):
 def ssd_layer(xbc, z, dt_raw, A, D, conv_w, conv_b, dt_bias, nheads, headdim, ngroups, dstate,
               chunk=256, init_state=None, zoh=False):
     """The block around the scan, each step in the library's kernels:
-    layer_in -> ssd_forward -> layer_out.  z [batch, L, H, P] in xbc's dtype.
-    Returns (out [batch, L, H, P], final_state [batch, H, P, N] fp32)."""
+    layer_in -> ssd_forward_gated (the gate inside the chunk scan's store where
+    that applies), or ssd_forward_zoh -> layer_out for ``zoh``.  z [batch, L,
+    H, P] in xbc's dtype.  Returns (out [batch, L, H, P], final_state [batch,
+    H, P, N] fp32)."""
     x, B, C, dt = layer_in(xbc, conv_w, conv_b, dt_raw, dt_bias, nheads, headdim, ngroups, dstate)
-    y, fin = ssd_forward(x, dt, A, B, C, D, chunk, init_state, zoh=zoh)
-    return layer_out(y, z, out=y), fin
+    if zoh:
+        y, fin = ssd_forward(x, dt, A, B, C, D, chunk, init_state, zoh=True)
+        return layer_out(y, z, out=y), fin
+    return ssd_forward(x, dt, A, B, C, D, chunk, init_state, z=z)

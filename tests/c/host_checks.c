@@ -89,6 +89,13 @@ static void library_checks(void) {
     CHECK(ssd_forward(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, y, fin, (char*)y + 512, need, NULL) == SSD_ERR_ALIAS);
     CHECK(ssd_forward(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, y, fin, A, need, NULL) == SSD_ERR_ALIAS);
     CHECK(ssd_forward_zoh(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, x, fin, ws, need, NULL) == SSD_ERR_ALIAS);
+    /* the gated forward: z is an input like x */
+    void* zz = FAKE(11);
+    CHECK(ssd_forward_gated(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, NULL, y, fin, ws, need, NULL) == SSD_ERR_NULL);
+    CHECK(ssd_forward_gated(0, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, NULL, y, fin, ws, need, NULL) == SSD_ERR_SHAPE);
+    CHECK(ssd_forward_gated(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, y, y, fin, ws, need, NULL) == SSD_ERR_ALIAS);
+    CHECK(ssd_forward_gated(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, zz, y, fin, (char*)zz + 256, need, NULL) == SSD_ERR_ALIAS);
+    CHECK(ssd_forward_gated(b, L, H, P, N, G, Q, f32, x, dt, A, B, C, D, init, (char*)zz + 4, y, fin, ws, need, NULL) == SSD_ERR_ALIGN);
 
     /* the allocation-free forward: sizes beyond its array are rejected first */
     CHECK(ssd_forward_noalloc(4, 8192, 80, 64, 128, 1, 256, SSD_DTYPE_BF16, x, dt, A, B, C, D, init, y, fin, NULL) == SSD_ERR_WORKSPACE);

@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("ssd_forward", "ssm_step", "ssd_forward_workspace_bytes", "ssd_status_str",
               "ssd_abi_version", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_chunk_cumsum_state",
+              "ssd_forward_gated",
               "ssd_state_passing",
               "ssd_state_scan", "ssd_chunk_scan", "ssd_forward_zoh", "ssd_chunk_cumsum_zoh",
               "ssm_step_zoh", "ssd_layer_in", "ssd_layer_out", "ssd_state_passing_seg",
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 6
+    assert lib.ssd_abi_version() == 7
     for s in range(8):
         assert lib.ssd_status_str(s)
     assert lib.ssd_status_str(99) == b"unknown status"

@@ -214,3 +214,45 @@ def test_layer_bitwise_deterministic():
                                  g["conv_b"], g["dt_bias"], 4, 64, 2, 128, 256, g["init"])
         outs.append((out.clone(), fin.clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+GATED_CASES = [
+    # (name, batch, L, H, P, N, G, chunk, dtype) -- the first three reach the
+    # 256-token matrix-core chunk scan (the gate inside its store), the rest
+    # the gate kernel after the scan
+    ("resident_ragged_groups", 2, 700, 4, 64, 128, 2, 256, "bf16"),
+    ("resident_130m_heads", 2, 1024, 24, 64, 128, 1, 256, "bf16"),
+    ("resident_one_chunk", 1, 100, 2, 64, 128, 1, 256, "bf16"),
+    ("streaming_q128", 1, 520, 2, 64, 128, 1, 128, "bf16"),
+    ("vector_units_q64", 1, 333, 2, 64, 128, 2, 64, "bf16"),
+    ("generic_f32", 1, 300, 3, 16, 16, 1, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+def test_forward_gated_matches_forward_then_gate(case):
+    """ssd_forward_gated gives, bit for bit, what ssd_forward followed by
+    ssd_layer_out(y, z, out = y) gives, with its outputs and workspace
+    guarded (canary bands, NaN fill); the final state is unchanged."""
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import make_forward_inputs
+    from tests.helpers import Guarded
+
+    name, batch, L, H, P, N, G, Q, dtype = case
+    say(f"[gated] {name}")
+    inp = make_forward_inputs(_spec(batch, L, H, P, N, G, dtype, chunk=Q, init_var=0.1, seed=61))
+    g = to_gpu(inp)
+    x = g["x"]
+    gen = torch.Generator(device="cpu").manual_seed(62)
+    z = torch.randn(x.shape, generator=gen, dtype=torch.float32).to(x.dtype).cuda()
+    y_ref, f_ref = ssd.ssd_forward(x, g["dt"], g["A"], g["B"], g["C"], g["D"], Q, g["init"])
+    out_ref = ssd.layer_out(y_ref, z, out=y_ref.clone())
+    yb = Guarded(tuple(x.shape), x.dtype)
+    fb = Guarded((batch, H, P, N), torch.float32)
+    wb = Guarded((ssd.workspace_bytes(batch, L, H, P, N, G, Q, x.dtype),), torch.uint8)
+    out, fin = ssd.ssd_forward(x, g["dt"], g["A"], g["B"], g["C"], g["D"], Q, g["init"], y=yb.t,
+                               final_state=fb.t, workspace=wb.t, z=z)
+    torch.cuda.synchronize()
+    assert yb.intact() and fb.intact() and wb.intact(), "a store landed outside its array"
+    assert torch.equal(out, out_ref), (name, max_rel_err(out, out_ref.cpu().double().numpy()))
+    assert torch.equal(fin, f_ref)
