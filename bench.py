@@ -690,7 +690,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the 130M-shaped forward printed beside the headline")
+                    help="skip the 130M-shaped and the one-million-token forwards printed beside "
+                         "the headline")
     ap.add_argument("--workload", default="mamba2_2p7b_b4_l8192_h80_p64_n128",
                     choices=["mamba2_2p7b_b4_l8192_h80_p64_n128", "mamba2_130m_b8_l2048_h24_p64_n128",
                              "long_b1_l1048576_h32_p64_n128_g8"],
@@ -826,6 +827,25 @@ def main():
                                "tokens_per_s": round(s2.batch * s2.seqlen / (ms2 * 1e-3), 1),
                                "forward_kernels": forward_kernels(dims2)}
         del g2, y2, f2, ws2
+        # one sequence of 1,048,576 tokens (8 groups of 4 heads): few steps,
+        # its seeded inputs take most of this leg's time to draw on the host
+        from mamba_ssd_scan_02_amd.workloads import LONG_1M as s4
+        log(f"[bench] {s4.name} forward")
+        inp4 = make_forward_inputs(s4)
+        g4 = {k: (v.cuda() if v is not None else None) for k, v in inp4.items()}
+        del inp4
+        y4 = torch.empty_like(g4["x"])
+        f4 = torch.empty((s4.batch, s4.nheads, s4.headdim, s4.dstate), dtype=torch.float32,
+                         device="cuda")
+        ws4 = torch.empty(ssd.workspace_bytes(s4.batch, s4.seqlen, s4.nheads, s4.headdim, s4.dstate,
+                                              s4.ngroups, s4.chunk, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        ms4, _ = time_forward(ssd, g4, y4, f4, ws4, s4.chunk, 5, 2)
+        dims4 = (s4.batch, s4.seqlen, s4.nheads, s4.headdim, s4.dstate, s4.ngroups, s4.chunk)
+        out["forward_long"] = {"workload": s4.name, "us_per_step": round(ms4 * 1e3, 2),
+                               "tokens_per_s": round(s4.batch * s4.seqlen / (ms4 * 1e-3), 1),
+                               "steps": 5, "forward_kernels": forward_kernels(dims4)}
+        del g4, y4, f4, ws4
     log("[bench] zero-order-hold forward")
     ms_zoh, _ = time_forward(ssd, g, y, fin, ws, Q, args.steps, args.warmup, zoh=True)
     out["forward_zoh"] = {"us_per_step": round(ms_zoh * 1e3, 2),

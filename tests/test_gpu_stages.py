@@ -303,8 +303,9 @@ def test_state_passing_segmented_errors():
 
 def test_state_passing_segmented_long_context():
     """At the long-context shape (32 chains of 4,096 chunks) the segmented scan
-    gives the sequential kernel's results up to rounding order (the
-    sequential kernel is checked against the oracle by the 1M-token forward)."""
+    gives the sequential kernel's results up to rounding order, and both
+    match the fp64 stage definition on a sample of heads and state entries
+    over the whole chain."""
     import mamba_ssd_scan_02_amd as ssd
     from mamba_ssd_scan_02_amd.workloads import LONG_1M as spec
     say("[state_passing_seg] long context")
@@ -325,6 +326,29 @@ def test_state_passing_segmented_long_context():
     # bf16 entering states: equal up to one rounding step
     d = (Hin2.float() - Hin.float()).abs()
     assert bool((d <= Hin.float().abs() * 2.0 ** -7 + 1e-6 * Hin.float().abs().max()).all())
+
+    # both kernels against the fp64 stage definition on a sample: two heads,
+    # 256 of the 8,192 state entries, every one of the 4,096 chunks (from the
+    # GPU's S and the host's fp64 prefix of dt A)
+    from oracle import stages
+    heads = [0, H - 1]
+    idx = torch.from_numpy(np.random.default_rng(78).choice(P * N, 256, replace=False)).cuda()
+    sub = lambda t: t[0, heads].reshape(len(heads), nc, P * N)[:, :, idx]          # [2, nc, 256]
+    S_sub = sub(S).cpu().double().numpy()[None, :, :, None, :]                   # [1, 2, nc, 1, 256]
+    init_sub = init[0, heads].reshape(len(heads), P * N)[:, idx].cpu().double().numpy()[None, :, None, :]
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    dt = torch.nn.functional.softplus(torch.randn(b, L, H, device="cuda", generator=gen) - 4.0)
+    A_h = A.cpu().double().numpy()
+    dt_h = dt[:, :, heads].cpu().double().numpy()
+    del dt
+    Acs = stages.chunk_cumsum(dt_h, A_h[heads], Q)                               # [1, 2, nc, Q]
+    Hin_ref, fin_ref = stages.state_passing(S_sub, Acs, init_sub)
+    Hin_mag, fin_mag = stages.state_passing(np.abs(S_sub), Acs, np.abs(init_sub))
+    for what, Hx, fx in (("sequential", Hin, fin), ("segmented", Hin2, fin2)):
+        Hs = sub(Hx).float()[None, :, :, None, :]
+        fs = fx[0, heads].reshape(len(heads), P * N)[:, idx][None, :, None, :]
+        gate(Hs, Hin_ref, 8e-3, f"{what} Hin (sampled)", Hin_mag)
+        gate(fs, fin_ref, 1e-5, f"{what} final (sampled)", fin_mag)
 
 
 def test_state_passing_segmented_deterministic():
