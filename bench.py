@@ -201,7 +201,7 @@ def forward_kernels(dims):
     (ssd_chunk_cumsum_state, one launch where a group's head count is even),
     state passing and chunk_scan."""
     b, L, H, P, N, G, Q = dims
-    fused = P == 64 and N == 128 and Q in (128, 256) and (H // G) % 2 == 0
+    fused = P == 64 and N == 128 and Q in (64, 128, 256) and (H // G) % 2 == 0
     return (["chunk_state_cumsum"] if fused else ["chunk_cumsum", "chunk_state"]) + \
         ["state_passing", "chunk_scan"]
 

@@ -61,9 +61,8 @@
  *    be partial.
  *  - Supported shapes (ssd_forward and the stage calls): either dtype with
  *    1 <= P <= 128, 1 <= N <= 128, 1 <= Q <= 256; bf16 with P = 64, N = 128
- *    and Q in {128, 256} runs on the matrix cores, everything else
- *    (chunk 64 included) on the vector units.  Anything else returns
- *    SSD_ERR_UNSUPPORTED.
+ *    and Q in {64, 128, 256} runs on the matrix cores, everything else on
+ *    the vector units.  Anything else returns SSD_ERR_UNSUPPORTED.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H

@@ -13,8 +13,8 @@
 // through the chunk; (iii) is the D x term of y = C h + D x (page "Puntata 205",
 // section "Cos'e' un SSM, in 30 secondi").
 //
-// Matrix-core kernel (bf16, P = 64, N = 128, Q in {128, 256}); one
-// workgroup of Q/64 waves per (batch, chunk, head); v_mfma_f32_32x32x16_bf16.
+// Matrix-core kernels (bf16, P = 64, N = 128, Q in {64, 128, 256}),
+// v_mfma_f32_32x32x16_bf16.
 // Everything is computed transposed, Y^T[p][i], so that each lane owns one
 // output token i (the MFMA result column) -- that makes the masked weights
 // G~^T[j][i] of a 32 x 32 tile come out of the C.B^T product in exactly the
@@ -33,17 +33,18 @@
 //     of its token: two 16-byte stores per tile.
 //   * Term (ii) first: Y^T = Hin C^T (K = N), then each column scaled by
 //     exp2(cs_i).
-// Two kernels share these steps:
-//   * the streaming kernel (Q = 128): wave w owns i tiles
+// Three kernels share these steps:
+//   * the streaming kernel (Q = 128, one workgroup of 2 waves per (batch,
+//     chunk, run of heads)): wave w owns i tiles
 //     {w, 2W-1-w} so that every wave has the same number of causal (j <= i)
 //     tiles; C fragments of the wave's own tokens stay in registers; the
 //     carried state and the j blocks of B (32 rows) and x (32 rows) are
 //     copied straight into LDS (lds_pipe.h) through a 3-buffer ring, two
 //     blocks ahead, and x is read back transposed with tr16;
-//   * the resident kernel (Q = 256, runs of heads sharing one B/C group):
-//     G^T does not depend on the head, so it is formed once per chunk and
-//     kept in registers across the run, two waves per SIMD (see its own
-//     description below).
+//   * the resident kernels (Q = 256 and Q = 64, runs of heads sharing one
+//     B/C group): G^T does not depend on the head, so it is formed once per
+//     chunk and kept in registers across the run (see their own
+//     descriptions below).
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
@@ -1073,6 +1074,182 @@ __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 64-token chunks: one workgroup of 4 waves per (batch, chunk, group, run of
+// heads), three workgroups per CU.  The chunk's three causal 32 x 32 blocks of
+// G^T = B C^T do not depend on the head: they are formed once per run and
+// stay in registers.  Wave w owns output tile t = w / 2 (tokens 32 t ..
+// 32 t + 31) for channels 32 (w % 2) .. + 31, so the two waves of a tile both
+// form its blocks (one for tile 0, two for tile 1).  A head's x rows (8 KB),
+// carried state (16 KB) and cs/dt rows are copied into one of two LDS slots
+// one head ahead.  Every weight is formed directly, exp2(cs_i - cs_j) dt_j
+// per element (within 64 tokens the factorised form saves little), and the
+// state term is scaled by exp2(cs_i).  Each lane stores 16 consecutive
+// channels of its token (two 16-byte stores); tokens past the end fall
+// outside the y record and are dropped.
+namespace q64 {
+constexpr int kX = 0;          // x: 64 rows x 128 B
+constexpr int kH = 8192;       // Hin: 64 rows x 256 B
+constexpr int kCs = 24576;     // cs: 64 floats
+constexpr int kDt = 24832;     // dt: 64 floats
+constexpr int kSlot = 25088;
+constexpr int kBytes = 2 * kSlot;
+static_assert(kSlot % 16 == 0 && 2 * kBytes <= 160 * 1024, "chunk_scan (64-token chunks) LDS");
+}  // namespace q64
+
+__global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
+    const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
+    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg,
+    int nsplit) {
+    using namespace q64;
+    constexpr int Q = 64, P = 64, N = 128;
+    __shared__ __align__(16) char smem[kBytes];
+    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int split = (int)(wg % (uint32_t)nsplit);
+    const uint32_t bcg = wg / (uint32_t)nsplit;
+    const int g = (int)(bcg % (uint32_t)G);
+    const int bc = (int)(bcg / (uint32_t)G);
+    const int c = bc % nc, b = bc / nc;
+    const int hpg = H / G;
+    const int h0 = g * hpg + split * hg;
+    const int cnt = min(hg, hpg - split * hg);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    __builtin_assume(wave >= 0 && wave < 4);
+    const int t = wave >> 1, mt = wave & 1;
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int tok0 = c * Q;
+    const int rowbytes = H * P * 2;
+    // end of the chunk's last valid row, for x and y
+    const int xrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
+    SSD_LDS char* const sm = (SSD_LDS char*)lds(smem);
+
+    // Copies of head k into the slot at s: x rows 8 q .. 8 q + 7 and Hin
+    // rows 4 q .. 4 q + 3 for the pieces q = wave + 4 m; cs (wave 0) and dt
+    // (wave 1) whole rows.
+    const uint32_t xo = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)rowbytes +
+                        16u * (uint32_t)((lane & 7) ^ swz_x(lane >> 3));
+    const uint32_t xstep = 32u * (uint32_t)rowbytes;
+    uint32_t ho[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r = 4 * (wave + 4 * m) + (lane >> 4);
+        ho[m] = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ swz_h(r)));
+    }
+    auto issue = [&](int k, SSD_LDS char* s) {
+        const int h = h0 + k;
+        const __amdgpu_buffer_rsrc_t rx = make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, xrecord);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) dma16_rs(rx, xo + (uint32_t)m * xstep, s + kX + (wave + 4 * m) * 1024);
+        const __amdgpu_buffer_rsrc_t rh =
+            make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), P * N * 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dma16_rs(rh, ho[m], s + kH + (wave + 4 * m) * 1024);
+        if (wave < 2) {
+            const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
+            dma4_rs(make_rs((wave == 0 ? cs : dtc) + row, Q * 4), 4u * (uint32_t)lane,
+                    s + (wave == 0 ? kCs : kDt));
+        }
+    };
+
+    issue(0, sm);
+
+    // C fragments of tile t (B operand of both C products) and the G^T
+    // blocks (t, s), s <= t, the diagonal one masked to j <= i.  Tokens past
+    // the end re-read the last token (their weights or outputs are dropped).
+    uint4 cf[8];
+    {
+        const int tok = min(tok0 + 32 * t + l32, L - 1);
+        const bf16_t* crow = Cm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) cf[kk] = *reinterpret_cast<const uint4*>(crow + 16 * kk);
+    }
+    f32x16 gt[2] = {f32x16{}, f32x16{}};
+    {
+        const int jr = perm_pi(l32);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            if (sb > t) break;
+            const int tok = min(tok0 + 32 * sb + jr, L - 1);
+            const bf16_t* brow = Bm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
+            uint4 bq[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) bq[kk] = *reinterpret_cast<const uint4*>(brow + 16 * kk);
+            f32x16 a = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bq[kk]),
+                                                            __builtin_bit_cast(bf16x8, cf[kk]), a, 0, 0, 0);
+            if (sb == t) mask_causal(a, l32, hf);
+            gt[sb] = a;
+        }
+    }
+
+    const XtAddr xa = xt_addr(lane);
+    const int pc = 32 * mt + xa.qb;
+    const int xchk = pc >> 3, xsub = (pc & 7) * 2;
+    const int pr = 32 * mt + perm_sigma(l32);
+    for (int k = 0; k < cnt; ++k) {
+        // head k's copies have landed (nothing else is outstanding), and
+        // every wave is past head k - 1, whose slot now takes head k + 1
+        wait_vmcnt<0>();
+        barrier_lds();
+        if (k + 1 < cnt) issue(k + 1, sm + ((k + 1) & 1) * kSlot);
+        const SSD_LDS char* S = sm + (k & 1) * kSlot;
+        const SSD_LDS float* css = (const SSD_LDS float*)(S + kCs);
+        const SSD_LDS float* dts = (const SSD_LDS float*)(S + kDt);
+        const float Dh = D ? D[h0 + k] : 0.0f;
+        const float csi = css[32 * t + l32];
+
+        // (i) + (iii): Y^T += X^T G~^T over the tile's blocks
+        f32x16 acc = {};
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            if (sb > t) break;
+            u32x4v gq[2];
+            rs_weights_direct(gq, gt[sb], css + 32 * sb, dts + 32 * sb, csi, Dh, sb == t, hf);
+            const SSD_LDS char* xb = S + kX + sb * 4096;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r0 = 16 * u + xa.trow0, r1 = r0 + 4;
+                const u32x2v lo = __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (SSD_LDS v4s*)(xb + r0 * 128 + ((xchk ^ swz_x(r0)) << 4) + xsub)));
+                const u32x2v hi = __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (SSD_LDS v4s*)(xb + r1 * 128 + ((xchk ^ swz_x(r1)) << 4) + xsub)));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, u32x4v{lo.x, lo.y, hi.x, hi.y}),
+                    __builtin_bit_cast(bf16x8, gq[u]), acc, 0, 0, 0);
+            }
+        }
+        // (ii): accS = Hin C_t^T, added as exp2(cs_i) accS
+        {
+            const SSD_LDS uint4* hs = (const SSD_LDS uint4*)(S + kH);
+            f32x16 accS = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int ch = 2 * kk + hf;
+                const u32x4v ha = *reinterpret_cast<const SSD_LDS u32x4v*>(hs + pr * 16 + (ch ^ swz_h(pr)));
+                accS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ha),
+                                                               __builtin_bit_cast(bf16x8, cf[kk]), accS, 0, 0, 0);
+            }
+            const float ss = fast_exp2(csi);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf(ss, accS[r], acc[r]);
+        }
+        // y: token 32 t + l32, channels 32 mt + 16 hf + 0..15
+        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+            y + (((int64_t)b * L + tok0) * H + h0 + k) * P, (short)0, xrecord, 0x00020000);
+        const int off = (32 * t + l32) * rowbytes + 64 * mt + 32 * hf;
+        uint32_t w8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w8[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{w8[0], w8[1], w8[2], w8[3]}, yrs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{w8[4], w8[5], w8[6], w8[7]}, yrs, off + 16, 0, 0);
+    }
+    wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
 // Generic kernel: workgroup per (batch, chunk, head, 32-token i tile).
 template <typename T, int MAXO>
 __global__ __launch_bounds__(256) void chunk_scan_generic_kernel(
@@ -1224,10 +1401,11 @@ static int scan_heads_per_workgroup(const Dims& d) {
     return best;
 }
 
-// Heads per workgroup of the resident kernel (one workgroup per CU): a run
-// of hg heads of one group, the group's heads split into nsplit runs, with
-// a start-up charge (the resident tiles, the first copies) of 1.5 heads.
-static void scan_resident_split(const Dims& d, int* hg_out, int* nsplit_out) {
+// Heads per workgroup of the resident kernels: a run of hg heads of one
+// group, the group's heads split into nsplit runs, with per_cu workgroups
+// resident on a CU and a start-up charge (the resident tiles, the first
+// copies) of `startup` heads.
+static void scan_run_split(const Dims& d, int per_cu, double startup, int* hg_out, int* nsplit_out) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
@@ -1235,12 +1413,13 @@ static void scan_resident_split(const Dims& d, int* hg_out, int* nsplit_out) {
     }
     const int64_t hpg = d.nheads / d.ngroups;
     const double units = (double)d.batch * (double)d.nchunks * (double)d.ngroups;
+    const double slots = (double)per_cu * (double)cus;
     int best = (int)hpg;
     double best_cost = 1e300;
     for (int64_t hg = 1; hg <= hpg; ++hg) {
         const int64_t ns = (hpg + hg - 1) / hg;
-        const double rounds = std::ceil(units * (double)ns / (double)cus);
-        const double cost = rounds * ((double)hg + 1.5);
+        const double rounds = std::ceil(units * (double)ns / slots);
+        const double cost = rounds * ((double)hg + startup);
         if (cost < best_cost - 1e-9) { best_cost = cost; best = (int)hg; }
     }
     *hg_out = best;
@@ -1263,17 +1442,25 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
             // measured on the MI355X it beats the streaming kernel from runs
             // of 4 heads on (the long-context shape) and at 6 (130M-shaped)
             int hg = 0, nsplit = 0;
-            scan_resident_split(d, &hg, &nsplit);
+            scan_run_split(d, 1, 1.5, &hg, &nsplit);
             const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
             chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D,
                                                                  static_cast<const bf16_t*>(z), yb, L, H, G,
                                                                  nc, hg, nsplit);
             return hipGetLastError();   // the gate, if any, is inside
         }
-        // 128-token chunks: the streaming kernel
-        const int hg = scan_heads_per_workgroup(d);
-        const unsigned blocks = (unsigned)(d.batch * nc * (d.nheads / hg));
-        chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg);
+        if (d.chunk == 64) {
+            int hg = 0, nsplit = 0;
+            scan_run_split(d, 3, 1.0, &hg, &nsplit);   // 139 VGPRs, 49 KB LDS: 3 per CU
+            const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
+            chunk_scan_q64_kernel<<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc,
+                                                              hg, nsplit);
+        } else {
+            // 128-token chunks: the streaming kernel
+            const int hg = scan_heads_per_workgroup(d);
+            const unsigned blocks = (unsigned)(d.batch * nc * (d.nheads / hg));
+            chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg);
+        }
     } else if (dtype == 1) {
         launch_generic_t<bf16_t>(d, x, B, C, cs, dtc, Hin, D, y, stream);
     } else {

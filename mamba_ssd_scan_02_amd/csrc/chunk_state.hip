@@ -740,7 +740,7 @@ static void launch_generic_t(const Dims& d, const void* x, const void* B, const 
 bool mfma_path(int32_t dtype, const Dims& d) {
     // chunk-relative y offsets of the scan kernel's buffer stores fit 31 bits
     return dtype == 1 && d.headdim == 64 && d.dstate == 128 &&
-           (d.chunk == 128 || d.chunk == 256) &&
+           (d.chunk == 64 || d.chunk == 128 || d.chunk == 256) &&
            (double)d.chunk * (double)d.nheads * (double)d.headdim * 2.0 < 2147483647.0;
 }
 
@@ -763,6 +763,7 @@ hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B,
     const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
     const int z = zoh ? 1 : 0;
     switch (d.chunk) {
+        case 64: chunk_state_mfmah_kernel<64, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
         case 128: chunk_state_mfmah_kernel<128, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
         default: chunk_state_mfmah_kernel<256, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
     }
@@ -770,7 +771,7 @@ hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B,
 }
 
 bool state_walk_applies(int32_t dtype, const Dims& d) {
-    return mfma_path(dtype, d) && (d.nheads / d.ngroups) % 2 == 0;
+    return mfma_path(dtype, d) && d.chunk >= 128 && (d.nheads / d.ngroups) % 2 == 0;
 }
 
 hipError_t launch_state_walk(const Dims& d, const void* x, const void* B, const float* cs,
@@ -799,12 +800,14 @@ hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const
         if ((d.nheads / d.ngroups) % kStateHeads == 0) {
             const unsigned hblocks = blocks / (unsigned)kStateHeads;
             switch (d.chunk) {
+                case 64: chunk_state_mfmah_kernel<64, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
                 case 128: chunk_state_mfmah_kernel<128, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
                 default: chunk_state_mfmah_kernel<256, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
             }
             return hipGetLastError();
         }
         switch (d.chunk) {
+            case 64: chunk_state_mfma_kernel<64><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
             case 128: chunk_state_mfma_kernel<128><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
             default: chunk_state_mfma_kernel<256><<<blocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc); break;
         }

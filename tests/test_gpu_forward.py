@@ -72,6 +72,16 @@ def test_mamba2_2p7b_shape():
                                  bh=sample_pairs(s.batch, s.nheads, 12, seed=3), label=s.name)
 
 
+def test_mamba2_2p7b_shape_chunk64():
+    """The 2.7B-shaped layer cut into 64-token chunks (512 per sequence): the
+    matrix-core kernels for short chunks, chunk_scan in runs of all 80 heads
+    of a chunk."""
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as s
+    inp = _spec_inputs(s)
+    _check_with_and_without_skip(inp, 64, s.dtype,
+                                 bh=sample_pairs(s.batch, s.nheads, 6, seed=4), label=s.name)
+
+
 def test_long_context_1m():
     """One 1M-token sequence, 8 groups of 4 heads (streaming chunk_scan, 4,096
     chained chunks).  Heads 0 and 31 (groups 0 and 7) plus two in between."""
@@ -123,11 +133,12 @@ def test_long_memory_f32():
     _check(inp, 64, "f32", label="long_memory_f32")
 
 
+@pytest.mark.parametrize("chunk", [256, 64])
 @pytest.mark.parametrize("L", [1, 63, 255, 257, 1000])
-def test_ragged_lengths_bf16(L):
+def test_ragged_lengths_bf16(L, chunk):
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
     inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=L, nheads=4, init_var=0.1, seed=77))
-    _check_with_and_without_skip(inp, 256, "bf16", label=f"ragged L={L}")
+    _check_with_and_without_skip(inp, chunk, "bf16", label=f"ragged L={L}")
 
 
 @pytest.mark.parametrize("chunk", [64, 128, 256])

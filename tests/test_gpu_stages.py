@@ -26,7 +26,8 @@ CASES = [
     # (name, batch, L, H, P, N, G, chunk, dtype)
     ("mfma_q256_ragged", 2, 700, 4, 64, 128, 2, 256, "bf16"),
     ("mfma_q128", 1, 512, 2, 64, 128, 1, 128, "bf16"),
-    ("bf16_q64_vector_units_ragged", 1, 333, 2, 64, 128, 2, 64, "bf16"),
+    ("mfma_q64_ragged", 1, 333, 2, 64, 128, 2, 64, "bf16"),
+    ("mfma_q64_odd_heads", 2, 700, 6, 64, 128, 2, 64, "bf16"),
     ("generic_f32", 2, 300, 3, 16, 16, 1, 64, "f32"),
     ("generic_f32_odd", 1, 77, 2, 3, 5, 1, 16, "f32"),
     ("generic_bf16", 1, 260, 2, 32, 64, 2, 128, "bf16"),
@@ -86,19 +87,21 @@ def test_stages(case):
         gate(y, y_ref, tol, what, y_mag)
 
 
+@pytest.mark.parametrize("Q", [256, 64])
 @pytest.mark.parametrize("skip", [True, False], ids=["with_D", "D_none"])
-def test_chunk_scan_head_runs(skip):
-    """128 (batch, chunk, group) units of 25 heads: the launcher gives each
-    workgroup a run of 13 or 12 heads of one chunk (on a 256-CU part), the
-    path that keeps the C.B^T tiles in registers across a run.  The first and
-    last head of both runs are checked against the oracle over every chunk,
-    including the ragged last one; with D = None the masked in-chunk product
-    and the carried state are gated at their own scale."""
+def test_chunk_scan_head_runs(skip, Q):
+    """25 heads over 32,731 tokens: with 256-token chunks (128 (batch, chunk,
+    group) units) the launcher gives each workgroup a run of 13 or 12 heads
+    of one chunk (on a 256-CU part), with 64-token chunks (512 units) one run
+    of all 25 -- the paths that keep the C.B^T tiles in registers across a
+    run.  Heads 0, 12, 13 and 24 are checked against the oracle over every
+    chunk, including the ragged last one; with D = None the masked in-chunk
+    product and the carried state are gated at their own scale."""
     import mamba_ssd_scan_02_amd as ssd
     from oracle import stages
 
-    batch, L, H, P, N, G, Q = 1, 128 * 256 - 37, 25, 64, 128, 1, 256
-    say(f"[stages] chunk_scan head runs ({'with D' if skip else 'D=None'})")
+    batch, L, H, P, N, G = 1, 128 * 256 - 37, 25, 64, 128, 1
+    say(f"[stages] chunk_scan head runs, chunk {Q} ({'with D' if skip else 'D=None'})")
     inp = _inputs(13, batch, L, H, P, N, G, "bf16")
     g = to_gpu(inp)
     cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
