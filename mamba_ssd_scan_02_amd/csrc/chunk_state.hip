@@ -252,7 +252,9 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
     }
 }
 
-// LDS of the paired-head body below.
+// LDS of the paired-head body below.  Once the last stage has been read,
+// the ring holds the heads' S tiles on their way out (stage_store_states):
+// head 0 in bsr, the others in xsr.
 template <int Q, int HG>
 struct StateSmem {
     uint4 bsr[kStateRing][512];
@@ -261,6 +263,48 @@ struct StateSmem {
     double wsum[HG][4];
     float cslast[HG];
 };
+
+// Write the HG heads' S tiles (acc[e], the MFMA result layout of
+// chunk_state_pair) as bf16 rows into LDS at st[e] (row p at 256 p, 16-byte
+// chunk k at (k ^ swz_b(p)) 16: lane pairs swap one value as in
+// store_state_bf16, so each writes a word of two adjacent columns), then
+// store them as whole 256-byte rows, 16 lanes a row: 1 KB of S per store
+// instruction instead of four 64-byte pieces, and full lines reach memory.
+// Non-temporal: S is read once, later.  Every wave must be past its last read
+// of st before the call.
+template <int HG>
+__device__ __forceinline__ void stage_store_states(const f32x16 (&acc)[HG][2], SSD_LDS char* const (&st)[HG],
+                                                   bf16_t* const (&dst)[HG], int wave, int lane) {
+    const bool odd = (lane & 1) != 0;
+    const int hf = lane >> 5;
+    const int n = 32 * wave + (lane & 31);
+    const int nb = 2 * (n & ~1);   // byte of the column pair in its row
+#pragma unroll
+    for (int e = 0; e < HG; ++e)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float h0v = acc[e][mt][r], h1v = acc[e][mt][r + 1];
+                const float got = __shfl_xor(odd ? h0v : h1v, 1, 64);
+                const float keep = odd ? h1v : h0v;
+                const int rr = odd ? r + 1 : r;
+                const int p = 32 * mt + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+                const uint32_t w = odd ? pack_bf16x2(got, keep) : pack_bf16x2(keep, got);
+                *reinterpret_cast<SSD_LDS uint32_t*>(st[e] + p * 256 + (((nb >> 4) ^ swz_b(p)) << 4) +
+                                                     (nb & 15)) = w;
+            }
+    barrier_lds();
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int k = lane & 15;
+#pragma unroll
+    for (int m = 0; m < 4 * HG; ++m) {
+        const int row = 4 * (wave + 4 * m) + (lane >> 4);   // 0 .. 64 HG - 1
+        const int e = row >> 6, p = row & 63;
+        const u32x4 v = *reinterpret_cast<const SSD_LDS u32x4*>(st[e] + p * 256 + ((k ^ swz_b(p)) << 4));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst[e] + p * 128 + 8 * k));
+    }
+}
 
 // The chunk states of HG heads of one group for one (batch, chunk): acc[e][mt]
 // = S_c of head h0 + e, p tile mt, in the MFMA result layout (lane (hf, l32)
@@ -447,11 +491,19 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     float cl[HG];
     chunk_state_pair<Q, HG, FUSE>(sm, b, c, h0, x, Bm, cs, dtc, L, H, G, nc, dtin, A, csw, dtcw, zoh,
                                   acc, cl);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    static_assert(sizeof(sm.bsr) >= P * N * 2 && sizeof(sm.xsr) >= (HG - 1) * P * N * 2,
+                  "the ring holds the S tiles");
+    bf16_t* dst[HG];
+    SSD_LDS char* st[HG];
 #pragma unroll
-    for (int e = 0; e < HG; ++e)
-        store_state_bf16(acc[e], S + (((int64_t)b * H + h0 + e) * nc + c) * (int64_t)(P * N), lane,
-                         32 * wave + (lane & 31));
+    for (int e = 0; e < HG; ++e) {
+        dst[e] = S + (((int64_t)b * H + h0 + e) * nc + c) * (int64_t)(P * N);
+        st[e] = e == 0 ? (SSD_LDS char*)lds(&sm.bsr[0][0]) : (SSD_LDS char*)lds(&sm.xsr[0][0]) + (e - 1) * P * N * 2;
+    }
+    barrier_lds();   // every wave is past its last read of the ring
+    stage_store_states<HG>(acc, st, dst, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
