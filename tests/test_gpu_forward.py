@@ -55,8 +55,8 @@ def test_tiny_f32():
 
 
 def test_mamba2_130m_shape():
-    """130M-shaped layer: 24 heads per group, so chunk_scan runs the
-    streaming kernel."""
+    """130M-shaped layer: 24 heads per group, which chunk_scan's resident
+    kernel takes in four runs of 6 heads per chunk."""
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M as s
     inp = _spec_inputs(s)
     _check_with_and_without_skip(inp, s.chunk, s.dtype,
@@ -83,13 +83,14 @@ def test_mamba2_2p7b_shape_chunk64():
 
 
 def test_long_context_1m():
-    """One 1M-token sequence, 8 groups of 4 heads (streaming chunk_scan, 4,096
-    chained chunks).  Heads 0 and 31 (groups 0 and 7) plus two in between."""
+    """One 1M-token sequence, 8 groups of 4 heads (resident chunk_scan in runs
+    of a whole group, 4,096 chained chunks).  One head of every group, at
+    every position within a group: heads 0, 5, 10, 15, 16, 21, 26 and 31."""
     from mamba_ssd_scan_02_amd.workloads import LONG_1M as s
     inp = _spec_inputs(s)
     say(f"[forward] {s.name}: inputs ready")
-    _check_with_and_without_skip(inp, s.chunk, s.dtype, bh=[(0, 0), (0, 5), (0, 18), (0, 31)],
-                                 label=s.name)
+    _check_with_and_without_skip(inp, s.chunk, s.dtype,
+                                 bh=[(0, h) for h in (0, 5, 10, 15, 16, 21, 26, 31)], label=s.name)
 
 
 # ---------------------------------------------------------------- edge cases
