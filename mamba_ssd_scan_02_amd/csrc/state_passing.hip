@@ -126,7 +126,10 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
         reinterpret_cast<uint4*>(p)[i] = make_uint4(pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3]),
                                                     pack_bf16x2(r.v[4], r.v[5]), pack_bf16x2(r.v[6], r.v[7]));
     } else if constexpr (VW == 4) {
-        reinterpret_cast<uint2*>(p)[i] = make_uint2(pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3]));
+        // the matrix-core path: Hin is read once, by chunk_scan (non-temporal
+        // stores ran the 2.7B-shaped forward 0.5% faster)
+        __builtin_nontemporal_store(u32x2{pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3])},
+                                    reinterpret_cast<u32x2*>(p) + i);
     } else if constexpr (VW == 2) {
         reinterpret_cast<uint32_t*>(p)[i] = pack_bf16x2(r.v[0], r.v[1]);
     } else {
