@@ -106,13 +106,17 @@ struct RingSlot<bf16_t, VW> {
     }
 };
 
-template <int VW>
+template <int VW, bool NT = false>
 __device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r) {
     if constexpr (VW >= 4) {
 #pragma unroll
-        for (int q = 0; q < VW / 4; ++q)
-            reinterpret_cast<float4*>(p)[i * (VW / 4) + q] =
-                make_float4(r.v[4 * q], r.v[4 * q + 1], r.v[4 * q + 2], r.v[4 * q + 3]);
+        for (int q = 0; q < VW / 4; ++q) {
+            const f32x4 w = {r.v[4 * q], r.v[4 * q + 1], r.v[4 * q + 2], r.v[4 * q + 3]};
+            if constexpr (NT)
+                __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p) + i * (VW / 4) + q);
+            else
+                reinterpret_cast<f32x4*>(p)[i * (VW / 4) + q] = w;
+        }
     } else if constexpr (VW == 2) {
         reinterpret_cast<float2*>(p)[i] = make_float2(r.v[0], r.v[1]);
     } else {
@@ -120,16 +124,19 @@ __device__ __forceinline__ void store_vec(float* p, int64_t i, const Vec<VW>& r)
     }
 }
 
-template <int VW>
+// NT: non-temporal stores, for an Hin too large to stay in the last-level
+// cache until chunk_scan reads it (see launch_sp).
+template <int VW, bool NT = false>
 __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r) {
     if constexpr (VW == 8) {
         reinterpret_cast<uint4*>(p)[i] = make_uint4(pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3]),
                                                     pack_bf16x2(r.v[4], r.v[5]), pack_bf16x2(r.v[6], r.v[7]));
     } else if constexpr (VW == 4) {
-        // the matrix-core path: Hin is read once, by chunk_scan (non-temporal
-        // stores ran the 2.7B-shaped forward 0.5% faster)
-        __builtin_nontemporal_store(u32x2{pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3])},
-                                    reinterpret_cast<u32x2*>(p) + i);
+        const u32x2 w = {pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3])};
+        if constexpr (NT)
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p) + i);
+        else
+            reinterpret_cast<u32x2*>(p)[i] = w;
     } else if constexpr (VW == 2) {
         reinterpret_cast<uint32_t*>(p)[i] = pack_bf16x2(r.v[0], r.v[1]);
     } else {
@@ -141,7 +148,8 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
 //     [store h at hp], h <- exp2(lg_c) h + S_c,   c = 0 .. n - 1,
 // where S_c sits at src + c * sstep (elements of ST) and lg_c, the chunk's decay in
 // log2 units, at dec[c * dstep].  kStore writes the entering state of every
-// chunk (hp advances by sstep); kSum adds the lg_c into *lsum.
+// chunk (hp advances by sstep), non-temporally with kNT; kSum adds the lg_c
+// into *lsum.
 //
 // The ring holds the next PF chunks.  Its loads are unconditional: a load past
 // the last chunk re-reads the last chunk (always in bounds) and is never used.
@@ -149,7 +157,7 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
 // beyond the group; the last 1..PF chunks run from the ring with no further
 // loads.  (A load or store under a branch makes the compiler wait for the
 // ring's loads at the join, which serialises it.)
-template <typename ST, typename HT, int PF, int VW, bool kStore, bool kSum>
+template <typename ST, typename HT, int PF, int VW, bool kStore, bool kSum, bool kNT = false>
 __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t sstep,
                                             const float* __restrict__ dec, int64_t dstep, int n,
                                             HT* hp, Vec<VW>& h, float* lsum) {
@@ -172,7 +180,7 @@ __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t 
             const float a = fast_exp2(lg[k]);
             if (kSum) ls += lg[k];
             if (kStore) {
-                store_vec<VW>(hp, 0, h);
+                store_vec<VW, kNT>(hp, 0, h);
                 hp += sstep;
             }
             const Vec<VW> sv = buf[k].widen();
@@ -190,7 +198,7 @@ __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t 
             const float a = fast_exp2(lg[k]);
             if (kSum) ls += lg[k];
             if (kStore) {
-                store_vec<VW>(hp, 0, h);
+                store_vec<VW, kNT>(hp, 0, h);
                 hp += sstep;
             }
             const Vec<VW> sv = buf[k].widen();
@@ -216,7 +224,7 @@ __device__ __forceinline__ Vec<VW> start_state(const float* init, int64_t idx) {
 // Element indices below are in units of VW floats; pnv = P N / VW.  Grids put
 // (batch, head) on x, so the decays are uniform across a workgroup and come
 // from scalar loads, off the vector memory counter that paces the S ring.
-template <typename HT, int PF, int VW>
+template <typename HT, int PF, int VW, bool NT>
 __global__ __launch_bounds__(256) void state_passing_kernel(const HT* __restrict__ S,
                                                             const float* __restrict__ cs,
                                                             const float* init, HT* __restrict__ Hin,
@@ -227,8 +235,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const HT* __restrict
     const int64_t idx = bh * pnv + off;
     Vec<VW> h = start_state<VW>(init, idx);
     const int64_t base = (bh * nc * (int64_t)pnv + off) * VW;
-    walk_chunks<HT, HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW, cs + bh * nc * (int64_t)Q + (Q - 1),
-                                             Q, nc, Hin + base, h, nullptr);
+    walk_chunks<HT, HT, PF, VW, true, false, NT>(S + base, (int64_t)pnv * VW,
+                                                 cs + bh * nc * (int64_t)Q + (Q - 1), Q, nc, Hin + base, h,
+                                                 nullptr);
     if (fin) store_vec<VW>(fin, idx, h);
 }
 
@@ -303,13 +312,30 @@ __global__ __launch_bounds__(256) void sp_seg_down_kernel(const HT* __restrict__
                                              h, nullptr);
 }
 
+constexpr double kHinTemporalMaxBytes = 64.0 * 1024 * 1024;
+
 template <typename HT, int PF, int VW>
 static void launch_sp_vw(const Dims& d, const void* S, const float* cs, const float* init,
                          void* Hin, float* fin, hipStream_t stream) {
     const int pnv = (int)(d.headdim * d.dstate / VW);
     const dim3 grid((unsigned)(d.batch * d.nheads), (unsigned)((pnv + 255) / 256));
-    state_passing_kernel<HT, PF, VW><<<grid, 256, 0, stream>>>(
-        static_cast<const HT*>(S), cs, init, reinterpret_cast<HT*>(Hin), fin, pnv, (int)d.nchunks, (int)d.chunk);
+    // Hin is read once, by chunk_scan.  Where it fits well inside the 256 MB
+    // last-level cache, ordinary stores leave it there for that read (the
+    // 130M-shaped forward, 25 MB: 65.9 us against 67.1 with non-temporal
+    // stores on one box, equal on another); beyond, non-temporal stores
+    // write it back during state passing instead of during chunk_scan (2.7B
+    // shape, 168 MB: state passing 61 -> 70 us, chunk_scan 205 -> 197 us,
+    // the forward within 1% either way).
+    const double hin_bytes = (double)d.batch * (double)d.nheads * (double)d.nchunks *
+                             (double)(d.headdim * d.dstate) * (double)sizeof(HT);
+    const HT* s = static_cast<const HT*>(S);
+    HT* h = reinterpret_cast<HT*>(Hin);
+    if (hin_bytes > kHinTemporalMaxBytes)
+        state_passing_kernel<HT, PF, VW, true><<<grid, 256, 0, stream>>>(s, cs, init, h, fin, pnv,
+                                                                         (int)d.nchunks, (int)d.chunk);
+    else
+        state_passing_kernel<HT, PF, VW, false><<<grid, 256, 0, stream>>>(s, cs, init, h, fin, pnv,
+                                                                          (int)d.nchunks, (int)d.chunk);
 }
 
 // Four elements per thread where P * N allows (measured best at the
