@@ -31,20 +31,16 @@
 //   * Y^T += X^T G~^T (M = P rows in two 32-row tiles, K = 32 tokens).  A-row m
 //     reads channel sigma(m) so that a lane ends with 16 consecutive channels
 //     of its token: two 16-byte stores per tile.
-//   * Term (ii) first: Y^T = Hin C^T (K = N), then each column scaled by
-//     exp2(cs_i).
-// Three kernels share these steps:
-//   * the streaming kernel (Q = 128, one workgroup of 2 waves per (batch,
-//     chunk, run of heads)): wave w owns i tiles
-//     {w, 2W-1-w} so that every wave has the same number of causal (j <= i)
-//     tiles; C fragments of the wave's own tokens stay in registers; the
-//     carried state and the j blocks of B (32 rows) and x (32 rows) are
-//     copied straight into LDS (lds_pipe.h) through a 3-buffer ring, two
-//     blocks ahead, and x is read back transposed with tr16;
-//   * the resident kernels (Q = 256 and Q = 64, runs of heads sharing one
-//     B/C group): G^T does not depend on the head, so it is formed once per
-//     chunk and kept in registers across the run (see their own
-//     descriptions below).
+//   * Term (ii): Y^T += Hin C^T (K = N), scaled per column by exp2(cs_i)
+//     (or exp2 of the tile's reference, in the factorised form).
+// Two kernels take these steps, both for runs of heads sharing one B/C group
+// and both copying each head's x rows, carried state and cs/dt rows straight
+// into LDS (lds_pipe.h) one head ahead: G^T does not depend on the head, so
+// it is formed once per chunk and kept in registers across the run.
+//   * the paired kernel (Q = 256): 8 waves, two per SIMD, the chunk's 36
+//     blocks split over pairs of waves (see its own description below);
+//   * the short-chunk kernel (Q = 64 or 128): Q / 16 waves, one output tile
+//     and half the channels each, direct weights.
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
@@ -97,27 +93,11 @@ __device__ __forceinline__ float uniform_f(float v) {
 // j = 16*(r/8) + 8*hf + r%8 and column (output token) i = l32.
 __host__ __device__ constexpr int gt_row(int r, int hf) { return 16 * (r >> 3) + 8 * hf + (r & 7); }
 
-// Causal keep bits of the diagonal block for this lane (direct form).
-__device__ __forceinline__ uint32_t diag_keep_bits(int l32, int hf) {
-    const int t = l32 - 8 * hf;
-    const int n0 = min(max(t + 1, 0), 8), n1 = min(max(t - 15, 0), 8);
-    return ((1u << n0) - 1u) | (((1u << n1) - 1u) << 8);
-}
-
-// Bit r set iff accumulator register r of this lane is the diagonal entry
-// j == i of the diagonal block (at most one per lane; direct form).
-__device__ __forceinline__ uint32_t diag_eq_bits(int l32, int hf) {
-    const int t = l32 - 8 * hf;
-    if (t >= 0 && t < 8) return 1u << t;
-    if (t >= 16 && t < 24) return 1u << (t - 8);
-    return 0u;
-}
-
-// The same two sets as lane masks of one register r of a diagonal block,
-// constant for every wave (register r holds j - 8 hf = 16 (r / 8) + r % 8
-// of column i = l32): j <= i holds in lanes l32 >= jr of the first half
-// and l32 >= jr + 8 of the second; j == i in lanes r and 40 + r (r < 8) or
-// r + 8 and 48 + r (r >= 8).
+// The causal set j <= i and the diagonal j == i of a diagonal block as lane
+// masks of one register r, constant for every wave (register r holds
+// j - 8 hf = 16 (r / 8) + r % 8 of column i = l32): j <= i holds in lanes
+// l32 >= jr of the first half and l32 >= jr + 8 of the second; j == i in
+// lanes r and 40 + r (r < 8) or r + 8 and 48 + r (r >= 8).
 __host__ __device__ constexpr uint64_t diag_keep_lanes(int r) {
     return ((0xffffffffull << (16 * (r >> 3) + (r & 7))) & 0xffffffffull) |
            (((0xffffffffull << (16 * (r >> 3) + (r & 7) + 8)) & 0xffffffffull) << 32);
@@ -155,22 +135,6 @@ __device__ __forceinline__ void mask_causal(f32x16& a, int l32, int hf) {
     for (int r = 0; r < 16; ++r) a[r] = l32 >= gt_row(r, hf) ? a[r] : 0.0f;
 }
 
-// C fragments of the wave's own tokens (B operand of both C products).
-// Tokens past the end of the sequence re-read the last token: C_i only
-// reaches output column i, which is not stored for those tokens.
-__device__ __forceinline__ void load_c_frags(uint4 (&cf)[2][8], const bf16_t* Cm, int64_t b, int L,
-                                             int G, int g, int tok0, const int (&it_)[2], int hf,
-                                             int l32) {
-    constexpr int N = 128;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int tok = min(tok0 + 32 * it_[t] + l32, L - 1);
-        const bf16_t* crow = Cm + ((b * L + tok) * G + g) * N + 8 * hf;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) cf[t][kk] = *reinterpret_cast<const uint4*>(crow + 16 * kk);
-    }
-}
-
 // Per-tile factors.  With the factorised form (fact), tile t's weights are
 // exp2(cs_i - cs_j) dt_j = colf_i * rf_j, colf_i = exp2(cs_i - cref) and
 // rf_j = exp2(cref - cs_j) dt_j with cref = cs of the tile's first token:
@@ -184,399 +148,6 @@ struct TileF {
     float sstate;   // scale of the state term
     float dprime;   // D / colf_i, the diagonal addend of the factorised form
 };
-
-// (ii) carried state: acc[t][mt] = sstate_t * sum_n Hin[p][n] C[i][n].
-__device__ __forceinline__ void scan_state_term(f32x16 (&acc)[2][2], const uint4* hs,
-                                                const uint4 (&cf)[2][8], const TileF (&tf)[2],
-                                                int hf, int l32) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[t][mt] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int pr = 32 * mt + perm_sigma(l32);
-            const int ch = 2 * kk + hf;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, hs[pr * 16 + (ch ^ swz_h(pr))]);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                acc[t][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, cf[t][kk]), acc[t][mt], 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][mt][r] *= tf[t].sstate;
-}
-
-// (i) + (iii) for j block jt: G^T tiles from the B block, decay weights
-// (+ D on the diagonal), then Y^T += X^T G~^T.
-template <int Q>
-__device__ __forceinline__ void scan_block(f32x16 (&acc)[2][2], int jt, const uint4* bst,
-                                           const uint4* xst, const float* cs_s, const float* dt_s,
-                                           const float* rfT, const uint4 (&cf)[2][8],
-                                           const float (&csi)[2], const int (&it_)[2],
-                                           const TileF (&tf)[2], float Dh, XtAddr xa, int hf,
-                                           int l32, uint32_t diag_keep, uint32_t diag_eq) {
-    if (it_[1] < jt) return;   // it_[1] >= it_[0]: nothing left for this wave
-    const bool act0 = it_[0] >= jt;
-    // G^T tiles.  The branch sits outside the K loop, and the B-row reads
-    // run two steps ahead of the products (the scheduler, short of
-    // registers, would otherwise wait out each read's latency in turn).
-    f32x16 gacc[2];
-    {
-        const int jr = perm_pi(l32);
-        const uint4* brow = bst + jr * 16;
-        const int sw = swz_b(jr);
-        bf16x8 bq[2];
-        bq[0] = __builtin_bit_cast(bf16x8, brow[hf ^ sw]);
-        bq[1] = __builtin_bit_cast(bf16x8, brow[(2 + hf) ^ sw]);
-        if (act0) {
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 cur = bq[kk & 1];
-                if (kk + 2 < 8) bq[kk & 1] = __builtin_bit_cast(bf16x8, brow[(2 * (kk + 2) + hf) ^ sw]);
-                gacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, cf[0][kk]), kk ? gacc[0] : f32x16{}, 0, 0, 0);
-                gacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, cf[1][kk]), kk ? gacc[1] : f32x16{}, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 cur = bq[kk & 1];
-                if (kk + 2 < 8) bq[kk & 1] = __builtin_bit_cast(bf16x8, brow[(2 * (kk + 2) + hf) ^ sw]);
-                gacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, cf[1][kk]), kk ? gacc[1] : f32x16{}, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    }
-    const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        if (t == 0 && !act0) continue;
-        uint32_t pk[8];
-        const bool dgb = it_[t] == jt;
-        if (tf[t].fact) {
-            // rf_j of this tile's reference for the lane's 16 block tokens
-            const float* rfb = rfT + it_[t] * Q + 32 * jt + 8 * hf;
-            const float4 f0 = *reinterpret_cast<const float4*>(rfb);
-            const float4 f1 = *reinterpret_cast<const float4*>(rfb + 4);
-            const float4 f2 = *reinterpret_cast<const float4*>(rfb + 16);
-            const float4 f3 = *reinterpret_cast<const float4*>(rfb + 20);
-            const float rf[16] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w,
-                                  f2.x, f2.y, f2.z, f2.w, f3.x, f3.y, f3.z, f3.w};
-            if (!dgb) {
-#pragma unroll
-                for (int r2 = 0; r2 < 8; ++r2)
-                    pk[r2] = pack_bf16x2(gacc[t][2 * r2] * rf[2 * r2], gacc[t][2 * r2 + 1] * rf[2 * r2 + 1]);
-            } else {
-                // causal mask j <= i and D on j == i, selects on constant
-                // lane masks
-                float v[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float w = lane_select(0.0f, gacc[t][r] * rf[r], diag_keep_lanes(r));
-                    v[r] = lane_select(w, w + tf[t].dprime, diag_eq_lanes(r));
-                }
-#pragma unroll
-                for (int r2 = 0; r2 < 8; ++r2) pk[r2] = pack_bf16x2(v[2 * r2], v[2 * r2 + 1]);
-            }
-        } else {
-            // direct weights for a tile with too much decay to factorise
-            const float* csb = cs_s + 32 * jt + 8 * hf;
-            const float* dtb = dt_s + 32 * jt + 8 * hf;
-            const uint32_t keep = dgb ? diag_keep : 0xffffu;
-            const uint32_t deq = dgb ? diag_eq : 0u;
-#pragma unroll
-            for (int r2 = 0; r2 < 8; ++r2) {
-                float v2[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = 2 * r2 + e;
-                    const int jl = 16 * (r >> 3) + (r & 7);
-                    const float kf = (float)((keep >> r) & 1u);
-                    const float df = (float)((deq >> r) & 1u);
-                    v2[e] = gacc[t][r] * (fast_exp2(fminf(csi[t] - csb[jl], 0.0f)) * dtb[jl] * kf) + Dh * df;
-                }
-                pk[r2] = pack_bf16x2(v2[0], v2[1]);
-            }
-        }
-        const bf16x8 gq[2] = {__builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3])),
-                              __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]))};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int pc = 32 * mt + xa.qb;          // multiple of 4
-            const int chk = pc >> 3, sub = (pc & 7) * 2;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r0 = 16 * u + xa.trow0, r1 = r0 + 4;
-                const uint2 lo = tr16(xb + r0 * 128 + ((chk ^ swz_x(r0)) << 4) + sub);
-                const uint2 hi = tr16(xb + r1 * 128 + ((chk ^ swz_x(r1)) << 4) + sub);
-                const bf16x8 xq = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                acc[t][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, gq[u], acc[t][mt], 0, 0, 0);
-            }
-        }
-    }
-}
-
-// y rows of the wave's own tokens: lane owns token i, channels
-// 32*mt + 16*hf + 0..15 (two 16-byte stores per tile), after the final
-// column scale.  Buffer stores against a record bounded by the sequence end:
-// every wave always issues its 8 stores (fixed memory-counter arithmetic),
-// and the hardware drops those of tokens past the end.
-__device__ __forceinline__ void scan_store_y(const f32x16 (&acc)[2][2], const TileF (&tf)[2],
-                                             __amdgpu_buffer_rsrc_t yrs, int rowbytes,
-                                             const int (&it_)[2], int hf, int l32) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int off = (32 * it_[t] + l32) * rowbytes + 32 * hf;
-        const float s = tf[t].colf;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            uint32_t w8[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) w8[k] = pack_bf16x2(acc[t][mt][2 * k] * s, acc[t][mt][2 * k + 1] * s);
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 v0 = {w8[0], w8[1], w8[2], w8[3]};
-            const u32x4 v1 = {w8[4], w8[5], w8[6], w8[7]};
-            __builtin_amdgcn_raw_buffer_store_b128(v0, yrs, off + 64 * mt, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(v1, yrs, off + 64 * mt + 16, 0, 0);
-        }
-    }
-}
-
-// Pipeline buffer k of a 4-deep ring (compile-time k after unrolling).
-template <typename T>
-__device__ __forceinline__ T* ring4(int k, T* a0, T* a1, T* a2, T* a3) {
-    const int m = k & 3;
-    return m == 0 ? a0 : (m == 1 ? a1 : (m == 2 ? a2 : a3));
-}
-
-// Memory operations a wave issues at loop step k of a head (stage k + 3 of
-// this head or of the next, and at k = 0 the next head's carried state and
-// cs/dt rows).
-__host__ __device__ constexpr int scan_issue_ops(int NT, int k, bool more, int DPS, int DH, int DC) {
-    return (k + 3 < NT ? DPS : (more ? DPS : 0)) + (k == 0 && more ? DH + DC : 0);
-}
-// Operations issued after stage jt of the current head and before the wait
-// at step jt: stages 0..2 came at the end of the previous head, followed by
-// its NY y stores.
-__host__ __device__ constexpr int scan_ops_after(int NT, int jt, bool more, int DPS, int DH, int DC,
-                                                 int NY) {
-    int n = 0;
-    if (jt <= 2) {
-        n = (2 - jt) * DPS + NY;
-        for (int k = 0; k < jt; ++k) n += scan_issue_ops(NT, k, more, DPS, DH, DC);
-    } else {
-        n = (jt == 3 && more) ? DH + DC : 0;   // issued right after stage 3
-        for (int k = jt - 2; k < jt; ++k) n += scan_issue_ops(NT, k, more, DPS, DH, DC);
-    }
-    return n;
-}
-
-// The streaming kernel's issue order for a run of hg heads (labels: stage s
-// of head h, carried state, cs/dt rows, y stores), replayed against the
-// counts above: each step's stage, and before the next head its carried
-// state and rows, must have landed.
-constexpr bool scan_waits_hold(int NT, int W, int hg) {
-    const int DPS = 12 / W, DH = 16 / W, DC = 2, NY = 8;
-    auto stage = [](int h, int s) { return 1000 + 16 * h + s; };
-    auto hin = [](int h) { return 2000 + h; };
-    auto rows = [](int h) { return 3000 + h; };
-    VmemLog o;
-    o.push(rows(0), DC);
-    o.push(hin(0), DH);
-    for (int s = 0; s < 3; ++s) o.push(stage(0, s), DPS);
-    if (!o.wait(0)) return false;
-    for (int hi = 0; hi < hg; ++hi) {
-        const bool more = hi + 1 < hg;
-        for (int jt = 0; jt < NT; ++jt) {
-            if (!o.wait(scan_ops_after(NT, jt, more, DPS, DH, DC, NY)) || !o.landed(stage(hi, jt))) return false;
-            if (jt + 3 < NT) o.push(stage(hi, jt + 3), DPS);
-            else if (more) o.push(stage(hi + 1, jt + 3 - NT), DPS);
-            if (jt == 0 && more) {
-                o.push(hin(hi + 1), DH);
-                o.push(rows(hi + 1), DC);
-            }
-        }
-        o.push(4000 + hi, NY);
-        if (more && (!o.wait((NT - 1) * DPS + NY) || !o.landed(hin(hi + 1)) || !o.landed(rows(hi + 1))))
-            return false;
-    }
-    return true;
-}
-static_assert(scan_waits_hold(8, 4, 1) && scan_waits_hold(8, 4, 2) && scan_waits_hold(8, 4, 5) &&
-              scan_waits_hold(4, 2, 1) && scan_waits_hold(4, 2, 2) && scan_waits_hold(4, 2, 5),
-              "chunk_scan wait counts do not cover its copies");
-
-// ---------------------------------------------------------------------------
-// One workgroup per (batch, chunk, run of hg heads of one group).  The heads
-// share C, so the C fragments are loaded once; everything a head needs
-// besides (its carried state, cs/dt rows, x) streams in while the previous
-// head computes:
-//   per wave and head, in issue order (Q = 256: 4 waves, 3 copies a stage):
-//     jt = 0: stage 3, Hin(next) x4, cs/dt(next) x2
-//     jt = 1..4: stages 4..7;  jt = 5..7: stages 0..2 of the next head
-//     end: 8 y stores
-// and the wait before block jt leaves exactly the operations issued after
-// stage jt outstanding (fewer on the last head, which prefetches nothing).
-template <int Q>
-__global__ __launch_bounds__(Q, 2) void chunk_scan_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
-    const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
-    const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg) {
-    constexpr int P = 64, N = 128, W = Q / 64, NT = Q / 32;
-    static_assert(NT % 4 == 0, "the ring index must repeat every head");
-    constexpr int DPS = 12 / W;      // LDS-copy instructions per wave per stage
-    constexpr int DH = 16 / W;       // ... for the carried state
-    constexpr int DC = 2;            // ... for the cs and dt rows
-    constexpr int NY = 8;            // y stores per wave
-    // One array per copy target in flight (the compiler tracks a few LDS
-    // copy targets separately and waits for all copies beyond that).
-    __shared__ uint4 hs[1024];                              // Hin, 64 rows x 256 B
-    __shared__ uint4 st0[768], st1[768], st2[768], st3[768];   // stages: B 32 x 256 B, x 32 x 128 B
-    __shared__ float csdt_n[2 * Q];                         // next head's cs and dt rows
-    __shared__ float cs_s[Q];                               // current head's
-    __shared__ float dt_s[Q];
-    __shared__ __align__(16) float rfT[NT * Q];             // rf_j per output tile
-
-    const int ngr = H / hg;
-    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int hgi = (int)(wg % (uint32_t)ngr);
-    const int bc = (int)(wg / (uint32_t)ngr);
-    const int c = bc % nc, b = bc / nc;
-    const int h0 = hgi * hg;
-    const int g = h0 / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hf = lane >> 5, l32 = lane & 31;
-    const int tok0 = c * Q;
-    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
-    const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
-    const int rowbytes = H * P * 2;
-    // end of the chunk's last valid row (within the chunk: Q rows of a
-    // token row's bytes fit 31 bits)
-    const int yrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
-
-    // Copies for head h0: cs/dt rows, the carried state, stages 0..2.
-    auto issue_csdt = [&](int h) {
-        const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-        dma4(cs + row, 4u * (uint32_t)tid, lds(csdt_n) + 64 * wave);
-        dma4(dtc + row, 4u * (uint32_t)tid, lds(csdt_n) + Q + 64 * wave);
-    };
-    // per-lane copy offsets, fixed for the whole workgroup
-    const BxOffsets<W> bxo = bx_offsets<W>(wave, lane, xstride, bstride);
-    uint32_t hoff[DH];
-#pragma unroll
-    for (int i = 0; i < DH; ++i) {
-        const int r = 4 * (wave + i * W) + (lane >> 4);
-        hoff[i] = (uint32_t)(r * N + 8 * ((lane & 15) ^ swz_h(r))) * 2u;
-    }
-    auto issue_hin = [&](int h) {
-        const bf16_t* hsrc = Hin + ((((int64_t)b * H + h) * nc + c) * (int64_t)(P * N));
-#pragma unroll
-        for (int i = 0; i < DH; ++i) dma16(hsrc, hoff[i], lds(hs) + (wave + i * W) * 64);
-    };
-    auto issue_stage = [&](int h, int s, uint4* bst, uint4* xst) {
-        const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
-        issue_bx_stage<W>(wave, lane, tok0 + 32 * s, L, xbase, xstride, bbase, bstride, bxo, bst, xst);
-    };
-    // rf table and current cs/dt rows from the copied next-head rows.
-    auto make_tables = [&]() {
-        const float cv = csdt_n[tid], dv = csdt_n[Q + tid];
-        cs_s[tid] = cv;
-        dt_s[tid] = dv;
-#pragma unroll
-        for (int k = 0; k < NT; ++k)
-            if (k >= (tid >> 5)) rfT[k * Q + tid] = fast_exp2(fminf(csdt_n[32 * k] - cv, kMaxTileDecayLog2)) * dv;
-    };
-
-    issue_csdt(h0);
-    issue_hin(h0);
-    issue_stage(h0, 0, st0, st0 + 512);
-    issue_stage(h0, 1, st1, st1 + 512);
-    issue_stage(h0, 2, st2, st2 + 512);
-    const int it_[2] = {wave, 2 * W - 1 - wave};
-    uint4 cf[2][8];
-    load_c_frags(cf, Cm, b, L, G, g, tok0, it_, hf, l32);
-    wait_vmcnt<0>();
-    barrier_lds();
-    make_tables();
-    barrier_lds();
-
-    for (int hi = 0; hi < hg; ++hi) {
-        const int h = h0 + hi;
-        // Lane-dependent values are re-derived every head: laundering the
-        // lane index keeps the compiler from hoisting every LDS address of
-        // the unrolled block loop out of the head loop (which costs far more
-        // registers than recomputing them).
-        int lane_o = lane;
-        asm volatile("" : "+v"(lane_o));
-        const int hf_o = lane_o >> 5, l32_o = lane_o & 31;
-        const XtAddr xa = xt_addr(lane_o);
-        const uint32_t dkeep = diag_keep_bits(l32_o, hf_o);
-        const uint32_t deq = diag_eq_bits(l32_o, hf_o);
-        const bool more = hi + 1 < hg;
-        const float Dh = D ? D[h] : 0.0f;
-        float csi[2];
-        TileF tf[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int i0 = 32 * it_[t];
-            const float cref = cs_s[i0];
-            csi[t] = cs_s[i0 + l32_o];
-            tf[t].fact = uniform_f(cref - cs_s[i0 + 31]) <= kMaxTileDecayLog2;
-            if (tf[t].fact) {
-                tf[t].colf = fast_exp2(csi[t] - cref);
-                tf[t].sstate = fast_exp2(cref);
-                tf[t].dprime = Dh * fast_exp2(cref - csi[t]);
-            } else {
-                tf[t].colf = 1.0f;
-                tf[t].sstate = fast_exp2(csi[t]);
-                tf[t].dprime = 0.0f;
-            }
-        }
-        f32x16 acc[2][2];
-        scan_state_term(acc, hs, cf, tf, hf_o, l32_o);
-
-#pragma unroll
-        for (int jt = 0; jt < NT; ++jt) {
-            // stage jt has landed once only the operations issued after it
-            // are outstanding (the first head's stages 0..2 were waited for
-            // in full before the loop)
-            if (more) wait_vmcnt_n(scan_ops_after(NT, jt, true, DPS, DH, DC, NY));
-            else wait_vmcnt_n(scan_ops_after(NT, jt, false, DPS, DH, DC, NY));
-            barrier_lds();
-            uint4* nst = ring4(jt + 3, st0, st1, st2, st3);
-            if (jt + 3 < NT) {
-                issue_stage(h, jt + 3, nst, nst + 512);
-            } else if (more) {
-                issue_stage(h + 1, jt + 3 - NT, nst, nst + 512);
-            }
-            if (jt == 0 && more) {
-                issue_hin(h + 1);
-                issue_csdt(h + 1);
-            }
-            uint4* cst = ring4(jt, st0, st1, st2, st3);
-            scan_block<Q>(acc, jt, cst, cst + 512, cs_s,
-                          dt_s, rfT, cf, csi, it_, tf, Dh, xa, hf_o, l32_o, dkeep, deq);
-        }
-        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
-            y + (((int64_t)b * L + tok0) * H + h) * P, (short)0, yrecord, 0x00020000);
-        scan_store_y(acc, tf, yrs, rowbytes, it_, hf_o, l32_o);
-        if (more) {
-            // the next head's carried state and cs/dt rows (issued at step 0)
-            wait_vmcnt_n((NT - 1) * DPS + NY);
-            barrier_lds();
-            make_tables();
-            barrier_lds();
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Pieces of the resident kernel below (Q = 256): per-slot LDS operands, the
@@ -1074,36 +645,73 @@ __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 64-token chunks: one workgroup of 4 waves per (batch, chunk, group, run of
-// heads), three workgroups per CU.  The chunk's three causal 32 x 32 blocks of
-// G^T = B C^T do not depend on the head: they are formed once per run and
+// Short chunks (Q = 64 or 128): one workgroup of W = Q / 16 waves per (batch,
+// chunk, group, run of heads).  The chunk's causal 32 x 32 blocks of G^T =
+// B C^T (3 or 10) do not depend on the head: they are formed once per run and
 // stay in registers.  Wave w owns output tile t = w / 2 (tokens 32 t ..
 // 32 t + 31) for channels 32 (w % 2) .. + 31, so the two waves of a tile both
-// form its blocks (one for tile 0, two for tile 1).  A head's x rows (8 KB),
-// carried state (16 KB) and cs/dt rows are copied into one of two LDS slots
-// one head ahead.  Every weight is formed directly, exp2(cs_i - cs_j) dt_j
-// per element (within 64 tokens the factorised form saves little), and the
-// state term is scaled by exp2(cs_i).  Each lane stores 16 consecutive
-// channels of its token (two 16-byte stores); tokens past the end fall
-// outside the y record and are dropped.
-namespace q64 {
-constexpr int kX = 0;          // x: 64 rows x 128 B
-constexpr int kH = 8192;       // Hin: 64 rows x 256 B
-constexpr int kCs = 24576;     // cs: 64 floats
-constexpr int kDt = 24832;     // dt: 64 floats
-constexpr int kSlot = 25088;
-constexpr int kBytes = 2 * kSlot;
-static_assert(kSlot % 16 == 0 && 2 * kBytes <= 160 * 1024, "chunk_scan (64-token chunks) LDS");
-}  // namespace q64
+// form its t + 1 blocks.  A head's x rows (Q x 128 B), carried state (16 KB)
+// and cs/dt rows are copied into one of two LDS slots one head ahead.  Every
+// weight is formed directly, exp2(cs_i - cs_j) dt_j per element (over so few
+// tokens the factorised form saves little), and the state term is scaled by
+// exp2(cs_i).  Each lane stores 16 consecutive channels of its token (two
+// 16-byte stores); tokens past the end fall outside the y record and are
+// dropped.  SLOTS LDS slots keep SLOTS - 1 heads' copies in flight.
+template <int Q, int SLOTS>
+struct ShortScan {
+    static constexpr int NT = Q / 32;          // output tiles
+    static constexpr int W = 2 * NT;           // waves
+    static constexpr int kX = 0;               // x: Q rows x 128 B
+    static constexpr int kH = Q * 128;         // Hin: 64 rows x 256 B
+    static constexpr int kCs = kH + 16384;     // cs: Q floats
+    static constexpr int kDt = kCs + 4 * Q;    // dt: Q floats
+    static constexpr int kSlot = kDt + 4 * Q;
+    static constexpr int kBytes = SLOTS * kSlot;
+    static constexpr int kHinCopies = 16 / W;  // 1 KB Hin pieces per wave
+    static constexpr int kRowCopies = Q / 32;  // 256-byte cs/dt pieces, one per wave
+    static constexpr int kStores = 2;          // y stores per wave and head
+    static_assert(kSlot % 16 == 0 && kBytes <= 160 * 1024 && kRowCopies <= W, "short-chunk chunk_scan LDS");
+};
 
-__global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
+// Operations a wave issued after head k's copies when it waits for them at
+// the top of head k (copies: per head, c of them; the issue order is the
+// copies of heads 0 .. SLOTS - 2, then per head j: the copies of head
+// j + SLOTS - 1, head j's y stores): the copies of the heads after k already
+// issued and the y stores of the heads since head k's copies.
+__host__ __device__ constexpr int short_ops_after(int slots, int c, int cnt, int k) {
+    int n = 0;
+    for (int i = k + 1; i <= k + slots - 2 && i < cnt; ++i) n += c;
+    for (int j = (k - slots + 1 > 0 ? k - slots + 1 : 0); j < k; ++j) n += 2;
+    return n;
+}
+constexpr bool short_waits_hold(int slots, int c, int cnt) {
+    VmemLog o;
+    for (int i = 0; i < slots - 1 && i < cnt; ++i) o.push(100 + i, c);
+    for (int k = 0; k < cnt; ++k) {
+        if (!o.wait(short_ops_after(slots, c, cnt, k)) || !o.landed(100 + k)) return false;
+        if (k + slots - 1 < cnt) o.push(100 + k + slots - 1, c);
+        o.push(500 + k, 2);
+    }
+    return true;
+}
+constexpr bool short_waits_hold_all() {
+    for (int slots = 2; slots <= 4; ++slots)
+        for (int c = 4; c <= 7; ++c)
+            for (int cnt = 1; cnt <= 9; ++cnt)
+                if (!short_waits_hold(slots, c, cnt)) return false;
+    return true;
+}
+static_assert(short_waits_hold_all(), "short-chunk chunk_scan wait counts do not cover its copies");
+
+template <int Q, int SLOTS>
+__global__ __launch_bounds__(Q * 4, Q == 64 ? 2 : 1) void chunk_scan_short_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
     const float* __restrict__ D, bf16_t* __restrict__ y, int L, int H, int G, int nc, int hg,
     int nsplit) {
-    using namespace q64;
-    constexpr int Q = 64, P = 64, N = 128;
-    __shared__ __align__(16) char smem[kBytes];
+    using K = ShortScan<Q, SLOTS>;
+    constexpr int P = 64, N = 128, NT = K::NT, W = K::W;
+    __shared__ __align__(16) char smem[K::kBytes];
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = (int)(wg % (uint32_t)nsplit);
     const uint32_t bcg = wg / (uint32_t)nsplit;
@@ -1115,7 +723,7 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
     const int cnt = min(hg, hpg - split * hg);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    __builtin_assume(wave >= 0 && wave < 4);
+    __builtin_assume(wave >= 0 && wave < W);
     const int t = wave >> 1, mt = wave & 1;
     const int hf = lane >> 5, l32 = lane & 31;
     const int tok0 = c * Q;
@@ -1124,35 +732,40 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
     const int xrecord = (min(L - tok0, Q) - 1) * rowbytes + P * 2;
     SSD_LDS char* const sm = (SSD_LDS char*)lds(smem);
 
-    // Copies of head k into the slot at s: x rows 8 q .. 8 q + 7 and Hin
-    // rows 4 q .. 4 q + 3 for the pieces q = wave + 4 m; cs (wave 0) and dt
-    // (wave 1) whole rows.
+    // Copies of head k into the slot at s: x rows 8 q .. 8 q + 7 for the
+    // pieces q = wave + W m (m = 0, 1), Hin rows 4 q .. 4 q + 3 for q = wave +
+    // W m (m < 16 / W), and 256-byte piece `wave` of the cs row then the dt
+    // row.
     const uint32_t xo = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)rowbytes +
                         16u * (uint32_t)((lane & 7) ^ swz_x(lane >> 3));
-    const uint32_t xstep = 32u * (uint32_t)rowbytes;
-    uint32_t ho[4];
+    const uint32_t xstep = (uint32_t)(8 * W) * (uint32_t)rowbytes;
+    uint32_t ho[K::kHinCopies];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = 4 * (wave + 4 * m) + (lane >> 4);
+    for (int m = 0; m < K::kHinCopies; ++m) {
+        const int r = 4 * (wave + W * m) + (lane >> 4);
         ho[m] = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ swz_h(r)));
     }
+    const int rarr = wave / (Q / 64), rpart = wave % (Q / 64);   // cs/dt piece of this wave
     auto issue = [&](int k, SSD_LDS char* s) {
         const int h = h0 + k;
         const __amdgpu_buffer_rsrc_t rx = make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, xrecord);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) dma16_rs(rx, xo + (uint32_t)m * xstep, s + kX + (wave + 4 * m) * 1024);
+        for (int m = 0; m < 2; ++m) dma16_rs(rx, xo + (uint32_t)m * xstep, s + K::kX + (wave + W * m) * 1024);
         const __amdgpu_buffer_rsrc_t rh =
             make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), P * N * 2);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) dma16_rs(rh, ho[m], s + kH + (wave + 4 * m) * 1024);
-        if (wave < 2) {
+        for (int m = 0; m < K::kHinCopies; ++m) dma16_rs(rh, ho[m], s + K::kH + (wave + W * m) * 1024);
+        if (wave < K::kRowCopies) {
             const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
-            dma4_rs(make_rs((wave == 0 ? cs : dtc) + row, Q * 4), 4u * (uint32_t)lane,
-                    s + (wave == 0 ? kCs : kDt));
+            dma4_rs(make_rs((rarr == 0 ? cs : dtc) + row, Q * 4), 4u * (uint32_t)(64 * rpart + lane),
+                    s + (rarr == 0 ? K::kCs : K::kDt) + 256 * rpart);
         }
     };
 
-    issue(0, sm);
+    const int ncopy = 2 + K::kHinCopies + (wave < K::kRowCopies ? 1 : 0);
+#pragma unroll
+    for (int i = 0; i < SLOTS - 1; ++i)
+        if (i < cnt) issue(i, sm + i * K::kSlot);
 
     // C fragments of tile t (B operand of both C products) and the G^T
     // blocks (t, s), s <= t, the diagonal one masked to j <= i.  Tokens past
@@ -1164,12 +777,13 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) cf[kk] = *reinterpret_cast<const uint4*>(crow + 16 * kk);
     }
-    f32x16 gt[2] = {f32x16{}, f32x16{}};
+    f32x16 gt[NT];
     {
         const int jr = perm_pi(l32);
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            if (sb > t) break;
+        for (int sb = 0; sb < NT; ++sb) {
+            gt[sb] = f32x16{};
+            if (sb > t) continue;
             const int tok = min(tok0 + 32 * sb + jr, L - 1);
             const bf16_t* brow = Bm + (((int64_t)b * L + tok) * G + g) * N + 8 * hf;
             uint4 bq[8];
@@ -1190,25 +804,25 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
     const int xchk = pc >> 3, xsub = (pc & 7) * 2;
     const int pr = 32 * mt + perm_sigma(l32);
     for (int k = 0; k < cnt; ++k) {
-        // head k's copies have landed (nothing else is outstanding), and
-        // every wave is past head k - 1, whose slot now takes head k + 1
-        wait_vmcnt<0>();
+        // head k's copies have landed, and every wave is past head k - 1,
+        // whose slot now takes head k + SLOTS - 1
+        wait_vmcnt_n(short_ops_after(SLOTS, ncopy, cnt, k));
         barrier_lds();
-        if (k + 1 < cnt) issue(k + 1, sm + ((k + 1) & 1) * kSlot);
-        const SSD_LDS char* S = sm + (k & 1) * kSlot;
-        const SSD_LDS float* css = (const SSD_LDS float*)(S + kCs);
-        const SSD_LDS float* dts = (const SSD_LDS float*)(S + kDt);
+        if (k + SLOTS - 1 < cnt) issue(k + SLOTS - 1, sm + ((k + SLOTS - 1) % SLOTS) * K::kSlot);
+        const SSD_LDS char* S = sm + (k % SLOTS) * K::kSlot;
+        const SSD_LDS float* css = (const SSD_LDS float*)(S + K::kCs);
+        const SSD_LDS float* dts = (const SSD_LDS float*)(S + K::kDt);
         const float Dh = D ? D[h0 + k] : 0.0f;
         const float csi = css[32 * t + l32];
 
         // (i) + (iii): Y^T += X^T G~^T over the tile's blocks
         f32x16 acc = {};
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            if (sb > t) break;
+        for (int sb = 0; sb < NT; ++sb) {
+            if (sb > t) continue;
             u32x4v gq[2];
             rs_weights_direct(gq, gt[sb], css + 32 * sb, dts + 32 * sb, csi, Dh, sb == t, hf);
-            const SSD_LDS char* xb = S + kX + sb * 4096;
+            const SSD_LDS char* xb = S + K::kX + sb * 4096;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int r0 = 16 * u + xa.trow0, r1 = r0 + 4;
@@ -1223,7 +837,7 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_q64_kernel(
         }
         // (ii): accS = Hin C_t^T, added as exp2(cs_i) accS
         {
-            const SSD_LDS uint4* hs = (const SSD_LDS uint4*)(S + kH);
+            const SSD_LDS uint4* hs = (const SSD_LDS uint4*)(S + K::kH);
             f32x16 accS = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
@@ -1377,30 +991,6 @@ static void launch_generic_t(const Dims& d, const void* x, const void* B, const 
     else launch_generic<T, 32>(d, x, B, C, cs, dtc, Hin, D, y, stream);
 }
 
-// Heads per workgroup of the matrix-core kernel: a divisor of the heads per
-// group (they share C) chosen so that the grid fills whole rounds of the
-// machine (two workgroups per CU), with a small charge per workgroup for
-// its start-up copies.
-static int scan_heads_per_workgroup(const Dims& d) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    const double slots = 2.0 * cus;
-    const int64_t hpg = d.nheads / d.ngroups;
-    const double items = (double)d.batch * (double)d.nchunks * (double)d.nheads;
-    int best = 1;
-    double best_cost = 1e300;
-    for (int64_t hg = 1; hg <= hpg && hg <= 64; ++hg) {
-        if (hpg % hg) continue;
-        const double rounds = std::ceil(items / (double)hg / slots);
-        const double cost = rounds * ((double)hg + 0.5);
-        if (cost < best_cost - 1e-9) { best_cost = cost; best = (int)hg; }
-    }
-    return best;
-}
-
 // Heads per workgroup of the resident kernels: a run of hg heads of one
 // group, the group's heads split into nsplit runs, with per_cu workgroups
 // resident on a CU and a start-up charge (the resident tiles, the first
@@ -1437,10 +1027,8 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         bf16_t* yb = static_cast<bf16_t*>(y);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
         if (d.chunk == 256) {
-            // the resident kernel pays for its start-up (each wave's 5 or 4
-            // G^T tiles and the first head's copies) once per run of heads;
-            // measured on the MI355X it beats the streaming kernel from runs
-            // of 4 heads on (the long-context shape) and at 6 (130M-shaped)
+            // the paired kernel pays for its start-up (each wave's 5 or 4
+            // G^T tiles and the first head's copies) once per run of heads
             int hg = 0, nsplit = 0;
             scan_run_split(d, 1, 1.5, &hg, &nsplit);
             const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
@@ -1449,17 +1037,19 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
                                                                  nc, hg, nsplit);
             return hipGetLastError();   // the gate, if any, is inside
         }
+        int hg = 0, nsplit = 0;
         if (d.chunk == 64) {
-            int hg = 0, nsplit = 0;
-            scan_run_split(d, 3, 1.0, &hg, &nsplit);   // 139 VGPRs, 49 KB LDS: 3 per CU
+            scan_run_split(d, 3, 1.0, &hg, &nsplit);   // 4 waves, 49 KB of LDS: 3 per CU
             const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
-            chunk_scan_q64_kernel<<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc,
-                                                              hg, nsplit);
+            chunk_scan_short_kernel<64, 2><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G,
+                                                                    nc, hg, nsplit);
         } else {
-            // 128-token chunks: the streaming kernel
-            const int hg = scan_heads_per_workgroup(d);
-            const unsigned blocks = (unsigned)(d.batch * nc * (d.nheads / hg));
-            chunk_scan_mfma_kernel<128><<<blocks, 128, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G, nc, hg);
+            scan_run_split(d, 1, 1.0, &hg, &nsplit);   // 8 waves, 66 KB of LDS: 1 per CU
+            const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
+            // two slots: three and four (one and two more heads in flight)
+            // measured 1-5% slower at the 2.7B, 130M and long-context shapes
+            chunk_scan_short_kernel<128, 2><<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G,
+                                                                     nc, hg, nsplit);
         }
     } else if (dtype == 1) {
         launch_generic_t<bf16_t>(d, x, B, C, cs, dtc, Hin, D, y, stream);

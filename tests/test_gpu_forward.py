@@ -72,13 +72,14 @@ def test_mamba2_2p7b_shape():
                                  bh=sample_pairs(s.batch, s.nheads, 12, seed=3), label=s.name)
 
 
-def test_mamba2_2p7b_shape_chunk64():
-    """The 2.7B-shaped layer cut into 64-token chunks (512 per sequence): the
-    matrix-core kernels for short chunks, chunk_scan in runs of all 80 heads
-    of a chunk."""
+@pytest.mark.parametrize("chunk", [128, 64])
+def test_mamba2_2p7b_shape_short_chunks(chunk):
+    """The 2.7B-shaped layer cut into 128- or 64-token chunks (64 or 128 per
+    sequence): the matrix-core kernels for short chunks, chunk_scan in runs
+    of all 80 heads of a chunk."""
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_2P7B as s
     inp = _spec_inputs(s)
-    _check_with_and_without_skip(inp, 64, s.dtype,
+    _check_with_and_without_skip(inp, chunk, s.dtype,
                                  bh=sample_pairs(s.batch, s.nheads, 6, seed=4), label=s.name)
 
 
@@ -134,7 +135,7 @@ def test_long_memory_f32():
     _check(inp, 64, "f32", label="long_memory_f32")
 
 
-@pytest.mark.parametrize("chunk", [256, 64])
+@pytest.mark.parametrize("chunk", [256, 128, 64])
 @pytest.mark.parametrize("L", [1, 63, 255, 257, 1000])
 def test_ragged_lengths_bf16(L, chunk):
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M

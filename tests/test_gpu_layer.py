@@ -223,8 +223,8 @@ GATED_CASES = [
     ("resident_ragged_groups", 2, 700, 4, 64, 128, 2, 256, "bf16"),
     ("resident_130m_heads", 2, 1024, 24, 64, 128, 1, 256, "bf16"),
     ("resident_one_chunk", 1, 100, 2, 64, 128, 1, 256, "bf16"),
-    ("streaming_q128", 1, 520, 2, 64, 128, 1, 128, "bf16"),
-    ("vector_units_q64", 1, 333, 2, 64, 128, 2, 64, "bf16"),
+    ("short_q128", 1, 520, 2, 64, 128, 1, 128, "bf16"),
+    ("short_q64", 1, 333, 2, 64, 128, 2, 64, "bf16"),
     ("generic_f32", 1, 300, 3, 16, 16, 1, 64, "f32"),
 ]
 

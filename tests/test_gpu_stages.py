@@ -87,14 +87,14 @@ def test_stages(case):
         gate(y, y_ref, tol, what, y_mag)
 
 
-@pytest.mark.parametrize("Q", [256, 64])
+@pytest.mark.parametrize("Q", [256, 128, 64])
 @pytest.mark.parametrize("skip", [True, False], ids=["with_D", "D_none"])
 def test_chunk_scan_head_runs(skip, Q):
     """25 heads over 32,731 tokens: with 256-token chunks (128 (batch, chunk,
     group) units) the launcher gives each workgroup a run of 13 or 12 heads
-    of one chunk (on a 256-CU part), with 64-token chunks (512 units) one run
-    of all 25 -- the paths that keep the C.B^T tiles in registers across a
-    run.  Heads 0, 12, 13 and 24 are checked against the oracle over every
+    of one chunk (on a 256-CU part), with 128- and 64-token chunks (256 and
+    512 units) one run of all 25 -- the paths that keep the C.B^T tiles in
+    registers across a run.  Heads 0, 12, 13 and 24 are checked against the oracle over every
     chunk, including the ragged last one; with D = None the masked in-chunk
     product and the carried state are gated at their own scale."""
     import mamba_ssd_scan_02_amd as ssd
