@@ -1,0 +1,118 @@
+"""The forward and the decode step captured in a HIP graph (torch.cuda.graph
+over the binding's calls) and replayed: every replay, with the program's own
+eager work and new input values in between, must give exactly what the same
+calls give eagerly.  ssd_forward_noalloc is the entry point meant for callers
+under capture (no workspace to allocate); ssd_forward with a caller-held
+workspace and ssm_step capture the same way.  None of them records a memset
+or allocates."""
+import ctypes
+
+import pytest
+import torch
+
+from tests.helpers import say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, batch=2, seqlen=1000, nheads=8, ngroups=2):
+    from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M, make_forward_inputs
+    spec = MAMBA2_130M.with_(batch=batch, seqlen=seqlen, nheads=nheads, ngroups=ngroups,
+                             init_var=0.1, seed=seed)
+    return spec, to_gpu(make_forward_inputs(spec))
+
+
+def _refill(dst: dict, src: dict):
+    for k, v in src.items():
+        if isinstance(v, torch.Tensor):
+            dst[k].copy_(v)
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                         # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+@pytest.mark.parametrize("entry", ["ssd_forward", "ssd_forward_noalloc"])
+def test_forward_graph_replays_match_eager(entry):
+    import mamba_ssd_scan_02_amd as ssd
+    lib = ssd.load()
+    spec, g = _inputs(91)
+    x = g["x"]
+    batch, L, H, P = x.shape
+    G, N, Q = g["B"].shape[2], g["B"].shape[3], spec.chunk
+    y = torch.empty_like(x)
+    fin = torch.empty((batch, H, P, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ssd.workspace_bytes(batch, L, H, P, N, G, Q, x.dtype), dtype=torch.uint8,
+                     device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def run():
+        if entry == "ssd_forward":
+            ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], Q, g["init"], y=y,
+                            final_state=fin, workspace=ws)
+        else:
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            st = lib.ssd_forward_noalloc(batch, L, H, P, N, G, Q, 1, p(g["x"]), p(g["dt"]),
+                                         p(g["A"]), p(g["B"]), p(g["C"]), p(g["D"]), p(g["init"]),
+                                         p(y), p(fin), stream)
+            assert st == 0, st
+
+    say(f"[graph] {entry}: capture")
+    graph = _capture(run)
+    for rep, seed in enumerate((91, 92, 92, 93)):
+        _, fresh = _inputs(seed)
+        _refill(g, fresh)                                   # eager work between replays
+        y_e, f_e = ssd.ssd_forward(fresh["x"], fresh["dt"], fresh["A"], fresh["B"], fresh["C"],
+                                   fresh["D"], Q, fresh["init"])
+        y.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep} (inputs seed {seed})")
+        assert torch.equal(y, y_e) and torch.equal(fin, f_e), (entry, rep)
+
+
+def test_decode_graph_replays_match_eager():
+    """Sixteen decode steps captured as one graph (the launch-bound small-batch
+    case), replayed from a re-initialised state."""
+    import mamba_ssd_scan_02_amd as ssd
+    from mamba_ssd_scan_02_amd.workloads import (DECODE_B256, make_decode_static,
+                                                 make_decode_step)
+    spec = DECODE_B256.with_(batch=4, steps=16, nheads=8)
+    st = make_decode_static(spec)
+    A, D = st["A"].cuda(), st["D"].cuda()
+    state0 = st["state"].cuda()
+    steps = [{k: v.cuda() for k, v in make_decode_step(spec, t).items()} for t in range(spec.steps)]
+    ys = [torch.empty_like(s["x"]) for s in steps]
+    state = state0.clone()
+
+    def run():
+        for s, yt in zip(steps, ys):
+            ssd.ssm_step(state, s["x"], s["dt"], A, s["B"], s["C"], D, y_t=yt)
+
+    graph = _capture(run)
+    ref_state = state0.clone()
+    ref_ys = []
+    for s in steps:
+        yt = torch.empty_like(s["x"])
+        ssd.ssm_step(ref_state, s["x"], s["dt"], A, s["B"], s["C"], D, y_t=yt)
+        ref_ys.append(yt)
+    for rep in range(3):
+        state.copy_(state0)
+        for yt in ys:
+            yt.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"[graph] decode replay {rep}")
+        assert torch.equal(state, ref_state), rep
+        assert all(torch.equal(a, b) for a, b in zip(ys, ref_ys)), rep
