@@ -87,6 +87,28 @@ def test_stages(case):
         gate(y, y_ref, tol, what, y_mag)
 
 
+def test_chunk_state_many_rounds():
+    """800 head-pair workgroups (100 chunks x 8 pairs), more than one round of
+    the machine (three per CU), each storing its S tiles through LDS as whole
+    rows: S and the forward's first launch against the fp64 stage
+    definition."""
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    batch, L, H, P, N, G, Q = 1, 256 * 100 - 3, 16, 64, 128, 2, 256
+    say("[stages] chunk_state, many rounds")
+    inp = _inputs(15, batch, L, H, P, N, G, "bf16")
+    g = to_gpu(inp)
+    cs, dtc = ssd.chunk_cumsum(g["dt"], g["A"], Q)
+    S = ssd.chunk_state(g["x"], g["B"], cs, dtc, Q)
+    cs2, dtc2, S2 = ssd.chunk_cumsum_state(g["x"], g["B"], g["dt"], g["A"], Q)
+    assert torch.equal(cs2, cs) and torch.equal(dtc2, dtc) and torch.equal(S2, S)
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    S_ref = stages.chunk_state(inp["x"], inp["dt"], inp["B"], Acs, Q)
+    S_mag = stages.chunk_state(inp["x"].abs(), inp["dt"], inp["B"].abs(), Acs, Q)
+    gate(S, S_ref, TOL["bf16"], "chunk_state S (many rounds)", S_mag)
+
+
 @pytest.mark.parametrize("Q", [256, 128, 64])
 @pytest.mark.parametrize("skip", [True, False], ids=["with_D", "D_none"])
 def test_chunk_scan_head_runs(skip, Q):
