@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
     const bf16_t* xbase = x + ((int64_t)b * L * H + h) * P;
     const bf16_t* bbase = Bm + ((int64_t)b * L * G + g) * N;
 
-    // ordinary loads first (see chunk_scan): w_j = exp2(cs_last - cs_j) dt_j
+    // ordinary loads first, so that the compiler's wait for them does not
+    // also wait for the LDS copies issued after: w_j = exp2(cs_last - cs_j) dt_j
     float w_v = 0.0f;
     if (tid < Q) w_v = fast_exp2(cs[row + Q - 1] - cs[row + tid]) * dtc[row + tid];
     asm volatile("" ::: "memory");
