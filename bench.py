@@ -23,7 +23,8 @@ warm-up steps and the K timed ones.
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (its
 algorithmic bytes per launch over its average launch time, measured here with
 HIP events on the stream it runs on), per-kernel figures, the decode step
-(batch 256, 64 steps), the zero-order-hold forward, the kernels of the block
+(batch 256, 64 steps; and at batch 1 and 4 issued call by call against one
+HIP graph of the 64 calls), the zero-order-hold forward, the kernels of the block
 around the scan (short convolution + step, gate) at the same shape, and the
 fp64 CPU oracle timed on a bounded sample.
 """
@@ -285,6 +286,55 @@ def bench_decode(ssd, steps_warm=3):
         "bytes_per_step": byts, "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
         "traffic": counter_traffic("ssm_step", spec.name),
     }
+
+
+def bench_decode_graph(ssd, batches=(1, 4), reps=5):
+    """Decode at small batch, where each step is a few microseconds of GPU
+    work: the 64 steps issued one binding call at a time (host-bound) against
+    the same 64 calls captured once in a HIP graph and replayed."""
+    import torch
+    from mamba_ssd_scan_02_amd.workloads import DECODE_B256, make_decode_static, make_decode_step
+    out = []
+    for batch in batches:
+        spec = DECODE_B256.with_(batch=batch)
+        st = make_decode_static(spec)
+        A, D = st["A"].cuda(), st["D"].cuda()
+        state = st["state"].cuda()
+        ins = [{k: v.cuda() for k, v in make_decode_step(spec, t).items()} for t in range(spec.steps)]
+        ys = [torch.empty_like(i["x"]) for i in ins]
+
+        def run():
+            for i, yt in zip(ins, ys):
+                ssd.ssm_step(state, i["x"], i["dt"], A, i["B"], i["C"], D, y_t=yt)
+
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        run()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) * 1e3 / (reps * spec.steps)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * spec.steps)
+        out.append({"batch": batch, "eager_us_per_step": round(eager, 2), "graph_us_per_step": round(us, 2)})
+    return out
 
 
 def bench_layer(ssd, spec, steps=20, block=True):
@@ -853,6 +903,7 @@ def main():
     if not args.no_decode:
         log("[bench] decode")
         out["decode"] = bench_decode(ssd)
+        out["decode_small_batch"] = bench_decode_graph(ssd)
     if not args.no_layer:
         log("[bench] layer around the scan")
         out["layer"] = bench_layer(ssd, spec)
