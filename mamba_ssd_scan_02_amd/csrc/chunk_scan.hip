@@ -63,8 +63,7 @@ __device__ __forceinline__ int perm_sigma(int m) {
 }
 
 // ---------------------------------------------------------------------------
-// Pieces shared by the two matrix-core kernels.  A workgroup has 4 waves (or
-// Q/64 for short chunks); wave w owns i tiles it_[0] = w and it_[1] = 2W-1-w.
+// Pieces shared by the two matrix-core kernels.
 
 // Per-lane tr16 addressing of the X^T operand (see lds_pipe.h): lane r of
 // 16-lane group grp supplies token row 8*(grp/2) + r/4 and channel quad qb,
@@ -150,8 +149,9 @@ struct TileF {
 };
 
 // ---------------------------------------------------------------------------
-// Pieces of the resident kernel below (Q = 256): per-slot LDS operands, the
-// slot's weights and its products.
+// Pieces of the paired kernel below (Q = 256): per-slot LDS operands, the
+// slot's weights and its products (the direct weights also serve the
+// short-chunk kernel).
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
