@@ -158,12 +158,13 @@ def test_chunk_sweep_f32(chunk):
     _check(inp, chunk, "f32", label="chunk sweep f32")
 
 
-def test_groups_and_permutation():
+@pytest.mark.parametrize("chunk", [256, 128, 64])
+def test_groups_and_permutation(chunk):
     """G = 8 groups of 4 heads; permuting groups together with their heads
     permutes the outputs exactly."""
     from mamba_ssd_scan_02_amd.workloads import LONG_1M
     inp = _spec_inputs(LONG_1M.with_(seqlen=1024, init_var=0.1, seed=80))
-    y, fin = _check(inp, 256, "bf16", label="groups G=8")
+    y, fin = _check(inp, chunk, "bf16", label="groups G=8")
     gperm = np.array([3, 0, 7, 1, 6, 2, 5, 4])
     hperm = np.concatenate([np.arange(4 * g, 4 * g + 4) for g in gperm])
     p = dict(inp)
@@ -171,7 +172,7 @@ def test_groups_and_permutation():
     p["x"], p["dt"] = inp["x"][:, :, hperm].contiguous(), inp["dt"][:, :, hperm].contiguous()
     p["A"], p["D"] = inp["A"][hperm].contiguous(), inp["D"][hperm].contiguous()
     p["init"] = inp["init"][:, hperm].contiguous()
-    y2, fin2 = gpu_forward(p, 256)
+    y2, fin2 = gpu_forward(p, chunk)
     assert torch.equal(y2.cpu(), y.cpu()[:, :, hperm])
     assert torch.equal(fin2.cpu(), fin.cpu()[:, hperm])
 

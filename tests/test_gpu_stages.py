@@ -26,6 +26,7 @@ CASES = [
     # (name, batch, L, H, P, N, G, chunk, dtype)
     ("mfma_q256_ragged", 2, 700, 4, 64, 128, 2, 256, "bf16"),
     ("mfma_q128", 1, 512, 2, 64, 128, 1, 128, "bf16"),
+    ("mfma_q128_groups_ragged", 2, 1000, 6, 64, 128, 3, 128, "bf16"),
     ("mfma_q64_ragged", 1, 333, 2, 64, 128, 2, 64, "bf16"),
     ("mfma_q64_odd_heads", 2, 700, 6, 64, 128, 2, 64, "bf16"),
     ("generic_f32", 2, 300, 3, 16, 16, 1, 64, "f32"),
