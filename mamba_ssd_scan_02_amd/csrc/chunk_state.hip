@@ -536,8 +536,9 @@ constexpr int kWalkHin = 32;                           // Hin stores per wave pe
 
 // Operations issued after stage k = c NT + jt when step jt of chunk c waits
 // for it: the stages issued ahead of it, plus chunk c's Hin stores and the
-// next chunk's row copies when they came after stage k's copies.
-__host__ __device__ constexpr int walk_ops_after(int NT, int jt) {
+// next chunk's row copies when they came after stage k's copies (which does
+// not depend on NT while the ring is shallower than a chunk is long).
+__host__ __device__ constexpr int walk_ops_after(int /*NT*/, int jt) {
     return (kWalkRing - 2) * kWalkDps + (jt < kWalkRing - 1 ? kWalkHin + kWalkRows : 0);
 }
 // The issue order replayed against those waits over a few chunks (labels:
@@ -627,7 +628,6 @@ __global__ __launch_bounds__(256, 1) void state_walk_kernel(
     const int grp = lane >> 4, rr4 = lane & 15;
     const int trow0 = 8 * (grp >> 1) + (rr4 >> 2);
     const int qcol = 16 * (grp & 1) + 4 * (rr4 & 3);
-    const bool odd = (lane & 1) != 0;
 
     for (int c = 0; c < nc; ++c) {
         // chunk c's rows were copied at chunk c - 1's start, before its NT stages

@@ -10,7 +10,11 @@
 //    accesses on their side of the issue): the compiler then never waits
 //    for them on its own -- it cannot tell every LDS read from a copy in
 //    flight and would otherwise drain all copies before such reads -- and
-//    the waits written here are the only ones that order them.
+//    the waits written here are the only ones that order them.  Each sets
+//    M0 (the copy's LDS base) inside its own asm; hipcc warns that M0 is a
+//    reserved register in the clobber list.  The kernels' compiled code
+//    reads M0 nowhere else: every M0 access in their ISA is one of these
+//    s_mov_b32 m0 writes directly before its copy.
 //  * tr16(): ds_read_b64_tr_b16 -- within each group of 16 lanes, lane i
 //    receives element (i % 4) of the 4-element (8-byte) rows addressed by
 //    lanes 4k + i/4, k = 0..3.  If lane r of a group addresses row (token)
