@@ -44,6 +44,7 @@
 //
 // Generic kernel (fp32 or bf16, any P, N within limits): the same three terms
 // in fp32 on the vector units, 32 x 32 tiles in LDS.
+#include <algorithm>
 #include <cmath>
 
 #include "device_common.h"
@@ -1016,6 +1017,29 @@ static void scan_run_split(const Dims& d, int per_cu, double startup, int* hg_ou
     *nsplit_out = (int)((hpg + best - 1) / best);
 }
 
+void chunk_scan_runs(const Dims& d, int* hg, int* nsplit) {
+    // the paired kernel pays for its start-up (each wave's 5 or 4 G^T tiles
+    // and the first head's copies) once per run of heads, one workgroup per
+    // CU; the short-chunk kernels take three (Q = 64: 4 waves, 49 KB of LDS)
+    // or one (Q = 128: 8 waves, 66 KB) per CU
+    if (d.chunk == 256) scan_run_split(d, 1, 1.5, hg, nsplit);
+    else if (d.chunk == 64) scan_run_split(d, 3, 1.0, hg, nsplit);
+    else scan_run_split(d, 1, 1.0, hg, nsplit);
+}
+
+int x_keep_positions(const Dims& d) {
+    // the chunk scan takes run position k of every run at about the same
+    // time, so ordinary (cache-allocating) x reads for the first positions
+    // give its first heads' x from the last-level cache; budget: ~5/8 of the
+    // cache, leaving room for what the kernels between allocate
+    int hg = 0, nsplit = 0;
+    chunk_scan_runs(d, &hg, &nsplit);
+    const double per_position = (double)d.batch * (double)d.seqlen * (double)d.headdim * 2.0 *
+                                (double)d.ngroups * (double)nsplit;
+    const double k = std::floor(0.625 * kLastLevelCacheBytes / per_position);
+    return (int)std::min<double>(k, (double)hg);
+}
+
 hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const void* B,
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream, const void* z) {
@@ -1026,26 +1050,19 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         const bf16_t* hb = static_cast<const bf16_t*>(Hin);
         bf16_t* yb = static_cast<bf16_t*>(y);
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
+        int hg = 0, nsplit = 0;
+        chunk_scan_runs(d, &hg, &nsplit);
+        const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
         if (d.chunk == 256) {
-            // the paired kernel pays for its start-up (each wave's 5 or 4
-            // G^T tiles and the first head's copies) once per run of heads
-            int hg = 0, nsplit = 0;
-            scan_run_split(d, 1, 1.5, &hg, &nsplit);
-            const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
             chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D,
                                                                  static_cast<const bf16_t*>(z), yb, L, H, G,
                                                                  nc, hg, nsplit);
             return hipGetLastError();   // the gate, if any, is inside
         }
-        int hg = 0, nsplit = 0;
         if (d.chunk == 64) {
-            scan_run_split(d, 3, 1.0, &hg, &nsplit);   // 4 waves, 49 KB of LDS: 3 per CU
-            const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
             chunk_scan_short_kernel<64, 2><<<blocks, 256, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G,
                                                                     nc, hg, nsplit);
         } else {
-            scan_run_split(d, 1, 1.0, &hg, &nsplit);   // 8 waves, 66 KB of LDS: 1 per CU
-            const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
             // two slots: three and four (one and two more heads in flight)
             // measured 1-5% slower at the 2.7B, 130M and long-context shapes
             chunk_scan_short_kernel<128, 2><<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D, yb, L, H, G,

@@ -221,7 +221,8 @@ template <int W, int HG>
 __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase, int L,
                                                 const bf16_t* xbase, int64_t xstride,
                                                 const bf16_t* bbase, int64_t bstride,
-                                                const BxhOffsets<W, HG>& off, uint4* bst, uint4* xst) {
+                                                const BxhOffsets<W, HG>& off, uint4* bst, uint4* xst,
+                                                bool keep) {
     constexpr int PPR = 8 * HG, RPC = 64 / PPR, XC = BxhOffsets<W, HG>::XC;
     asm volatile("" : "+s"(tokbase));
     if (tokbase + 31 < L) {
@@ -229,8 +230,13 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
         const char* xb = reinterpret_cast<const char*>(xbase + (int64_t)tokbase * xstride);
 #pragma unroll
         for (int i = 0; i < 8 / W; ++i) dma16(bb, off.b[i], lds(bst) + (wave + i * W) * 64);
+        if (keep) {
 #pragma unroll
-        for (int i = 0; i < XC; ++i) dma16_nt(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
+            for (int i = 0; i < XC; ++i) dma16(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
+        } else {
+#pragma unroll
+            for (int i = 0; i < XC; ++i) dma16_nt(xb, off.x[i], lds(xst) + (wave + i * W) * 64);
+        }
         return;
     }
     const int tb = min(tokbase, L - 1);
@@ -325,7 +331,7 @@ __device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, in
                                                  const float* dtc, int L, int H, int G, int nc,
                                                  const float* __restrict__ dtin,
                                                  const float* __restrict__ A, float* csw,
-                                                 float* dtcw, int zoh, f32x16 (&acc)[HG][2],
+                                                 float* dtcw, int zoh, bool keepx, f32x16 (&acc)[HG][2],
                                                  float (&cl)[HG]) {
     constexpr int W = 4, NT = Q / 32;
     constexpr int XR = 128 * HG;                         // bytes of a token's x row
@@ -378,7 +384,7 @@ __device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, in
     const BxhOffsets<W, HG> off = bxh_offsets<W, HG>(wave, lane, xstride, bstride);
 #pragma unroll
     for (int k = 0; k < R - 1; ++k)
-        if (k < NT) issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * k, L, xbase, xstride, bbase, bstride, off, bsr[k], xsr[k]);
+        if (k < NT) issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * k, L, xbase, xstride, bbase, bstride, off, bsr[k], xsr[k], keepx);
     if constexpr (FUSE) {
         // the prefix while the first copies are in flight (LDS-only barriers:
         // a full barrier would wait for the copies)
@@ -425,7 +431,7 @@ __device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, in
         barrier_lds();
         if (jt + R - 1 < NT)
             issue_bxh_stage<W, HG>(wave, lane, tok0 + 32 * (jt + R - 1), L, xbase, xstride, bbase, bstride,
-                                   off, bsr[(jt + R - 1) % R], xsr[(jt + R - 1) % R]);
+                                   off, bsr[(jt + R - 1) % R], xsr[(jt + R - 1) % R], keepx);
         const SSD_LDS char* xb = (const SSD_LDS char*)lds(xst);
         const SSD_LDS char* bb = (const SSD_LDS char*)lds(bst);
 #pragma unroll
@@ -480,7 +486,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
                                                                    int H, int G, int nc,
                                                                    const float* __restrict__ dtin,
                                                                    const float* __restrict__ A,
-                                                                   float* csw, float* dtcw, int zoh) {
+                                                                   float* csw, float* dtcw, int zoh,
+                                                                   int keep_run, int keep_k) {
     constexpr int P = 64, N = 128;
     __shared__ StateSmem<Q, HG> sm;
     const int HP = H / HG;
@@ -488,10 +495,12 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     const int h0 = HG * (int)(wg % (uint32_t)HP);
     const int bc = (int)(wg / (uint32_t)HP);
     const int c = bc % nc, b = bc / nc;
+    // x of the heads at the chunk scan's first run positions stays cached
+    const bool keepx = (h0 % (H / G)) % keep_run < keep_k;
     f32x16 acc[HG][2];
     float cl[HG];
     chunk_state_pair<Q, HG, FUSE>(sm, b, c, h0, x, Bm, cs, dtc, L, H, G, nc, dtin, A, csw, dtcw, zoh,
-                                  acc, cl);
+                                  keepx, acc, cl);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     static_assert(sizeof(sm.bsr) >= P * N * 2 && sizeof(sm.xsr) >= (HG - 1) * P * N * 2,
@@ -605,7 +614,7 @@ __global__ __launch_bounds__(256, 1) void state_walk_kernel(
     };
     auto issue_stage = [&](int k) {
         issue_bxh_stage<W, HG>(wave, lane, 32 * k, L, xbase, xstride, bbase, bstride, off, bsr[k % R],
-                               xsr[k % R]);
+                               xsr[k % R], false);
     };
 
     // running state, from init or zero
@@ -815,10 +824,13 @@ hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B,
     const bf16_t* bb = static_cast<const bf16_t*>(B);
     const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
     const int z = zoh ? 1 : 0;
+    int krun = 1, nsplit = 1;
+    chunk_scan_runs(d, &krun, &nsplit);
+    const int kk = x_keep_positions(d);
     switch (d.chunk) {
-        case 64: chunk_state_mfmah_kernel<64, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
-        case 128: chunk_state_mfmah_kernel<128, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
-        default: chunk_state_mfmah_kernel<256, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z); break;
+        case 64: chunk_state_mfmah_kernel<64, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z, krun, kk); break;
+        case 128: chunk_state_mfmah_kernel<128, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z, krun, kk); break;
+        default: chunk_state_mfmah_kernel<256, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z, krun, kk); break;
     }
     return hipGetLastError();
 }
@@ -852,10 +864,13 @@ hipError_t launch_chunk_state(const Dims& d, int32_t dtype, const void* x, const
         const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
         if ((d.nheads / d.ngroups) % kStateHeads == 0) {
             const unsigned hblocks = blocks / (unsigned)kStateHeads;
+            int krun = 1, nsplit = 1;
+            chunk_scan_runs(d, &krun, &nsplit);
+            const int kk = x_keep_positions(d);
             switch (d.chunk) {
-                case 64: chunk_state_mfmah_kernel<64, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
-                case 128: chunk_state_mfmah_kernel<128, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
-                default: chunk_state_mfmah_kernel<256, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0); break;
+                case 64: chunk_state_mfmah_kernel<64, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0, krun, kk); break;
+                case 128: chunk_state_mfmah_kernel<128, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0, krun, kk); break;
+                default: chunk_state_mfmah_kernel<256, kStateHeads, false><<<hblocks, 256, 0, stream>>>(xb, bb, cs, dtc, S, L, H, G, nc, nullptr, nullptr, nullptr, nullptr, 0, krun, kk); break;
             }
             return hipGetLastError();
         }

@@ -45,6 +45,18 @@ hipError_t launch_state_passing_seg(const Dims& d, int32_t dtype, int64_t nseg_r
                                     const float* cs, const float* init, void* Hin,
                                     float* final_state, void* workspace, hipStream_t stream);
 
+// The runs of heads the matrix-core chunk scan gives each workgroup: hg heads
+// of one group per run, a group's heads in nsplit runs (mfma_path shapes).
+void chunk_scan_runs(const Dims& d, int* hg, int* nsplit);
+
+// x is read twice (chunk state, then chunk scan).  The chunk-state kernel
+// reads with ordinary (cache-allocating) loads the x of the heads at run
+// positions below x_keep_positions, which the chunk scan reads first, and
+// non-temporally the rest, so that the chunk scan finds those heads' x in
+// the 256 MB last-level cache.
+constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
+int x_keep_positions(const Dims& d);
+
 // With z, y receives y * silu(z) (the gate of the block around the scan):
 // inside the store of the 256-token matrix-core kernel, else by the gate
 // kernel in place after the chunk scan.
