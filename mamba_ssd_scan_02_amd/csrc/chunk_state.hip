@@ -187,8 +187,9 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfma_kernel(const bf16_t* 
 // and each B fragment read from LDS serves all HG heads (scaled by each
 // head's weights).  Wave w owns state columns n in [32w, 32w+32) of every
 // head.  Wider rows read faster from HBM than one head's 128-byte rows, and B
-// crosses L2 -> LDS once per HG heads.  x is read once, with non-temporal
-// copies (138 -> 132 us at the 2.7B shape).
+// crosses L2 -> LDS once per HG heads.  x is copied non-temporally (138 ->
+// 132 us at the 2.7B shape), except for the heads whose x the chunk scan
+// reads first (x_keep_positions), which stay in the last-level cache.
 template <int W, int HG>
 struct BxhOffsets {
     static constexpr int XC = 4 * HG / W;   // x copies per wave per stage
