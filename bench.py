@@ -212,10 +212,10 @@ def time_stages(ssd, g, y, fin, dims, steps):
     stream the stage calls are launched on (torch's current stream): first
     the forward's own kernels in the forward's order (chunk state with the
     cumsum inside, state passing, chunk scan -- each launched by the stage
-    call that runs the same kernel, so each one follows what it follows in
-    the forward), then the stand-alone cumsum and chunk state and the
-    one-pass state stage.  Buffers of their own, not the forward's
-    workspace."""
+    call that runs the same kernel), repeated with nothing else in between,
+    so each one follows what it follows in the forward; then, in a loop of
+    their own, the stand-alone cumsum and chunk state and the one-pass state
+    stage.  Buffers of their own, not the forward's workspace."""
     import ctypes
     import torch
     lib = ssd.load()
@@ -245,16 +245,23 @@ def time_stages(ssd, g, y, fin, dims, steps):
     for f in calls:            # warm
         assert f() == 0
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
-    for k in range(steps):
-        ev[k][0].record()
-        for i, f in enumerate(calls):
-            if f() != 0:
-                raise RuntimeError(f"{names[i]} failed")
-            ev[k][i + 1].record()
-    torch.cuda.synchronize()
-    return {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps * 1e3
-            for i, n in enumerate(names)}   # microseconds
+    out = {}
+    # the forward's three kernels on their own, back to back: what each finds
+    # in the caches is what it finds inside ssd_forward; then the stand-alone
+    # stage kernels in a loop of their own
+    for group in ((0, 1, 2), (3, 4, 5)):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(group) + 1)]
+              for _ in range(steps)]
+        for k in range(steps):
+            ev[k][0].record()
+            for j, i in enumerate(group):
+                if calls[i]() != 0:
+                    raise RuntimeError(f"{names[i]} failed")
+                ev[k][j + 1].record()
+        torch.cuda.synchronize()
+        for j, i in enumerate(group):   # microseconds
+            out[names[i]] = sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(steps)) / steps * 1e3
+    return out
 
 
 def bench_decode(ssd, steps_warm=3):
@@ -857,6 +864,7 @@ def main():
                  "mfma_frac_algorithmic_flops": round(flops_total / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                  "compulsory_bytes": comp, "forward_kernels": path,
                  "forward_kernel_bytes": sum(kbytes[n] for n in path),
+                 "forward_kernel_event_sum_us": round(sum(k_us[n] for n in path), 2),
                  "algorithmic_flops": flops_total, "wall_s_timed_region": round(wall, 4)},
         "kernels": kernels,
     }

@@ -226,7 +226,10 @@ int32_t ssm_step_zoh(int64_t batch, int64_t nheads, int64_t headdim, int64_t dst
 /*
  * The four stages of ssd_forward, callable one by one (per-stage checks and
  * timing).  Arrays named after the workspace regions have the layouts given
- * at ssd_forward_workspace_bytes.
+ * at ssd_forward_workspace_bytes.  Every stage call returns SSD_ERR_ALIAS,
+ * before any launch, when one of its outputs overlaps one of its inputs or
+ * another of its outputs; the one permitted overlap is final_state on
+ * init_state (each entry is read before it is written).
  */
 
 /* cs, dtc from dt and A: the per-chunk inclusive prefix of dt * A, scaled by

@@ -101,6 +101,49 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// A device array of a call: its first byte and its length (NULL: absent).
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+// SSD_ERR_ALIAS when an output overlaps an input or another output.  The
+// one pair that may overlap (final_state on init_state, whose entries are
+// read before they are written) is named by its indices, or -1.
+template <size_t NI, size_t NO>
+int32_t check_spans(const Span (&in)[NI], const Span (&out)[NO], int ok_out = -1, int ok_in = -1) {
+    for (size_t o = 0; o < NO; ++o) {
+        for (size_t i = 0; i < NI; ++i) {
+            if ((int)o == ok_out && (int)i == ok_in) continue;
+            if (overlaps(out[o].p, out[o].n, in[i].p, in[i].n)) return SSD_ERR_ALIAS;
+        }
+        for (size_t o2 = o + 1; o2 < NO; ++o2)
+            if (overlaps(out[o].p, out[o].n, out[o2].p, out[o2].n)) return SSD_ERR_ALIAS;
+    }
+    return SSD_OK;
+}
+
+// Byte lengths of the arrays the stage calls share (sizes already checked,
+// so no product overflows: chunk, P and N are at most 256, 128 and 128 and
+// batch * chunks * heads fits 31 bits).
+struct Sizes {
+    size_t x, bc, dt, head, rows, states, state32;
+};
+
+Sizes sizes_of(const Dims& d, size_t es) {
+    const size_t tok = (size_t)d.batch * (size_t)d.seqlen;
+    const size_t bhc = (size_t)d.batch * (size_t)d.nheads * (size_t)d.nchunks;
+    Sizes z;
+    z.x = tok * (size_t)d.nheads * (size_t)d.headdim * es;
+    z.bc = tok * (size_t)d.ngroups * (size_t)d.dstate * es;
+    z.dt = tok * (size_t)d.nheads * 4;
+    z.head = (size_t)d.nheads * 4;
+    z.rows = bhc * (size_t)d.chunk * 4;
+    z.states = bhc * (size_t)d.headdim * (size_t)d.dstate * es;
+    z.state32 = (size_t)d.batch * (size_t)d.nheads * (size_t)d.headdim * (size_t)d.dstate * 4;
+    return z;
+}
+
 }  // namespace
 
 // Workspace of ssd_forward_noalloc: one array per device, resident from the
@@ -172,6 +215,10 @@ static int32_t chunk_cumsum_impl(int64_t batch, int64_t seqlen, int64_t nheads, 
     if (chunk > 256) return SSD_ERR_UNSUPPORTED;
     if (!dt || !A || !cs || !dtc) return SSD_ERR_NULL;
     if (!aligned(dt, 4) || !aligned(A, 4) || !aligned(cs, 4) || !aligned(dtc, 4)) return SSD_ERR_ALIGN;
+    const Sizes z = sizes_of(d, 4);
+    const Span in[] = {{dt, z.dt}, {A, z.head}};
+    const Span out[] = {{cs, z.rows}, {dtc, z.rows}};
+    if ((st = check_spans(in, out)) != SSD_OK) return st;
     return hip_status(ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, zoh));
 }
 
@@ -198,6 +245,12 @@ int32_t ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
     if (!x || !B || !cs || !dtc || !S) return SSD_ERR_NULL;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(S, 16) || !aligned(cs, 4) || !aligned(dtc, 4))
         return SSD_ERR_ALIGN;
+    size_t es;
+    elem_size(dtype, &es);
+    const Sizes z = sizes_of(d, es);
+    const Span in[] = {{x, z.x}, {B, z.bc}, {cs, z.rows}, {dtc, z.rows}};
+    const Span out[] = {{S, z.states}};
+    if ((st = check_spans(in, out)) != SSD_OK) return st;
     return hip_status(ssd::launch_chunk_state(d, dtype, x, B, cs, dtc, S, stream));
 }
 
@@ -213,6 +266,12 @@ int32_t ssd_chunk_cumsum_state(int64_t batch, int64_t seqlen, int64_t nheads, in
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(S, 16) || !aligned(dt, 4) || !aligned(A, 4) ||
         !aligned(cs, 4) || !aligned(dtc, 4))
         return SSD_ERR_ALIGN;
+    size_t es;
+    elem_size(dtype, &es);
+    const Sizes z = sizes_of(d, es);
+    const Span in[] = {{x, z.x}, {B, z.bc}, {dt, z.dt}, {A, z.head}};
+    const Span out[] = {{cs, z.rows}, {dtc, z.rows}, {S, z.states}};
+    if ((st = check_spans(in, out)) != SSD_OK) return st;
     if (ssd::chunk_state_fuses_cumsum(dtype, d))
         return hip_status(ssd::launch_chunk_state_fused(d, x, B, dt, A, 0, cs, dtc, S, stream));
     hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, cs, dtc, stream, 0);
@@ -232,6 +291,12 @@ int32_t ssd_state_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t
     if (!aligned(S, 16) || !aligned(Hin, 16) || !aligned(cs, 4) ||
         (init_state && !aligned(init_state, 16)) || (final_state && !aligned(final_state, 16)))
         return SSD_ERR_ALIGN;
+    size_t es;
+    elem_size(dtype, &es);
+    const Sizes z = sizes_of(d, es);
+    const Span in[] = {{S, z.states}, {cs, z.rows}, {init_state, z.state32}};
+    const Span out[] = {{Hin, z.states}, {final_state, z.state32}};
+    if ((st = check_spans(in, out, 1, 2)) != SSD_OK) return st;
     return hip_status(ssd::launch_state_passing(d, dtype, S, cs, init_state, Hin, final_state, stream));
 }
 
@@ -262,6 +327,12 @@ int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int
     ssd::state_passing_segments(d.nchunks, nsegments, &seg, &nseg);
     if (workspace_bytes < ssd::state_passing_seg_workspace_bytes(batch, nheads, headdim, dstate, nseg))
         return SSD_ERR_WORKSPACE;
+    size_t es;
+    elem_size(dtype, &es);
+    const Sizes z = sizes_of(d, es);
+    const Span in[] = {{S, z.states}, {cs, z.rows}, {init_state, z.state32}};
+    const Span out[] = {{Hin, z.states}, {final_state, z.state32}, {workspace, workspace_bytes}};
+    if ((st = check_spans(in, out, 1, 2)) != SSD_OK) return st;
     return hip_status(ssd::launch_state_passing_seg(d, dtype, nsegments, S, cs, init_state, Hin,
                                                     final_state, workspace, stream));
 }
@@ -283,6 +354,10 @@ int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
         !aligned(dtc, 4) || (init_state && !aligned(init_state, 16)) ||
         (final_state && !aligned(final_state, 16)))
         return SSD_ERR_ALIGN;
+    const Sizes z = sizes_of(d, es);
+    const Span in[] = {{x, z.x}, {B, z.bc}, {cs, z.rows}, {dtc, z.rows}, {init_state, z.state32}};
+    const Span out[] = {{Hin, z.states}, {final_state, z.state32}};
+    if ((st = check_spans(in, out, 1, 4)) != SSD_OK) return st;
     if (walk)
         return hip_status(ssd::launch_state_walk(d, x, B, cs, dtc, init_state, Hin, final_state, stream));
     return hip_status(ssd::launch_state_scan(d, x, B, cs, dtc, init_state, Hin, final_state, stream));
@@ -303,11 +378,11 @@ int32_t ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
         return SSD_ERR_ALIGN;
     size_t es;
     elem_size(dtype, &es);
-    const size_t ybytes = (size_t)d.batch * d.seqlen * d.nheads * d.headdim * es;
-    const size_t bcbytes = (size_t)d.batch * d.seqlen * d.ngroups * d.dstate * es;
-    if (overlaps(y, ybytes, x, ybytes) || overlaps(y, ybytes, B, bcbytes) ||
-        overlaps(y, ybytes, C, bcbytes))
-        return SSD_ERR_ALIAS;
+    const Sizes z = sizes_of(d, es);
+    const Span in[] = {{x, z.x},      {B, z.bc},       {C, z.bc},     {cs, z.rows},
+                       {dtc, z.rows}, {Hin, z.states}, {D, z.head}};
+    const Span out[] = {{y, z.x}};
+    if ((st = check_spans(in, out)) != SSD_OK) return st;
     return hip_status(ssd::launch_chunk_scan(d, dtype, x, B, C, cs, dtc, Hin, D, y, stream));
 }
 
@@ -343,18 +418,10 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     // input (the gate's z included) and of the other outputs; the one
     // permitted overlap is final_state on init_state (the state is read
     // before it is written).
-    struct Span { const void* p; size_t n; };
     const Span inputs[] = {{x, ybytes}, {B, bcbytes}, {C, bcbytes}, {dt, dtbytes},
                            {A, hbytes}, {D, hbytes}, {init_state, stbytes}, {z, ybytes}};
     const Span outs[] = {{y, ybytes}, {workspace, lo.total}, {final_state, stbytes}};
-    for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 8; ++i) {
-            if (o == 2 && i == 6) continue;   // final_state may alias init_state
-            if (overlaps(outs[o].p, outs[o].n, inputs[i].p, inputs[i].n)) return SSD_ERR_ALIAS;
-        }
-        for (int o2 = o + 1; o2 < 3; ++o2)
-            if (overlaps(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n)) return SSD_ERR_ALIAS;
-    }
+    if ((st = check_spans(inputs, outs, 2, 6)) != SSD_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
     float* cs = reinterpret_cast<float*>(ws + lo.cs);

@@ -182,6 +182,49 @@ def test_stage_argument_errors(lib):
                               P(0x10), P(0x20), P(0x8000), None, P(0x1000), None) == ALIAS
 
 
+def test_stage_outputs_must_not_overlap_inputs(lib):
+    """Each stage call refuses an output on top of an input or of another
+    output before any launch (every call below would otherwise reach a
+    launch, so a missed check shows up as a HIP error, not as ALIAS)."""
+    P = ctypes.c_void_p
+    M = 1 << 24                      # arrays 16 MiB apart: none of them overlaps another
+    a = [P((k + 1) * M) for k in range(12)]
+    # batch 1, 512 tokens, 4 heads, P 64, N 128, 1 group, chunk 256, bf16:
+    # x 256 KB, B/C 128 KB, dt 8 KB, cs/dtc rows 8 KB, S/Hin 128 KB, fp32 state 128 KB
+    dims = (1, 512, 4, 64, 128, 1, 256, 1)
+    cum = lambda dt, A, cs, dtc: lib.ssd_chunk_cumsum(1, 512, 4, 256, dt, A, cs, dtc, None)
+    assert cum(a[0], a[1], a[0], a[3]) == ALIAS                   # cs on dt
+    assert cum(a[0], a[1], a[2], P(a[1].value + 8)) == ALIAS      # dtc inside A's 16 bytes
+    assert cum(a[0], a[1], a[2], P(a[2].value + 4096)) == ALIAS   # dtc on cs
+    st = lambda x, B, cs, dtc, S: lib.ssd_chunk_state(*dims, x, B, cs, dtc, S, None)
+    assert st(a[0], a[1], a[2], a[3], P(a[0].value + 65536)) == ALIAS   # S inside x
+    assert st(a[0], a[1], a[2], a[3], a[3]) == ALIAS                    # S on dtc
+    cst = lambda x, B, dt, A, cs, dtc, S: lib.ssd_chunk_cumsum_state(*dims, x, B, dt, A, cs, dtc,
+                                                                      S, None)
+    assert cst(a[0], a[1], a[2], a[3], a[4], a[5], a[1]) == ALIAS     # S on B
+    assert cst(a[0], a[1], a[2], a[3], a[4], a[4], a[6]) == ALIAS     # dtc on cs
+    sp = lambda S, cs, init, Hin, fin: lib.ssd_state_passing(1, 512, 4, 64, 128, 256, 1, S, cs,
+                                                             init, Hin, fin, None)
+    assert sp(a[0], a[1], a[2], a[0], a[4]) == ALIAS                  # Hin on S
+    assert sp(a[0], a[1], a[2], a[3], a[3]) == ALIAS                  # final on Hin
+    assert sp(a[0], a[1], a[2], a[3], a[1]) == ALIAS                  # final on cs
+    assert sp(a[0], a[1], a[2], a[2], a[4]) == ALIAS                  # Hin on init
+    ws = lib.ssd_state_passing_seg_workspace_bytes(1, 4, 64, 128, 2)
+    seg = lambda S, Hin, fin, w: lib.ssd_state_passing_seg(1, 512, 4, 64, 128, 256, 2, 1, S, a[1],
+                                                           None, Hin, fin, w, ws, None)
+    assert seg(a[0], a[3], a[4], a[0]) == ALIAS                       # workspace on S
+    assert seg(a[0], a[3], a[4], a[3]) == ALIAS                       # workspace on Hin
+    scan = lambda x, B, cs, dtc, init, Hin, fin: lib.ssd_state_scan(*dims, x, B, cs, dtc, init,
+                                                                     Hin, fin, None)
+    assert scan(a[0], a[1], a[2], a[3], a[4], a[1], a[6]) == ALIAS    # Hin on B
+    assert scan(a[0], a[1], a[2], a[3], a[4], a[5], a[2]) == ALIAS    # final on cs
+    cscan = lambda y, Hin, D: lib.ssd_chunk_scan(*dims, a[0], a[1], a[2], a[3], a[4], Hin, D, y,
+                                                 None)
+    assert cscan(a[5], a[5], None) == ALIAS                           # y on Hin
+    assert cscan(a[3], a[5], None) == ALIAS                           # y on cs
+    assert cscan(a[6], a[5], a[6]) == ALIAS                           # y on D
+
+
 def test_layer_argument_errors(lib):
     P = ctypes.c_void_p
 
