@@ -53,6 +53,9 @@ KERNEL_SOURCES = {
     "state_passing": "state_passing.hip",
     "chunk_scan": "chunk_scan.hip",
     "state_scan": "state_scan.hip",
+    "chunk_state_runs": "chunk_state.hip",
+    "run_passing": "state_passing.hip",
+    "chunk_scan_runs": "chunk_scan.hip",
     "ssm_step": "ssm_step.hip",
     "layer_in": "layer.hip",
     "layer_dt": "layer.hip",
@@ -66,11 +69,15 @@ def log(msg):
 
 
 # --------------------------------------------------------------- byte models
-def forward_model(b, L, H, P, N, G, Q):
+def forward_model(b, L, H, P, N, G, Q, K=0):
     """Algorithmic HBM bytes and flops of each kernel: every input read once,
-    every output written once (workspace intermediates included, S and Hin in
-    bf16).
-    state_scan does what chunk_state + state_passing do without S."""
+    every output written once (workspace intermediates included, S, Hin, T
+    and Hr in bf16).
+    state_scan does what chunk_state + state_passing do without S.  With a
+    run length K > 0, also the two-level path: chunk_state_runs writes one T
+    per chunk (and lam, rdec), run_passing reads the T ending each run and
+    writes one Hr per run, chunk_scan_runs reads the T of every chunk past a
+    run's first and each run's Hr once."""
     nc = -(-L // Q)
     tok = b * L
     x = tok * H * P * 2
@@ -88,6 +95,15 @@ def forward_model(b, L, H, P, N, G, Q):
         "chunk_scan": x + 2 * bc + 2 * rows + Hin + x,
         "state_scan": x + bc + 2 * rows + st + Hin + st,
     }
+    if K > 0:
+        nruns = -(-nc // K)
+        pn = P * N * 2
+        bytes_.update({
+            "chunk_state_runs": x + bc + dt + 2 * rows + S + b * H * nc * 4 + b * H * nruns * 4,
+            "run_passing": b * H * nruns * pn + b * H * nruns * 4 + st + b * H * nruns * pn + st,
+            "chunk_scan_runs": x + 2 * bc + 2 * rows + b * H * (nc - nruns) * pn + b * H * nruns * pn +
+                               b * H * nc * 4 + x,
+        })
     th = tok * H
     flops = {
         "chunk_cumsum": 2 * th,
@@ -97,6 +113,12 @@ def forward_model(b, L, H, P, N, G, Q):
         "chunk_scan": ((Q + 1) * P + 2 * N * P) * th + (Q + 1) * N * tok * G,  # causal-exact
         "state_scan": 2 * P * N * th + 2 * b * H * nc * P * N,
     }
+    if K > 0:
+        flops.update({
+            "chunk_state_runs": flops["chunk_state_cumsum"] + 2 * b * H * nc * P * N,
+            "run_passing": 2 * b * H * (-(-nc // K)) * P * N,
+            "chunk_scan_runs": flops["chunk_scan"] + 2 * b * H * nc * P * N,
+        })
     return bytes_, flops
 
 
@@ -196,18 +218,23 @@ def time_forward(ssd, g, y, fin, ws, chunk, steps, warmup, zoh=False):
     return start.elapsed_time(end) / steps, wall
 
 
-def forward_kernels(dims):
+def forward_kernels(dims, K=0):
     """The kernels ssd_forward runs at these sizes, by the names of the stage
-    calls that launch the same kernels: chunk state with the cumsum inside
-    (ssd_chunk_cumsum_state, one launch where a group's head count is even),
-    state passing and chunk_scan."""
+    calls that launch the same kernels: with a run length K > 0 (what
+    ssd_forward_run_chunks reports) the two-level path (chunk states over
+    runs, the chain over runs, the chunk scan forming the entering states);
+    else chunk state with the cumsum inside (ssd_chunk_cumsum_state, one
+    launch where a group's head count is even), state passing and
+    chunk_scan."""
     b, L, H, P, N, G, Q = dims
+    if K > 0:
+        return ["chunk_state_runs", "run_passing", "chunk_scan_runs"]
     fused = P == 64 and N == 128 and Q in (64, 128, 256) and (H // G) % 2 == 0
     return (["chunk_state_cumsum"] if fused else ["chunk_cumsum", "chunk_state"]) + \
         ["state_passing", "chunk_scan"]
 
 
-def time_stages(ssd, g, y, fin, dims, steps):
+def time_stages(ssd, g, y, fin, dims, steps, K=0):
     """Average duration of each kernel, from HIP events recorded on the
     stream the stage calls are launched on (torch's current stream): first
     the forward's own kernels in the forward's order (chunk state with the
@@ -231,6 +258,16 @@ def time_stages(ssd, g, y, fin, dims, steps):
     p = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
     names = ["chunk_state_cumsum", "state_passing", "chunk_scan", "chunk_cumsum", "chunk_state",
              "state_scan"]
+    groups = [(0, 1, 2), (3, 4, 5)]
+    if K > 0:   # the forward's two-level path first; the per-chunk trio as a stage group
+        nruns = -(-nc // K)
+        T_t = torch.empty((b, H, nc, P, N), dtype=torch.bfloat16, device=dev)
+        Hr_t = torch.empty((b, H, nruns, P, N), dtype=torch.bfloat16, device=dev)
+        lam_t = torch.empty((b, H, nc), dtype=torch.float32, device=dev)
+        rdec_t = torch.empty((b, H, nruns), dtype=torch.float32, device=dev)
+        T, Hr, lam, rdec = (ctypes.c_void_p(t.data_ptr()) for t in (T_t, Hr_t, lam_t, rdec_t))
+        names += ["chunk_state_runs", "run_passing", "chunk_scan_runs"]
+        groups = [(6, 7, 8), (0, 1, 2), (3, 4, 5)]
     calls = [
         lambda: lib.ssd_chunk_cumsum_state(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), p(g["dt"]),
                                            p(g["A"]), cs, dtc, S, stream),
@@ -242,14 +279,23 @@ def time_stages(ssd, g, y, fin, dims, steps):
         lambda: lib.ssd_state_scan(b, L, H, P, N, G, Q, 1, p(g["x"]), p(g["B"]), cs, dtc,
                                    p(g["init"]), Hin, p(fin), stream),
     ]
+    if K > 0:
+        calls += [
+            lambda: lib.ssd_chunk_state_runs(b, L, H, P, N, G, Q, 1, K, p(g["x"]), p(g["B"]),
+                                             p(g["dt"]), p(g["A"]), cs, dtc, T, lam, rdec, stream),
+            lambda: lib.ssd_run_passing(b, L, H, P, N, Q, 1, K, T, rdec, p(g["init"]), Hr, p(fin),
+                                        stream),
+            lambda: lib.ssd_chunk_scan_runs(b, L, H, P, N, G, Q, 1, K, p(g["x"]), p(g["B"]),
+                                            p(g["C"]), cs, dtc, T, Hr, lam, p(g["D"]), p(y), stream),
+        ]
     for f in calls:            # warm
         assert f() == 0
     torch.cuda.synchronize()
     out = {}
     # the forward's three kernels on their own, back to back: what each finds
-    # in the caches is what it finds inside ssd_forward; then the stand-alone
-    # stage kernels in a loop of their own
-    for group in ((0, 1, 2), (3, 4, 5)):
+    # in the caches is what it finds inside ssd_forward; then each other group
+    # of stage kernels in a loop of its own
+    for group in groups:
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(group) + 1)]
               for _ in range(steps)]
         for k in range(steps):
@@ -532,7 +578,7 @@ def profile_loop(k: int):
     for _ in range(k):   # the forward itself, so the trace holds its kernels as it runs them
         ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], Q, g["init"], y=y,
                         final_state=fin, workspace=ws)
-    time_stages(ssd, g, y, fin, dims, k)
+    time_stages(ssd, g, y, fin, dims, k, ssd.forward_run_chunks(*dims, torch.bfloat16))
     from mamba_ssd_scan_02_amd.workloads import DECODE_B256 as dspec
     from mamba_ssd_scan_02_amd.workloads import make_decode_static, make_decode_step
     st = make_decode_static(dspec)
@@ -552,6 +598,12 @@ def profile_loop(k: int):
 
 
 def _short_kernel(name: str) -> str:
+    if "chunk_state_runs_kernel" in name:
+        return "chunk_state_runs"     # chunk states over runs (two-level path)
+    if "run_passing_kernel" in name:
+        return "run_passing"          # the chain over runs
+    if "chunk_scan_paired_kernel<true>" in name:
+        return "chunk_scan_runs"      # chunk scan forming the entering states
     if "chunk_state" in name and ", true>" in name:
         return "chunk_state_cumsum"   # chunk state with the cumsum inside
     if "state_walk" in name:
@@ -655,7 +707,10 @@ def summarize_counters(d_fetch: str, d_write: str, out_dir: str, cmd_fetch: str,
     b, L, H, P, N, G, Q = (MAMBA2_2P7B.batch, MAMBA2_2P7B.seqlen, MAMBA2_2P7B.nheads,
                            MAMBA2_2P7B.headdim, MAMBA2_2P7B.dstate, MAMBA2_2P7B.ngroups,
                            MAMBA2_2P7B.chunk)
-    alg, _ = forward_model(b, L, H, P, N, G, Q)
+    import mamba_ssd_scan_02_amd as ssd
+    import torch
+    alg, _ = forward_model(b, L, H, P, N, G, Q,
+                           ssd.forward_run_chunks(b, L, H, P, N, G, Q, torch.bfloat16))
     alg.update(layer_model(b, L, H, P, N, G, LAYER_K))
     db = DECODE_B256
     alg["ssm_step"] = (db.batch * db.nheads * db.headdim * db.dstate * 4 * 2 +
@@ -825,9 +880,10 @@ def main():
     log(f"[bench] forward {ms * 1e3:.1f} us/step, {tokens_per_s:.4g} tokens/s")
 
     log("[bench] per-kernel event timing")
-    k_us = time_stages(ssd, g, y, fin, dims, max(args.steps, 10))
-    kbytes, kflops = forward_model(*dims)
-    path = forward_kernels(dims)
+    K = ssd.forward_run_chunks(*dims, torch.bfloat16)
+    k_us = time_stages(ssd, g, y, fin, dims, max(args.steps, 10), K)
+    kbytes, kflops = forward_model(*dims, K)
+    path = forward_kernels(dims, K)
     kernels = {}
     for n, us in k_us.items():
         gbs = kbytes[n] / (us * 1e-6) / 1e9
@@ -862,7 +918,7 @@ def main():
         "roofline": roofline,
         "path": {"hbm_frac_of_compulsory_bytes": round(comp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_frac_algorithmic_flops": round(flops_total / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                 "compulsory_bytes": comp, "forward_kernels": path,
+                 "compulsory_bytes": comp, "forward_kernels": path, "run_chunks": K,
                  "forward_kernel_bytes": sum(kbytes[n] for n in path),
                  "forward_kernel_event_sum_us": round(sum(k_us[n] for n in path), 2),
                  "algorithmic_flops": flops_total, "wall_s_timed_region": round(wall, 4)},
@@ -883,7 +939,8 @@ def main():
         dims2 = (s2.batch, s2.seqlen, s2.nheads, s2.headdim, s2.dstate, s2.ngroups, s2.chunk)
         out["forward_130m"] = {"workload": s2.name, "us_per_step": round(ms2 * 1e3, 2),
                                "tokens_per_s": round(s2.batch * s2.seqlen / (ms2 * 1e-3), 1),
-                               "forward_kernels": forward_kernels(dims2)}
+                               "forward_kernels": forward_kernels(
+                                   dims2, ssd.forward_run_chunks(*dims2, torch.bfloat16))}
         del g2, y2, f2, ws2
         # one sequence of 1,048,576 tokens (8 groups of 4 heads): few steps,
         # its seeded inputs take most of this leg's time to draw on the host
@@ -902,7 +959,8 @@ def main():
         dims4 = (s4.batch, s4.seqlen, s4.nheads, s4.headdim, s4.dstate, s4.ngroups, s4.chunk)
         out["forward_long"] = {"workload": s4.name, "us_per_step": round(ms4 * 1e3, 2),
                                "tokens_per_s": round(s4.batch * s4.seqlen / (ms4 * 1e-3), 1),
-                               "steps": 5, "forward_kernels": forward_kernels(dims4)}
+                               "steps": 5, "forward_kernels": forward_kernels(
+                                   dims4, ssd.forward_run_chunks(*dims4, torch.bfloat16))}
         del g4, y4, f4, ws4
     log("[bench] zero-order-hold forward")
     ms_zoh, _ = time_forward(ssd, g, y, fin, ws, Q, args.steps, args.warmup, zoh=True)

@@ -107,7 +107,11 @@ const char* ssd_status_str(int32_t status);
  *     Hin  [B][H][nc][P][N]    state entering each chunk
  * S and Hin are in the storage type (bf16 for bf16, fp32 for fp32): each is
  * written once and read once, as a summand of the fp32 carried state (S) or
- * a matrix operand (Hin); the carried state itself stays fp32.
+ * a matrix operand (Hin); the carried state itself stays fp32.  Where the
+ * two-level recurrence between chunks applies (see ssd_chunk_state_runs) the
+ * forward carves the same workspace as cs, dtc, T [B][H][nc][P][N],
+ * Hr [B][H][nruns][P][N], lam [B][H][nc], rdec [B][H][nruns] instead, and the
+ * size returned is the larger of the two layouts.
  */
 size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
                                    int64_t headdim, int64_t dstate, int64_t ngroups,
@@ -119,7 +123,9 @@ size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
  * chunk length `chunk` (see the block-algorithm sources above).  Runs, in
  * order on `stream`: ssd_chunk_cumsum, ssd_chunk_state, ssd_state_passing,
  * ssd_chunk_scan (the cumsum inside the chunk-state launch where the
- * paired-head matrix-core kernel applies).
+ * paired-head matrix-core kernel applies); where the two-level recurrence
+ * applies (bf16, P = 64, N = 128, chunk 256, an even head count per group)
+ * ssd_chunk_state_runs, ssd_run_passing and ssd_chunk_scan_runs instead.
  *   D           may be NULL: no skip term.
  *   init_state  may be NULL: zero initial state.  When given it is decayed by
  *               exp(dt_0 A) at the first token, like any carried state.
@@ -299,6 +305,56 @@ int32_t ssd_state_passing_seg(int64_t batch, int64_t seqlen, int64_t nheads, int
                               const void* S, const float* cs, const float* init_state, void* Hin,
                               float* final_state, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * The two-level recurrence between chunks that ssd_forward runs where it
+ * applies (bf16, P = 64, N = 128, chunk 256, an even number of heads per
+ * group; SSD_ERR_UNSUPPORTED elsewhere).  Two steps of the linear recurrence
+ * H_{c+1} = exp(Acs_last,c) H_c + S_c merge into one step of the same kind
+ * (page "State Space Model", book.paithon.it, section "Dai sistemi dinamici a
+ * Mamba", the parallel scan), so with the chunks cut into runs of
+ * run_chunks = K consecutive chunks (run r: chunks rK .. min(rK + K, nc) - 1,
+ * nruns = ceil(nc / K); K in 1 .. 65536):
+ *     T_c    = the state after chunk c from a zero state at its run's start,
+ *     lam_c  = the summed decay (log2 units, as cs) of the run's chunks before c,
+ *     rdec_r = the summed decay (log2 units) of run r's chunks,
+ *     Hr_0   = init (or 0),  Hr_{r+1} = exp2(rdec_r) Hr_r + T_{last chunk of r},
+ *     Hin_c  = Hr_r at a run's first chunk, else T_{c-1} + exp2(lam_c) Hr_r,
+ *     final  = exp2(rdec_last) Hr_last + T_{nc-1}.
+ * Only every K-th state crosses memory twice; the per-chunk S and Hin never do.
+ */
+
+/* The run length K ssd_forward uses at these sizes (2 to 16: the longest
+ * whose run walks still fill two rounds of the device's CUs), or 0 where it
+ * keeps the per-chunk stages (unsupported sizes included).  The stage calls
+ * below with this K run exactly the forward's kernels. */
+int64_t ssd_forward_run_chunks(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype);
+
+/* cs and dtc as ssd_chunk_cumsum; T [B][H][nc][P][N] (dtype, accumulated in
+ * fp32 and rounded once), lam [B][H][nc] and rdec [B][H][nruns] (fp32). */
+int32_t ssd_chunk_state_runs(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                             int64_t run_chunks, const void* x, const void* B, const float* dt,
+                             const float* A, float* cs, float* dtc, void* T, float* lam, float* rdec,
+                             hipStream_t stream);
+
+/* Hr [B][H][nruns][P][N] (dtype; the chain runs in fp32) and final_state
+ * (fp32, may be NULL) from T and rdec; init_state may be NULL and may alias
+ * final_state. */
+int32_t ssd_run_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t chunk, int32_t dtype, int64_t run_chunks,
+                        const void* T, const float* rdec, const float* init_state, void* Hr,
+                        float* final_state, hipStream_t stream);
+
+/* y as ssd_chunk_scan, with each chunk's entering state formed from T, Hr
+ * and lam as above (T_{c-1} + exp2(lam_c) Hr_r evaluated in fp32 and rounded
+ * once to dtype). */
+int32_t ssd_chunk_scan_runs(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                            int64_t run_chunks, const void* x, const void* B, const void* C,
+                            const float* cs, const float* dtc, const void* T, const void* Hr,
+                            const float* lam, const float* D, void* y, hipStream_t stream);
 
 /* Hin and final_state straight from x, B, cs and dtc: what ssd_chunk_state
  * followed by ssd_state_passing compute, in one pass that keeps the running

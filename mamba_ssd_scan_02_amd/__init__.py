@@ -20,6 +20,10 @@ from .ssd import (  # noqa: F401
     library_path,
     load,
     n_chunks,
+    chunk_scan_runs,
+    chunk_state_runs,
+    forward_run_chunks,
+    run_passing,
     ssd_forward,
     ssd_layer,
     ssm_step,
@@ -35,5 +39,6 @@ __all__ = [
     "ssd_forward", "ssm_step", "workspace_bytes", "workspace_regions", "chunk_cumsum",
     "chunk_cumsum_state", "chunk_state", "state_passing", "state_scan", "chunk_scan", "load", "library_path", "abi_version",
     "status_str", "SSDError", "n_chunks", "DTYPE_F32", "DTYPE_BF16", "ABI_VERSION", "layer_in",
-    "layer_out", "ssd_layer", "state_passing_seg",
+    "layer_out", "ssd_layer", "state_passing_seg", "chunk_state_runs", "run_passing",
+    "chunk_scan_runs", "forward_run_chunks",
 ]

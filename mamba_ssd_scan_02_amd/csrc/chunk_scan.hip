@@ -315,15 +315,30 @@ __device__ __forceinline__ int stage_off(int r, int c) {
 constexpr int kIssueOrder[kCopies] = {6, 0, 1, 2, 3, 4, 5};
 }  // namespace rpl
 
-// One wave of the paired kernel; ROLE 0 = lead, 1 = helper.
-template <int ROLE>
+// The state entering a chunk from the two-level recurrence between chunks
+// (runs of K chunks; chunk_state_runs_kernel): Hin_c = T_{c-1} + exp2(lam_c)
+// Hr_r past a run's first chunk, Hr_r at it.  The slot's state rows then
+// come from T_{c-1} (or Hr_r) by the same copies that bring Hin, and the wave
+// that copied a piece of them adds exp2(lam_c) times the same piece of Hr_r
+// (loaded into registers with the copies, a head ahead) once its copies have
+// landed, rounding once to bf16, before the barrier that opens the head.
+struct RunState {
+    const bf16_t* Hr;    // [B][H][nruns][P][N], storage type
+    const float* lam;    // [B][H][nc]
+    int K, nruns;
+};
+
+// One wave of the paired kernel; ROLE 0 = lead, 1 = helper.  RUNS: the
+// carried state is formed from the two-level recurrence's T (passed as Hin)
+// and Hr (RunState) instead of read whole.
+template <int ROLE, bool RUNS>
 __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm,
                                            const bf16_t* __restrict__ Cm, const float* __restrict__ cs,
                                            const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
                                            const float* __restrict__ D, const bf16_t* __restrict__ z,
                                            bf16_t* __restrict__ y, int L, int H, int G, int nc, int b,
                                            int c, int g, int h0, int cnt, int wave, int lane,
-                                           SSD_LDS char* sm) {
+                                           SSD_LDS char* sm, const RunState& rs) {
     using namespace rpl;
     constexpr int Q = 256, P = 64, N = 128;
     constexpr int NB = ROLE == 0 ? 5 : 4;       // blocks of this wave
@@ -357,14 +372,35 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
     // the first four blocks of the previous head (kIssueOrder), so that a
     // wave held at issue by a full memory pipeline leaves its SIMD to the
     // other wave and the last copy still has most of a head to land.
+    // RUNS: the run of chunk c, whether c is past the run's first chunk (then
+    // the slot takes T_{c-1} and Hr is added), and the next head's Hr pieces
+    // and lam_c, loaded with its copies
+    const int run = RUNS ? c / rs.K : 0;
+    const bool comb = RUNS && c % rs.K != 0;
+    uint4 hrp[2] = {};
+    float lamp = 0.0f;
+    auto state_tile = [&](int h) {
+        if (RUNS) {
+            const int64_t bh = (int64_t)b * H + h;
+            return comb ? Hin + (bh * nc + c - 1) * (int64_t)(P * N)
+                        : rs.Hr + (bh * rs.nruns + run) * (int64_t)(P * N);
+        }
+        return Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N);
+    };
     auto issue_part = [&](int k, SSD_LDS char* s, int m) {
         const int h = h0 + k;
         if (m < 4) {
             const __amdgpu_buffer_rsrc_t rx = make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, xrecord);
             dma16_rs(rx, xo0 + (uint32_t)m * xstep, s + kX + (wave + 8 * m) * 1024);
         } else if (m < 6) {
-            const __amdgpu_buffer_rsrc_t rh =
-                make_rs(Hin + (((int64_t)b * H + h) * nc + c) * (int64_t)(P * N), P * N * 2);
+            if (comb && m == 4) {
+                const int64_t bh = (int64_t)b * H + h;
+                const char* hr = reinterpret_cast<const char*>(rs.Hr + (bh * rs.nruns + run) * (int64_t)(P * N));
+                hrp[0] = *reinterpret_cast<const uint4*>(hr + ho[0]);
+                hrp[1] = *reinterpret_cast<const uint4*>(hr + ho[1]);
+                lamp = rs.lam[bh * nc + c];
+            }
+            const __amdgpu_buffer_rsrc_t rh = make_rs(state_tile(h), P * N * 2);
             dma16_rs(rh, ho[m - 4], s + kH + (wave + 8 * (m - 4)) * 1024);
         } else {
             const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
@@ -502,6 +538,22 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
     SSD_LDS float* const rfo = (SSD_LDS float*)(sm + kRf) + 160 * wave;
     for (int k = 0; k < cnt; ++k) {
         wait_vmcnt<0>();
+        if (comb) {
+            // this wave's two landed pieces of T_{c-1}: + exp2(lam_c) Hr_r
+            const float lf = fast_exp2(lamp);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                SSD_LDS u32x4v* q = (SSD_LDS u32x4v*)(sm + (k & 1) * kSlot + kH + (wave + 8 * m) * 1024) + lane;
+                const u32x4v t = *q;
+                const u32x4v hv = __builtin_bit_cast(u32x4v, hrp[m]);
+                u32x4v o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = pack_bf16x2(fmaf(lf, bf16_bits_to_f32(hv[e] & 0xffffu), bf16_bits_to_f32(t[e] & 0xffffu)),
+                                       fmaf(lf, bf16_bits_to_f32(hv[e] >> 16), bf16_bits_to_f32(t[e] >> 16)));
+                *q = o;
+            }
+        }
         barrier_lds();
         // every wave is past head k - 1: its slot takes this wave's tile of
         // head k - 1 on its way out, then head k + 1, copied during this
@@ -620,11 +672,12 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
     wait_vmcnt<0>();
 }
 
+template <bool RUNS>
 __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
     const float* __restrict__ D, const bf16_t* __restrict__ z, bf16_t* __restrict__ y, int L, int H,
-    int G, int nc, int hg, int nsplit) {
+    int G, int nc, int hg, int nsplit, RunState rs) {
     __shared__ __align__(16) char smem[rpl::kBytes];
     const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = (int)(wg % (uint32_t)nsplit);
@@ -640,9 +693,9 @@ __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     __builtin_assume(wave >= 0 && wave < 8);
     SSD_LDS char* const sm = (SSD_LDS char*)lds(smem);
     if (wave < 4)
-        paired_run<0>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
+        paired_run<0, RUNS>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm, rs);
     else
-        paired_run<1>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm);
+        paired_run<1, RUNS>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1054,9 +1107,9 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         chunk_scan_runs(d, &hg, &nsplit);
         const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
         if (d.chunk == 256) {
-            chunk_scan_paired_kernel<<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D,
-                                                                 static_cast<const bf16_t*>(z), yb, L, H, G,
-                                                                 nc, hg, nsplit);
+            chunk_scan_paired_kernel<false><<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D,
+                                                                        static_cast<const bf16_t*>(z), yb, L,
+                                                                        H, G, nc, hg, nsplit, RunState{});
             return hipGetLastError();   // the gate, if any, is inside
         }
         if (d.chunk == 64) {
@@ -1078,6 +1131,22 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
     if (e == hipSuccess && z)
         e = launch_layer_out(d.batch * d.seqlen * d.nheads * d.headdim, dtype, y, z, y, stream);
     return e;
+}
+
+hipError_t launch_chunk_scan_runs(const Dims& d, int K, const void* x, const void* B, const void* C,
+                                  const float* cs, const float* dtc, const void* T, const void* Hr,
+                                  const float* lam, const float* D, void* y, hipStream_t stream,
+                                  const void* z) {
+    const int L = (int)d.seqlen, H = (int)d.nheads, G = (int)d.ngroups, nc = (int)d.nchunks;
+    int hg = 0, nsplit = 0;
+    chunk_scan_runs(d, &hg, &nsplit);
+    const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
+    const RunState rs{static_cast<const bf16_t*>(Hr), lam, K, (nc + K - 1) / K};
+    chunk_scan_paired_kernel<true><<<blocks, 512, 0, stream>>>(
+        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), cs, dtc,
+        static_cast<const bf16_t*>(T), D, static_cast<const bf16_t*>(z), static_cast<bf16_t*>(y), L, H, G, nc,
+        hg, nsplit, rs);
+    return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -333,7 +333,7 @@ __device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, in
                                                  const float* __restrict__ dtin,
                                                  const float* __restrict__ A, float* csw,
                                                  float* dtcw, int zoh, bool keepx, f32x16 (&acc)[HG][2],
-                                                 float (&cl)[HG]) {
+                                                 float (&cl)[HG], bool carry = false) {
     constexpr int W = 4, NT = Q / 32;
     constexpr int XR = 128 * HG;                         // bytes of a token's x row
     constexpr int DPS = 8 / W + BxhOffsets<W, HG>::XC;   // copies per wave per stage
@@ -422,8 +422,21 @@ __device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, in
     const int trow0 = 8 * (grp >> 1) + (rr >> 2);
     const int qcol = 16 * (grp & 1) + 4 * (rr & 3);
 
+    // from zero, or (carry: acc holds the state entering the chunk) from that
+    // state decayed through the chunk, exp2(cs_last) H, so that the products
+    // below leave the state after the chunk
 #pragma unroll
-    for (int e = 0; e < HG; ++e) acc[e][0] = acc[e][1] = f32x16{};
+    for (int e = 0; e < HG; ++e) {
+        if (carry) {
+            const float a = fast_exp2(cl[e]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[e][mt][r] *= a;
+        } else {
+            acc[e][0] = acc[e][1] = f32x16{};
+        }
+    }
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
         uint4* bst = bsr[jt % R];
@@ -515,6 +528,75 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
     }
     barrier_lds();   // every wave is past its last read of the ring
     stage_store_states<HG>(acc, st, dst, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Chunk states over runs of K consecutive chunks (the first level of a
+// two-level recurrence between chunks).  Two steps of the linear recurrence
+// H_{c+1} = exp2(cs_last,c) H_c + S_c merge into one step of the same kind
+// (the parallel scan of page "State Space Model", section "Dai sistemi
+// dinamici a Mamba"), so the state entering chunk c of run r splits into the
+// part formed inside the run from a zero start and the run's entering state
+// decayed to chunk c:  Hin_c = T_{c-1} + exp2(lam_c) Hr_r  (c past the run's
+// first chunk; Hin = Hr_r at the first), where
+//     T_c   = the state after chunk c from zero at the run's start,
+//     lam_c = the summed log2 decay of the run's chunks before c,
+//     rdec_r = the summed log2 decay of the whole run.
+// One workgroup (4 waves) per (batch, run, head pair of one group) walks the
+// run's chunks with the paired-head chunk state above (the cumsum in its
+// prologue), carrying the state in the MFMA accumulators, decayed by each
+// chunk's own decay before the chunk's products add onto it; after every
+// chunk it stores T_c (bf16, staged through the idle ring as whole rows) and
+// lam_c, after the run rdec_r.  The run's entering states Hr then come from a
+// chain over runs (state_passing.hip), and chunk_scan forms Hin_c from T_{c-1}
+// and Hr_r itself, so neither the per-chunk S nor the per-chunk Hin reaches
+// memory.
+template <int Q, int HG>
+__global__ __launch_bounds__(256, 2) void chunk_state_runs_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, bf16_t* __restrict__ T,
+    float* __restrict__ lam, float* __restrict__ rdec, int L, int H, int G, int nc, int K, int nruns,
+    const float* __restrict__ dtin, const float* __restrict__ A, float* csw, float* dtcw, int zoh,
+    int keep_run, int keep_k) {
+    constexpr int P = 64, N = 128;
+    __shared__ StateSmem<Q, HG> sm;
+    const int HP = H / HG;
+    const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int h0 = HG * (int)(wg % (uint32_t)HP);
+    const int br = (int)(wg / (uint32_t)HP);
+    const int r = br % nruns, b = br / nruns;
+    const int c0 = r * K, c1 = min(c0 + K, nc);
+    const bool keepx = (h0 % (H / G)) % keep_run < keep_k;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    static_assert(sizeof(sm.bsr) >= P * N * 2 && sizeof(sm.xsr) >= (HG - 1) * P * N * 2,
+                  "the ring holds the T tiles");
+    SSD_LDS char* st[HG];
+#pragma unroll
+    for (int e = 0; e < HG; ++e)
+        st[e] = e == 0 ? (SSD_LDS char*)lds(&sm.bsr[0][0]) : (SSD_LDS char*)lds(&sm.xsr[0][0]) + (e - 1) * P * N * 2;
+    f32x16 acc[HG][2];
+    float cl[HG], lsum[HG];
+#pragma unroll
+    for (int e = 0; e < HG; ++e) lsum[e] = 0.0f;
+    for (int c = c0; c < c1; ++c) {
+        chunk_state_pair<Q, HG, true>(sm, b, c, h0, x, Bm, nullptr, nullptr, L, H, G, nc, dtin, A, csw,
+                                      dtcw, zoh, keepx, acc, cl, c > c0);
+        bf16_t* dst[HG];
+#pragma unroll
+        for (int e = 0; e < HG; ++e) {
+            const int64_t bhc = ((int64_t)b * H + h0 + e) * nc + c;
+            dst[e] = T + bhc * (int64_t)(P * N);
+            if (tid == 0) lam[bhc] = lsum[e];
+            lsum[e] += cl[e];
+        }
+        barrier_lds();   // every wave is past its last read of the ring
+        stage_store_states<HG>(acc, st, dst, wave, lane);
+        barrier_lds();   // every wave has read its staged rows back before the ring refills
+    }
+    if (tid == 0) {
+#pragma unroll
+        for (int e = 0; e < HG; ++e) rdec[((int64_t)b * H + h0 + e) * nruns + r] = lsum[e];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -833,6 +915,48 @@ hipError_t launch_chunk_state_fused(const Dims& d, const void* x, const void* B,
         case 128: chunk_state_mfmah_kernel<128, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z, krun, kk); break;
         default: chunk_state_mfmah_kernel<256, kStateHeads, true><<<hblocks, 256, 0, stream>>>(xb, bb, nullptr, nullptr, S, L, H, G, nc, dt, A, cs, dtc, z, krun, kk); break;
     }
+    return hipGetLastError();
+}
+
+bool state_runs_apply(int32_t dtype, const Dims& d) {
+    return chunk_state_fuses_cumsum(dtype, d) && d.chunk == 256;
+}
+
+// Run length for ssd_forward, or 0 to keep the per-chunk path.  Longer runs
+// shorten the chain over runs and keep more states out of memory, but leave
+// fewer workgroups for the run walks, whose chunks are sequential: take the
+// longest K in {16, 8, 4, 2} whose grid still fills two rounds of the
+// machine (two workgroups per CU).  Measured (chunk-state runs + run chain +
+// chunk scan, one box): 2.7B shape K = 2/4/8/16: 346/341/359/371 us against
+// 361 us for the per-chunk path (K = 4 taken); 1M-token sequence 5,728 /
+// 5,588 / 5,505 / 5,447 us against 5,948 (K = 16); the 130M shape has 96
+// head-pair sequences of 8 chunks, too few workgroups at any K (73 us at K = 2
+// against 63), and keeps the per-chunk path.
+int state_run_chunks(const Dims& d) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const double chains = (double)d.batch * (double)(d.nheads / kStateHeads);
+    for (int K = 16; K >= 2; K /= 2) {
+        const double wgs = chains * (double)((d.nchunks + K - 1) / K);
+        if (wgs >= 2.0 * 2.0 * cus) return K;
+    }
+    return 0;
+}
+
+hipError_t launch_chunk_state_runs(const Dims& d, int K, const void* x, const void* B,
+                                   const float* dt, const float* A, bool zoh, float* cs, float* dtc,
+                                   void* T, float* lam, float* rdec, hipStream_t stream) {
+    const int nc = (int)d.nchunks, nruns = (nc + K - 1) / K;
+    const unsigned blocks = (unsigned)(d.batch * nruns * (d.nheads / kStateHeads));
+    int krun = 1, nsplit = 1;
+    chunk_scan_runs(d, &krun, &nsplit);
+    chunk_state_runs_kernel<256, kStateHeads><<<blocks, 256, 0, stream>>>(
+        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(B), static_cast<bf16_t*>(T), lam,
+        rdec, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, nc, K, nruns, dt, A, cs, dtc, zoh ? 1 : 0,
+        krun, x_keep_positions(d));
     return hipGetLastError();
 }
 

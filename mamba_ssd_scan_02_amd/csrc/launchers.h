@@ -64,6 +64,24 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
                              const void* C, const float* cs, const float* dtc, const void* Hin,
                              const float* D, void* y, hipStream_t stream, const void* z = nullptr);
 
+// Two-level recurrence between chunks (bf16 matrix-core path, chunk 256, an
+// even head count per group): chunk states over runs of K chunks (T, lam,
+// rdec, and the cumsum rows cs / dtc), a chain over the runs (Hr and the
+// final state), and the chunk scan forming each chunk's entering state from
+// T and Hr.  state_run_chunks gives the K ssd_forward uses (2 to 16), or 0
+// where the per-chunk path stays (too few workgroups for runs).
+bool state_runs_apply(int32_t dtype, const Dims& d);
+int state_run_chunks(const Dims& d);
+hipError_t launch_chunk_state_runs(const Dims& d, int K, const void* x, const void* B,
+                                   const float* dt, const float* A, bool zoh, float* cs, float* dtc,
+                                   void* T, float* lam, float* rdec, hipStream_t stream);
+hipError_t launch_run_passing(const Dims& d, int K, const void* T, const float* rdec, const float* init,
+                              void* Hr, float* final_state, hipStream_t stream);
+hipError_t launch_chunk_scan_runs(const Dims& d, int K, const void* x, const void* B, const void* C,
+                                  const float* cs, const float* dtc, const void* T, const void* Hr,
+                                  const float* lam, const float* D, void* y, hipStream_t stream,
+                                  const void* z = nullptr);
+
 // Chunk state and state passing walked per (batch, head pair) in one pass
 // (bf16 matrix-core path, chunk 128 or 256, an even head count per group).
 bool state_walk_applies(int32_t dtype, const Dims& d);

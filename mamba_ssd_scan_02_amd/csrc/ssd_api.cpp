@@ -92,6 +92,45 @@ bool workspace_layout(const Dims& d, int32_t dtype, Layout* lo) {
     return true;
 }
 
+// The same workspace carved for the two-level recurrence (runs of K >= 2
+// chunks): cs, dtc, T (one state per chunk), Hr (one per run), lam (one
+// float per chunk), rdec (one per run) -- never more than the layout above.
+struct RunLayout {
+    size_t cs, dtc, T, Hr, lam, rdec, total;
+};
+
+bool run_layout(const Dims& d, int32_t dtype, int64_t K, RunLayout* lo) {
+    size_t es;
+    if (!elem_size(dtype, &es) || K < 1) return false;
+    const size_t bh = (size_t)d.batch * (size_t)d.nheads;
+    const size_t nruns = (size_t)((d.nchunks + K - 1) / K);
+    const size_t pn = (size_t)d.headdim * (size_t)d.dstate * es;
+    const size_t rows = bh * (size_t)d.nchunks * (size_t)d.chunk * 4;
+    lo->cs = 0;
+    lo->dtc = align_up(rows);
+    lo->T = lo->dtc + align_up(rows);
+    lo->Hr = lo->T + align_up(bh * (size_t)d.nchunks * pn);
+    lo->lam = lo->Hr + align_up(bh * nruns * pn);
+    lo->rdec = lo->lam + align_up(bh * (size_t)d.nchunks * 4);
+    lo->total = lo->rdec + align_up(bh * nruns * 4);
+    return true;
+}
+
+// Bytes ssd_forward needs: the larger of the two layouts where the
+// two-level recurrence applies (a sequence of one or a few chunks needs more
+// for Hr than the per-chunk Hin it replaces).
+bool forward_workspace(const Dims& d, int32_t dtype, Layout* lo, size_t* total) {
+    if (!workspace_layout(d, dtype, lo)) return false;
+    *total = lo->total;
+    const int K = ssd::state_runs_apply(dtype, d) ? ssd::state_run_chunks(d) : 0;
+    if (K > 0) {
+        RunLayout rl;
+        if (!run_layout(d, dtype, K, &rl)) return false;
+        if (rl.total > *total) *total = rl.total;
+    }
+    return true;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
     const uintptr_t x0 = reinterpret_cast<uintptr_t>(a), x1 = x0 + na;
@@ -202,8 +241,17 @@ size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
     if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d) != SSD_OK) return 0;
     if (check_supported(dtype, d) != SSD_OK) return 0;
     Layout lo;
-    if (!workspace_layout(d, dtype, &lo)) return 0;
-    return lo.total;
+    size_t total;
+    if (!forward_workspace(d, dtype, &lo, &total)) return 0;
+    return total;
+}
+
+int64_t ssd_forward_run_chunks(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype) {
+    Dims d;
+    if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, &d) != SSD_OK) return 0;
+    if (check_supported(dtype, d) != SSD_OK || !ssd::state_runs_apply(dtype, d)) return 0;
+    return ssd::state_run_chunks(d);
 }
 
 static int32_t chunk_cumsum_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64_t chunk,
@@ -363,6 +411,86 @@ int32_t ssd_state_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     return hip_status(ssd::launch_state_scan(d, x, B, cs, dtc, init_state, Hin, final_state, stream));
 }
 
+// Shared checks of the three two-level stage calls.
+static int32_t runs_check(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                          int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                          int64_t run_chunks, Dims* d) {
+    int32_t st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, d);
+    if (st != SSD_OK) return st;
+    size_t es;
+    if (!elem_size(dtype, &es)) return SSD_ERR_UNSUPPORTED;
+    if (!ssd::state_runs_apply(dtype, *d)) return SSD_ERR_UNSUPPORTED;
+    if (run_chunks < 1 || run_chunks > 65536) return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+
+int32_t ssd_chunk_state_runs(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                             int64_t run_chunks, const void* x, const void* B, const float* dt,
+                             const float* A, float* cs, float* dtc, void* T, float* lam, float* rdec,
+                             hipStream_t stream) {
+    Dims d;
+    int32_t st = runs_check(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, run_chunks, &d);
+    if (st != SSD_OK) return st;
+    if (!x || !B || !dt || !A || !cs || !dtc || !T || !lam || !rdec) return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(T, 16) || !aligned(dt, 4) || !aligned(A, 4) ||
+        !aligned(cs, 4) || !aligned(dtc, 4) || !aligned(lam, 4) || !aligned(rdec, 4))
+        return SSD_ERR_ALIGN;
+    const Sizes z = sizes_of(d, 2);
+    const size_t nruns = (size_t)((d.nchunks + run_chunks - 1) / run_chunks);
+    const size_t bh = (size_t)d.batch * (size_t)d.nheads;
+    const Span in[] = {{x, z.x}, {B, z.bc}, {dt, z.dt}, {A, z.head}};
+    const Span out[] = {{cs, z.rows}, {dtc, z.rows}, {T, z.states}, {lam, bh * (size_t)d.nchunks * 4},
+                        {rdec, bh * nruns * 4}};
+    if ((st = check_spans(in, out)) != SSD_OK) return st;
+    return hip_status(ssd::launch_chunk_state_runs(d, (int)run_chunks, x, B, dt, A, false, cs, dtc, T, lam,
+                                                   rdec, stream));
+}
+
+int32_t ssd_run_passing(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t chunk, int32_t dtype, int64_t run_chunks,
+                        const void* T, const float* rdec, const float* init_state, void* Hr,
+                        float* final_state, hipStream_t stream) {
+    Dims d;
+    int32_t st = runs_check(batch, seqlen, nheads, headdim, dstate, 1, chunk, dtype, run_chunks, &d);
+    if (st != SSD_OK) return st;
+    if (!T || !rdec || !Hr) return SSD_ERR_NULL;
+    if (!aligned(T, 16) || !aligned(Hr, 16) || !aligned(rdec, 4) ||
+        (init_state && !aligned(init_state, 16)) || (final_state && !aligned(final_state, 16)))
+        return SSD_ERR_ALIGN;
+    const Sizes z = sizes_of(d, 2);
+    const size_t nruns = (size_t)((d.nchunks + run_chunks - 1) / run_chunks);
+    const size_t bh = (size_t)d.batch * (size_t)d.nheads;
+    const Span in[] = {{T, z.states}, {rdec, bh * nruns * 4}, {init_state, z.state32}};
+    const Span out[] = {{Hr, bh * nruns * (size_t)(d.headdim * d.dstate) * 2}, {final_state, z.state32}};
+    if ((st = check_spans(in, out, 1, 2)) != SSD_OK) return st;
+    return hip_status(ssd::launch_run_passing(d, (int)run_chunks, T, rdec, init_state, Hr, final_state, stream));
+}
+
+int32_t ssd_chunk_scan_runs(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
+                            int64_t run_chunks, const void* x, const void* B, const void* C,
+                            const float* cs, const float* dtc, const void* T, const void* Hr,
+                            const float* lam, const float* D, void* y, hipStream_t stream) {
+    Dims d;
+    int32_t st = runs_check(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, run_chunks, &d);
+    if (st != SSD_OK) return st;
+    if (!x || !B || !C || !cs || !dtc || !T || !Hr || !lam || !y) return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(T, 16) || !aligned(Hr, 16) ||
+        !aligned(y, 16) || !aligned(cs, 4) || !aligned(dtc, 4) || !aligned(lam, 4) || (D && !aligned(D, 4)))
+        return SSD_ERR_ALIGN;
+    const Sizes z = sizes_of(d, 2);
+    const size_t nruns = (size_t)((d.nchunks + run_chunks - 1) / run_chunks);
+    const size_t bh = (size_t)d.batch * (size_t)d.nheads;
+    const Span in[] = {{x, z.x},      {B, z.bc},       {C, z.bc},
+                       {cs, z.rows},  {dtc, z.rows},   {T, z.states},
+                       {Hr, bh * nruns * (size_t)(d.headdim * d.dstate) * 2},
+                       {lam, bh * (size_t)d.nchunks * 4}, {D, z.head}};
+    const Span out[] = {{y, z.x}};
+    if ((st = check_spans(in, out)) != SSD_OK) return st;
+    return hip_status(ssd::launch_chunk_scan_runs(d, (int)run_chunks, x, B, C, cs, dtc, T, Hr, lam, D, y, stream));
+}
+
 int32_t ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t dstate, int64_t ngroups, int64_t chunk, int32_t dtype,
                        const void* x, const void* B, const void* C, const float* cs,
@@ -398,8 +526,9 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     if ((st = check_supported(dtype, d)) != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     Layout lo;
-    if (!workspace_layout(d, dtype, &lo)) return SSD_ERR_SHAPE;
-    if (!workspace || workspace_bytes < lo.total) return SSD_ERR_WORKSPACE;
+    size_t wtotal;
+    if (!forward_workspace(d, dtype, &lo, &wtotal)) return SSD_ERR_SHAPE;
+    if (!workspace || workspace_bytes < wtotal) return SSD_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
         !aligned(workspace, 16) || !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
         (init_state && !aligned(init_state, 16)) || (final_state && !aligned(final_state, 16)) ||
@@ -420,16 +549,33 @@ static int32_t forward_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64
     // before it is written).
     const Span inputs[] = {{x, ybytes}, {B, bcbytes}, {C, bcbytes}, {dt, dtbytes},
                            {A, hbytes}, {D, hbytes}, {init_state, stbytes}, {z, ybytes}};
-    const Span outs[] = {{y, ybytes}, {workspace, lo.total}, {final_state, stbytes}};
+    const Span outs[] = {{y, ybytes}, {workspace, wtotal}, {final_state, stbytes}};
     if ((st = check_spans(inputs, outs, 2, 6)) != SSD_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
     float* cs = reinterpret_cast<float*>(ws + lo.cs);
     float* dtc = reinterpret_cast<float*>(ws + lo.dtc);
-    void* S = ws + lo.S;
-    void* Hin = ws + lo.Hin;
 
     hipError_t e;
+    const int K = ssd::state_runs_apply(dtype, d) ? ssd::state_run_chunks(d) : 0;
+    if (K > 0) {
+        // the two-level recurrence between chunks: chunk states over runs of
+        // K chunks, the chain over runs, and the chunk scan forming each
+        // chunk's entering state itself (neither S nor Hin in memory)
+        RunLayout rl;
+        if (!run_layout(d, dtype, K, &rl) || rl.total > wtotal) return SSD_ERR_SHAPE;
+        void* T = ws + rl.T;
+        void* Hr = ws + rl.Hr;
+        float* lam = reinterpret_cast<float*>(ws + rl.lam);
+        float* rdec = reinterpret_cast<float*>(ws + rl.rdec);
+        e = ssd::launch_chunk_state_runs(d, K, x, B, dt, A, zoh, cs, dtc, T, lam, rdec, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        e = ssd::launch_run_passing(d, K, T, rdec, init_state, Hr, final_state, stream);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        return hip_status(ssd::launch_chunk_scan_runs(d, K, x, B, C, cs, dtc, T, Hr, lam, D, y, stream, z));
+    }
+    void* S = ws + lo.S;
+    void* Hin = ws + lo.Hin;
     // chunk cumsum and chunk states (one launch where the paired-head kernel
     // applies), then the recurrence between chunks (the one-pass
     // ssd_state_scan measured slower than this pair at every shape tried)
@@ -469,8 +615,9 @@ int32_t ssd_forward_noalloc(int64_t batch, int64_t seqlen, int64_t nheads, int64
     if (st != SSD_OK) return st;
     if ((st = check_supported(dtype, d)) != SSD_OK) return st;
     Layout lo;
-    if (!workspace_layout(d, dtype, &lo)) return SSD_ERR_SHAPE;
-    if (lo.total > (size_t)SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    size_t total;
+    if (!forward_workspace(d, dtype, &lo, &total)) return SSD_ERR_SHAPE;
+    if (total > (size_t)SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     void* ws = nullptr;
     if ((st = scratch_address(&ws)) != SSD_OK) return st;

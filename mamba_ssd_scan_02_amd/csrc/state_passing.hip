@@ -148,8 +148,8 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
 //     [store h at hp], h <- exp2(lg_c) h + S_c,   c = 0 .. n - 1,
 // where S_c sits at src + c * sstep (elements of ST) and lg_c, the chunk's decay in
 // log2 units, at dec[c * dstep].  kStore writes the entering state of every
-// chunk (hp advances by sstep), non-temporally with kNT; kSum adds the lg_c
-// into *lsum.
+// chunk (hp advances by hstep, sstep when hstep is 0), non-temporally with
+// kNT; kSum adds the lg_c into *lsum.
 //
 // The ring holds the next PF chunks.  Its loads are unconditional: a load past
 // the last chunk re-reads the last chunk (always in bounds) and is never used.
@@ -160,7 +160,8 @@ __device__ __forceinline__ void store_vec(bf16_t* p, int64_t i, const Vec<VW>& r
 template <typename ST, typename HT, int PF, int VW, bool kStore, bool kSum, bool kNT = false>
 __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t sstep,
                                             const float* __restrict__ dec, int64_t dstep, int n,
-                                            HT* hp, Vec<VW>& h, float* lsum) {
+                                            HT* hp, Vec<VW>& h, float* lsum, int64_t hstep = 0) {
+    if (hstep == 0) hstep = sstep;
     RingSlot<ST, VW> buf[PF];
     float lg[PF];
 #pragma unroll
@@ -181,7 +182,7 @@ __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t 
             if (kSum) ls += lg[k];
             if (kStore) {
                 store_vec<VW, kNT>(hp, 0, h);
-                hp += sstep;
+                hp += hstep;
             }
             const Vec<VW> sv = buf[k].widen();
 #pragma unroll
@@ -199,7 +200,7 @@ __device__ __forceinline__ void walk_chunks(const ST* __restrict__ src, int64_t 
             if (kSum) ls += lg[k];
             if (kStore) {
                 store_vec<VW, kNT>(hp, 0, h);
-                hp += sstep;
+                hp += hstep;
             }
             const Vec<VW> sv = buf[k].widen();
 #pragma unroll
@@ -310,6 +311,59 @@ __global__ __launch_bounds__(256) void sp_seg_down_kernel(const HT* __restrict__
     walk_chunks<HT, HT, PF, VW, true, false>(S + base, (int64_t)pnv * VW,
                                              cs + (bh * nc + c0) * (int64_t)Q + (Q - 1), Q, n, Hin + base,
                                              h, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// The second level of the two-level recurrence whose first level is the
+// chunk state over runs of K chunks (chunk_state_runs_kernel): a chain over
+// the runs,
+//     Hr_0 = init,   Hr_{r+1} = exp2(rdec_r) Hr_r + T_{last chunk of run r},
+// writing every run's entering state Hr_r (storage type) and the final state
+// exp2(rdec_last) Hr_last + T_{nc-1} (fp32).  Full runs end at chunk
+// rK + K - 1, so their T are K chunks apart; the last run may be shorter and
+// ends at chunk nc - 1.
+template <typename HT, int PF, int VW>
+__global__ __launch_bounds__(256) void run_passing_kernel(const HT* __restrict__ T,
+                                                          const float* __restrict__ rdec,
+                                                          const float* init, HT* __restrict__ Hr,
+                                                          float* fin, int pnv, int nc, int K,
+                                                          int nruns) {
+    const int64_t bh = blockIdx.x;
+    const int off = blockIdx.y * 256 + threadIdx.x;
+    if (off >= pnv) return;
+    const int64_t idx = bh * pnv + off;
+    Vec<VW> h = start_state<VW>(init, idx);
+    const int64_t pn = (int64_t)pnv * VW;
+    const HT* tb = T + (bh * nc * (int64_t)pnv + off) * VW;
+    HT* hb = Hr + (bh * nruns * (int64_t)pnv + off) * VW;
+    if (nruns > 1)
+        walk_chunks<HT, HT, PF, VW, true, false>(tb + (int64_t)(K - 1) * pn, (int64_t)K * pn,
+                                                 rdec + bh * nruns, 1, nruns - 1, hb, h, nullptr, pn);
+    store_vec<VW>(hb, (int64_t)(nruns - 1) * pnv, h);
+    if (fin) {
+        const float a = fast_exp2(rdec[bh * nruns + nruns - 1]);
+        RingSlot<HT, VW> last;
+        last.load(tb + (int64_t)(nc - 1) * pn);
+        const Vec<VW> tv = last.widen();
+#pragma unroll
+        for (int e = 0; e < VW; ++e) h.v[e] = a * h.v[e] + tv.v[e];
+        store_vec<VW>(fin, idx, h);
+    }
+}
+
+hipError_t launch_run_passing(const Dims& d, int K, const void* T, const float* rdec, const float* init,
+                              void* Hr, float* final_state, hipStream_t stream) {
+    const int nc = (int)d.nchunks, nruns = (nc + K - 1) / K;
+    constexpr int VW = 4;
+    const int pnv = (int)(d.headdim * d.dstate / VW);
+    const dim3 grid((unsigned)(d.batch * d.nheads), (unsigned)((pnv + 255) / 256));
+    const bf16_t* t = static_cast<const bf16_t*>(T);
+    bf16_t* hr = static_cast<bf16_t*>(Hr);
+    if (nruns > 64)
+        run_passing_kernel<bf16_t, 16, VW><<<grid, 256, 0, stream>>>(t, rdec, init, hr, final_state, pnv, nc, K, nruns);
+    else
+        run_passing_kernel<bf16_t, 4, VW><<<grid, 256, 0, stream>>>(t, rdec, init, hr, final_state, pnv, nc, K, nruns);
+    return hipGetLastError();
 }
 
 constexpr double kHinTemporalMaxBytes = 64.0 * 1024 * 1024;

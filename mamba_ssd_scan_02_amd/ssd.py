@@ -87,6 +87,14 @@ def load():
     lib.ssd_state_passing_seg_workspace_bytes.argtypes = [i64] * 5
     lib.ssd_state_passing_seg.restype = i32
     lib.ssd_state_passing_seg.argtypes = [i64] * 7 + [i32] + [vp] * 6 + [sz, vp]
+    lib.ssd_forward_run_chunks.restype = i64
+    lib.ssd_forward_run_chunks.argtypes = [i64] * 7 + [i32]
+    lib.ssd_chunk_state_runs.restype = i32
+    lib.ssd_chunk_state_runs.argtypes = [i64] * 7 + [i32, i64] + [vp] * 9 + [vp]
+    lib.ssd_run_passing.restype = i32
+    lib.ssd_run_passing.argtypes = [i64] * 6 + [i32, i64] + [vp] * 5 + [vp]
+    lib.ssd_chunk_scan_runs.restype = i32
+    lib.ssd_chunk_scan_runs.argtypes = [i64] * 7 + [i32, i64] + [vp] * 10 + [vp]
     lib.ssd_layer_in.restype = i32
     lib.ssd_layer_in.argtypes = [i64] * 7 + [i32] + [vp] * 9 + [vp]
     lib.ssd_layer_out.restype = i32
@@ -394,6 +402,83 @@ def chunk_scan(x, B, C, cs, dtc, Hin, D, chunk, y=None):
     _check("ssd_chunk_scan", lib.ssd_chunk_scan(batch, L, H, P, N, G, chunk, _dtype_code(x), _p(x),
                                                 _p(B), _p(C), _p(cs), _p(dtc), _p(Hin), _p(D),
                                                 _p(y), _stream(x.device)))
+    return y
+
+
+def forward_run_chunks(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype) -> int:
+    """The run length ssd_forward uses (0: the per-chunk stages) -- see
+    ssd_forward_run_chunks."""
+    code = dtype if isinstance(dtype, int) else (DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32)
+    return int(load().ssd_forward_run_chunks(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                             code))
+
+
+def chunk_state_runs(x, B, dt, A, chunk, run_chunks):
+    """(cs, dtc, T [batch, H, nc, P, N], lam [batch, H, nc], rdec [batch, H, nruns])
+    -- see ssd_chunk_state_runs (chunk states over runs of ``run_chunks``)."""
+    lib = load()
+    x = _dev(x, "x")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = n_chunks(L, chunk)
+    nruns = -(-nc // run_chunks)
+    _dev(B, "B", x.dtype, (batch, L, G, N), x.device)
+    _dev(dt, "dt", torch.float32, (batch, L, H), x.device)
+    _dev(A, "A", torch.float32, (H,), x.device)
+    cs = torch.empty((batch, H, nc, chunk), dtype=torch.float32, device=x.device)
+    dtc = torch.empty_like(cs)
+    T = torch.empty((batch, H, nc, P, N), dtype=x.dtype, device=x.device)
+    lam = torch.empty((batch, H, nc), dtype=torch.float32, device=x.device)
+    rdec = torch.empty((batch, H, nruns), dtype=torch.float32, device=x.device)
+    _check("ssd_chunk_state_runs",
+           lib.ssd_chunk_state_runs(batch, L, H, P, N, G, chunk, _dtype_code(x), run_chunks, _p(x),
+                                    _p(B), _p(dt), _p(A), _p(cs), _p(dtc), _p(T), _p(lam), _p(rdec),
+                                    _stream(x.device)))
+    return cs, dtc, T, lam, rdec
+
+
+def run_passing(T, rdec, seqlen, chunk, run_chunks, init_state=None, final_state=None):
+    """(Hr [batch, H, nruns, P, N] in T's dtype, final [batch, H, P, N] fp32)
+    -- see ssd_run_passing (the chain over runs)."""
+    lib = load()
+    T = _dev(T, "T")
+    batch, H, nc, P, N = T.shape
+    nruns = -(-nc // run_chunks)
+    _dev(rdec, "rdec", torch.float32, (batch, H, nruns), T.device)
+    _dev(init_state, "init_state", torch.float32, (batch, H, P, N), T.device)
+    Hr = torch.empty((batch, H, nruns, P, N), dtype=T.dtype, device=T.device)
+    if final_state is None:
+        final_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=T.device)
+    _dev(final_state, "final_state", torch.float32, (batch, H, P, N), T.device)
+    _check("ssd_run_passing",
+           lib.ssd_run_passing(batch, seqlen, H, P, N, chunk, _dtype_code(T), run_chunks, _p(T),
+                               _p(rdec), _p(init_state), _p(Hr), _p(final_state), _stream(T.device)))
+    return Hr, final_state
+
+
+def chunk_scan_runs(x, B, C, cs, dtc, T, Hr, lam, D, chunk, run_chunks, y=None):
+    """y [batch, L, H, P] in x's dtype -- see ssd_chunk_scan_runs (each chunk's
+    entering state formed from T and Hr)."""
+    lib = load()
+    x = _dev(x, "x")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = n_chunks(L, chunk)
+    nruns = -(-nc // run_chunks)
+    _dev(B, "B", x.dtype, (batch, L, G, N), x.device)
+    _dev(C, "C", x.dtype, (batch, L, G, N), x.device)
+    _dev(cs, "cs", torch.float32, (batch, H, nc, chunk), x.device)
+    _dev(dtc, "dtc", torch.float32, (batch, H, nc, chunk), x.device)
+    _dev(T, "T", x.dtype, (batch, H, nc, P, N), x.device)
+    _dev(Hr, "Hr", x.dtype, (batch, H, nruns, P, N), x.device)
+    _dev(lam, "lam", torch.float32, (batch, H, nc), x.device)
+    _dev(D, "D", torch.float32, (H,), x.device)
+    if y is None:
+        y = torch.empty_like(x)
+    _check("ssd_chunk_scan_runs",
+           lib.ssd_chunk_scan_runs(batch, L, H, P, N, G, chunk, _dtype_code(x), run_chunks, _p(x),
+                                   _p(B), _p(C), _p(cs), _p(dtc), _p(T), _p(Hr), _p(lam), _p(D),
+                                   _p(y), _stream(x.device)))
     return y
 
 

@@ -93,6 +93,62 @@ def state_passing(S, Acs, init=None):
     return Hin, h
 
 
+def run_states(S, Acs, K):
+    """First level of the two-level recurrence between blocks, runs of K
+    blocks (run r = blocks rK .. min(rK + K, nc) - 1).  Two steps of the
+    recurrence h <- a h + s merge into one step of the same kind (the
+    parallel scan of page "State Space Model", section "Dai sistemi dinamici
+    a Mamba"), so each run is scanned from a zero state on its own:
+        T[c]    = the state after block c from zero at its run's start
+        lam[c]  = summed decay (natural log) of the run's blocks before c
+        rdec[r] = summed decay of run r's blocks.
+    Returns (T [batch, H, nc, P, N], lam [batch, H, nc], rdec [batch, H, nruns])."""
+    batch, H, nc, P, N = S.shape
+    nruns = (nc + K - 1) // K
+    T = np.empty_like(S, dtype=np.float64)
+    lam = np.zeros((batch, H, nc))
+    rdec = np.zeros((batch, H, nruns))
+    for r in range(nruns):
+        h = np.zeros((batch, H, P, N))
+        ls = np.zeros((batch, H))
+        for c in range(r * K, min(r * K + K, nc)):
+            lam[:, :, c] = ls
+            h = np.exp(Acs[:, :, c, -1])[:, :, None, None] * h + S[:, :, c]
+            T[:, :, c] = h
+            ls = ls + Acs[:, :, c, -1]
+        rdec[:, :, r] = ls
+    return T, lam, rdec
+
+
+def run_passing(T, rdec, K, init=None):
+    """Second level: the chain over runs, Hr[0] = init (or 0),
+    Hr[r + 1] = exp(rdec[r]) Hr[r] + T[last block of run r]; returns
+    (Hr [batch, H, nruns, P, N], final state)."""
+    batch, H, nc, P, N = T.shape
+    nruns = rdec.shape[2]
+    h = np.zeros((batch, H, P, N)) if init is None else _f64(init).copy()
+    Hr = np.empty((batch, H, nruns, P, N))
+    for r in range(nruns):
+        Hr[:, :, r] = h
+        last = min(r * K + K, nc) - 1
+        h = np.exp(rdec[:, :, r])[:, :, None, None] * h + T[:, :, last]
+    return Hr, h
+
+
+def runs_entering_states(T, Hr, lam, K):
+    """The state entering each block from the two levels: Hr[r] at a run's
+    first block, T[c - 1] + exp(lam[c]) Hr[r] past it."""
+    batch, H, nc, P, N = T.shape
+    Hin = np.empty((batch, H, nc, P, N))
+    for c in range(nc):
+        r = c // K
+        if c % K == 0:
+            Hin[:, :, c] = Hr[:, :, r]
+        else:
+            Hin[:, :, c] = T[:, :, c - 1] + np.exp(lam[:, :, c])[:, :, None, None] * Hr[:, :, r]
+    return Hin
+
+
 def chunk_scan(x, dt, B, C, Acs, Hin, D, Q):
     """y [batch, L, H, P]: masked quadratic form inside each block plus the
     carried-state term and the D skip term."""

@@ -387,3 +387,75 @@ def test_state_passing_segmented_deterministic():
     r2 = ssd.state_passing_seg(S, cs, 1000, 64, torch.bfloat16, 5, init_state=g["init"])
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
 
+
+
+RUN_CASES = [
+    # (name, batch, L, H, G, run length K)
+    ("runs_k3_ragged_groups", 2, 256 * 9 - 37, 4, 2, 3),
+    ("runs_k4_exact", 1, 256 * 8, 2, 1, 4),
+    ("runs_k1", 1, 256 * 3 - 5, 2, 1, 1),
+    ("runs_k16_one_run", 2, 256 * 5, 4, 1, 16),
+]
+
+
+@pytest.mark.parametrize("case", RUN_CASES, ids=[c[0] for c in RUN_CASES])
+def test_two_level_stages(case):
+    """The two-level recurrence between chunks, stage by stage against the
+    fp64 definitions, each stage fed the GPU's own upstream outputs: chunk
+    states over runs of K chunks (T, lam, rdec, and the cumsum rows bit for
+    bit those of the forward's per-chunk first launch), the chain over runs
+    (Hr, final), and the chunk scan forming each chunk's entering state from
+    T and Hr (with and without the skip term)."""
+    import mamba_ssd_scan_02_amd as ssd
+    from oracle import stages
+
+    name, batch, L, H, G, K = case
+    P, N, Q = 64, 128, 256
+    say(f"[stages] {name}")
+    inp = _inputs(23, batch, L, H, P, N, G, "bf16")
+    g = to_gpu(inp)
+    tol = TOL["bf16"]
+    LN2 = math.log(2.0)
+
+    cs, dtc, T, lam, rdec = ssd.chunk_state_runs(g["x"], g["B"], g["dt"], g["A"], Q, K)
+    cs1, dtc1, S1 = ssd.chunk_cumsum_state(g["x"], g["B"], g["dt"], g["A"], Q)
+    assert torch.equal(cs, cs1) and torch.equal(dtc, dtc1), "cumsum rows of the run walk"
+    Acs = stages.chunk_cumsum(inp["dt"], inp["A"], Q)
+    S_ref = stages.chunk_state(inp["x"], inp["dt"], inp["B"], Acs, Q)
+    S_mag = stages.chunk_state(inp["x"].abs(), inp["dt"], inp["B"].abs(), Acs, Q)
+    T_ref, lam_ref, rdec_ref = stages.run_states(S_ref, Acs, K)
+    T_mag, _, _ = stages.run_states(S_mag, Acs, K)
+    gate(T, T_ref, tol, "chunk_state_runs T", T_mag)
+    scale = max(1.0, float(np.abs(rdec_ref).max()))
+    err_lam = np.max(np.abs(lam.cpu().double().numpy() * LN2 - lam_ref)) / scale
+    err_rdec = np.max(np.abs(rdec.cpu().double().numpy() * LN2 - rdec_ref)) / scale
+    say(f"  lam {err_lam:.2e}  rdec {err_rdec:.2e}")
+    assert err_lam < 2e-6 and err_rdec < 2e-6, (err_lam, err_rdec)
+
+    # the chain over runs, from the GPU's T and rdec
+    Hr, fin = ssd.run_passing(T, rdec, L, Q, K, g["init"])
+    T_gpu = T.cpu().double().numpy()
+    rdec_gpu = rdec.cpu().double().numpy() * LN2
+    Hr_ref, fin_ref = stages.run_passing(T_gpu, rdec_gpu, K, inp["init"])
+    Hr_mag, fin_mag = stages.run_passing(np.abs(T_gpu), rdec_gpu, K, inp["init"].abs())
+    gate(Hr, Hr_ref, 8e-3, "run_passing Hr", Hr_mag)
+    gate(fin, fin_ref, 1e-5, "run_passing final", fin_mag)
+
+    # the final state against the per-chunk chain on the fp64 S
+    _, fin_chain = stages.state_passing(S_ref, Acs, inp["init"])
+    _, fin_chain_mag = stages.state_passing(S_mag, Acs, inp["init"].abs())
+    gate(fin, fin_chain, tol, "run_passing final vs the per-chunk chain", fin_chain_mag)
+
+    # chunk scan from the GPU's T, Hr and lam: each entering state is formed
+    # (and rounded once to bf16) in the kernel
+    Hin = stages.runs_entering_states(T_gpu, Hr.cpu().double().numpy(),
+                                      lam.cpu().double().numpy() * LN2, K)
+    Hin_mag = stages.runs_entering_states(np.abs(T_gpu), np.abs(Hr.cpu().double().numpy()),
+                                          lam.cpu().double().numpy() * LN2, K)
+    for D_gpu, D_ref, what in ((g["D"], inp["D"], "chunk_scan_runs y"),
+                               (None, None, "chunk_scan_runs y (D=None)")):
+        y = ssd.chunk_scan_runs(g["x"], g["B"], g["C"], cs, dtc, T, Hr, lam, D_gpu, Q, K)
+        y_ref = stages.chunk_scan(inp["x"], inp["dt"], inp["B"], inp["C"], Acs, Hin, D_ref, Q)
+        y_mag = stages.chunk_scan(inp["x"].abs(), inp["dt"], inp["B"].abs(), inp["C"].abs(), Acs,
+                                  Hin_mag, None if D_ref is None else D_ref.abs(), Q)
+        gate(y, y_ref, tol, what, y_mag)

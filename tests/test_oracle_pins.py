@@ -531,3 +531,28 @@ def test_zoh_step_equals_forward(oracle_mod):
     y_ref = y_full.reshape(2, 4, 12, 3).transpose(0, 2, 1, 3)
     np.testing.assert_allclose(y_steps, y_ref, rtol=0, atol=1e-12)
     np.testing.assert_allclose(state, fin_full.reshape(2, 4, 3, 5), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 40])
+def test_two_level_recurrence_equals_the_chain(K):
+    """The two-level form (runs of K blocks scanned from zero, a chain over
+    the runs, entering states recombined) gives the same entering states and
+    final state as the plain chain between blocks, for run lengths that
+    divide the block count, leave a short last run, and exceed it."""
+    from oracle import stages
+    rng = np.random.default_rng(7)
+    batch, H, nc, P, N = 2, 3, 11, 4, 5
+    S = rng.standard_normal((batch, H, nc, P, N))
+    Acs = -np.abs(rng.standard_normal((batch, H, nc, 6))).cumsum(axis=3) * 0.3
+    init = rng.standard_normal((batch, H, P, N))
+    Hin, fin = stages.state_passing(S, Acs, init)
+    T, lam, rdec = stages.run_states(S, Acs, K)
+    Hr, fin2 = stages.run_passing(T, rdec, K, init)
+    Hin2 = stages.runs_entering_states(T, Hr, lam, K)
+    assert np.allclose(Hin2, Hin, rtol=1e-12, atol=1e-12)
+    assert np.allclose(fin2, fin, rtol=1e-12, atol=1e-12)
+    # a run of one block is the plain chain: T is S and Hr is Hin
+    if K == 1:
+        assert np.allclose(T, S) and np.allclose(Hr, Hin)
+    # the run decays sum the blocks' decays
+    assert np.allclose(rdec.sum(axis=2), Acs[:, :, :, -1].sum(axis=2))
