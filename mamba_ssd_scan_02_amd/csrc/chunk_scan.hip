@@ -393,16 +393,18 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
             const __amdgpu_buffer_rsrc_t rx = make_rs(x + (((int64_t)b * L + tok0) * H + h) * P, xrecord);
             dma16_rs(rx, xo0 + (uint32_t)m * xstep, s + kX + (wave + 8 * m) * 1024);
         } else if (m < 6) {
-            if (comb && m == 4) {
+            const __amdgpu_buffer_rsrc_t rh = make_rs(state_tile(h), P * N * 2);
+            dma16_rs(rh, ho[m - 4], s + kH + (wave + 8 * (m - 4)) * 1024);
+        } else {
+            // with the head's first copy: its Hr pieces and lam, which the
+            // combine at the head's top waits for
+            if (comb) {
                 const int64_t bh = (int64_t)b * H + h;
                 const char* hr = reinterpret_cast<const char*>(rs.Hr + (bh * rs.nruns + run) * (int64_t)(P * N));
                 hrp[0] = *reinterpret_cast<const uint4*>(hr + ho[0]);
                 hrp[1] = *reinterpret_cast<const uint4*>(hr + ho[1]);
                 lamp = rs.lam[bh * nc + c];
             }
-            const __amdgpu_buffer_rsrc_t rh = make_rs(state_tile(h), P * N * 2);
-            dma16_rs(rh, ho[m - 4], s + kH + (wave + 8 * (m - 4)) * 1024);
-        } else {
             const int64_t row = (((int64_t)b * H + h) * nc + c) * Q;
             const int part = wave & 3;
             dma4_rs(make_rs((wave < 4 ? cs : dtc) + row, Q * 4), 4u * (uint32_t)(64 * part + lane),

@@ -263,10 +263,10 @@ __device__ __forceinline__ void issue_bxh_stage(int wave, int lane, int tokbase,
 // LDS of the paired-head body below.  Once the last stage has been read,
 // the ring holds the heads' S tiles on their way out (stage_store_states):
 // head 0 in bsr, the others in xsr.
-template <int Q, int HG>
+template <int Q, int HG, int RING = kStateRing>
 struct StateSmem {
-    uint4 bsr[kStateRing][512];
-    uint4 xsr[kStateRing][32 * 128 * HG / 16];
+    uint4 bsr[RING][512];
+    uint4 xsr[RING][32 * 128 * HG / 16];
     float wv[HG][Q];
     double wsum[HG][4];
     float cslast[HG];
@@ -325,26 +325,31 @@ __device__ __forceinline__ void stage_store_states(const f32x16 (&acc)[HG][2], S
 // scan, then the wave totals), rounded once to fp32, and dt (or its
 // zero-order-hold weight) as dtc.  Both rows are written out at the end for
 // the later stages.
-template <int Q, int HG, bool FUSE>
-__device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, int c, int h0,
+template <int Q, int HG, bool FUSE, bool CARRY = false, int RING = kStateRing>
+__device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG, RING>& sm, int b, int c, int h0,
                                                  const bf16_t* __restrict__ x,
                                                  const bf16_t* __restrict__ Bm, const float* cs,
                                                  const float* dtc, int L, int H, int G, int nc,
                                                  const float* __restrict__ dtin,
                                                  const float* __restrict__ A, float* csw,
                                                  float* dtcw, int zoh, bool keepx, f32x16 (&acc)[HG][2],
-                                                 float (&cl)[HG], bool carry = false) {
+                                                 float (&cl)[HG]) {
     constexpr int W = 4, NT = Q / 32;
     constexpr int XR = 128 * HG;                         // bytes of a token's x row
     constexpr int DPS = 8 / W + BxhOffsets<W, HG>::XC;   // copies per wave per stage
-    constexpr int R = kStateRing;
+    constexpr int R = RING;
     static_assert(state_ring_waits_hold(NT, R, DPS), "chunk_state wait counts do not cover its copies");
     auto& bsr = sm.bsr;
     auto& xsr = sm.xsr;
     auto& wv = sm.wv;
 
     const int g = h0 / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63;
+    int tid = threadIdx.x;
+    // inside a run's loop over chunks: the thread index is opaque to the
+    // compiler, so the body's many lane addresses are formed per chunk
+    // instead of hoisted out of the loop and held in registers across it
+    if constexpr (CARRY) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5;
     const int64_t row0 = (((int64_t)b * H + h0) * nc + c) * Q;   // head h0 + e: + e * nc * Q
@@ -422,12 +427,12 @@ __device__ __forceinline__ void chunk_state_pair(StateSmem<Q, HG>& sm, int b, in
     const int trow0 = 8 * (grp >> 1) + (rr >> 2);
     const int qcol = 16 * (grp & 1) + 4 * (rr & 3);
 
-    // from zero, or (carry: acc holds the state entering the chunk) from that
+    // from zero, or (CARRY: acc holds the state entering the chunk) from that
     // state decayed through the chunk, exp2(cs_last) H, so that the products
     // below leave the state after the chunk
 #pragma unroll
     for (int e = 0; e < HG; ++e) {
-        if (carry) {
+        if constexpr (CARRY) {
             const float a = fast_exp2(cl[e]);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -551,8 +556,12 @@ __global__ __launch_bounds__(256, 2) void chunk_state_mfmah_kernel(const bf16_t*
 // chain over runs (state_passing.hip), and chunk_scan forms Hin_c from T_{c-1}
 // and Hr_r itself, so neither the per-chunk S nor the per-chunk Hin reaches
 // memory.
+// Three workgroups per CU, as the one-chunk kernel: the lane addresses of
+// the chunk body and of the T store are formed inside the loop over chunks
+// (opaque thread index), so only the carried state and a few scalars live
+// across it (151 VGPRs, no spills).
 template <int Q, int HG>
-__global__ __launch_bounds__(256, 2) void chunk_state_runs_kernel(
+__global__ __launch_bounds__(256, 3) void chunk_state_runs_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, bf16_t* __restrict__ T,
     float* __restrict__ lam, float* __restrict__ rdec, int L, int H, int G, int nc, int K, int nruns,
     const float* __restrict__ dtin, const float* __restrict__ A, float* csw, float* dtcw, int zoh,
@@ -578,19 +587,32 @@ __global__ __launch_bounds__(256, 2) void chunk_state_runs_kernel(
     float cl[HG], lsum[HG];
 #pragma unroll
     for (int e = 0; e < HG; ++e) lsum[e] = 0.0f;
+    // the run starts from zero; every chunk decays the carried state (a zero
+    // state stays exactly zero: the decay factors lie in [0, 1]) and adds its
+    // products
+#pragma unroll
+    for (int e = 0; e < HG; ++e) acc[e][0] = acc[e][1] = f32x16{};
     for (int c = c0; c < c1; ++c) {
-        chunk_state_pair<Q, HG, true>(sm, b, c, h0, x, Bm, nullptr, nullptr, L, H, G, nc, dtin, A, csw,
-                                      dtcw, zoh, keepx, acc, cl, c > c0);
+        chunk_state_pair<Q, HG, true, true>(sm, b, c, h0, x, Bm, nullptr, nullptr, L, H, G, nc, dtin, A, csw,
+                                            dtcw, zoh, keepx, acc, cl);
         bf16_t* dst[HG];
 #pragma unroll
         for (int e = 0; e < HG; ++e) {
             const int64_t bhc = ((int64_t)b * H + h0 + e) * nc + c;
             dst[e] = T + bhc * (int64_t)(P * N);
             if (tid == 0) lam[bhc] = lsum[e];
-            lsum[e] += cl[e];
+            // wave-uniform: kept in scalar registers across the run
+            lsum[e] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                    __builtin_bit_cast(int, lsum[e] + cl[e])));
         }
         barrier_lds();   // every wave is past its last read of the ring
-        stage_store_states<HG>(acc, st, dst, wave, lane);
+        {
+            // the store's lane addresses formed per chunk (an opaque index,
+            // as in chunk_state_pair), not held across the loop
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            stage_store_states<HG>(acc, st, dst, __builtin_amdgcn_readfirstlane(t >> 6), t & 63);
+        }
         barrier_lds();   // every wave has read its staged rows back before the ring refills
     }
     if (tid == 0) {
