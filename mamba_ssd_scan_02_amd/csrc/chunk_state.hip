@@ -947,13 +947,14 @@ bool state_runs_apply(int32_t dtype, const Dims& d) {
 // Run length for ssd_forward, or 0 to keep the per-chunk path.  Longer runs
 // shorten the chain over runs and keep more states out of memory, but leave
 // fewer workgroups for the run walks, whose chunks are sequential: take the
-// longest K in {16, 8, 4, 2} whose grid still fills two rounds of the
-// machine (two workgroups per CU).  Measured (chunk-state runs + run chain +
-// chunk scan, one box): 2.7B shape K = 2/4/8/16: 346/341/359/371 us against
-// 361 us for the per-chunk path (K = 4 taken); 1M-token sequence 5,728 /
-// 5,588 / 5,505 / 5,447 us against 5,948 (K = 16); the 130M shape has 96
-// head-pair sequences of 8 chunks, too few workgroups at any K (73 us at K = 2
-// against 63), and keeps the per-chunk path.
+// longest K in {16, 8, 4, 2} whose grid still gives every CU four workgroups
+// (three run at a time on a CU).  Measured (chunk-state runs + run chain
+// + chunk scan in the forward's order, one box): 2.7B shape K = 4 / 8: 337.8 /
+// 336.3 us against 365.0 us for the per-chunk path (K = 4 taken); 1M-token
+// sequence K = 8 / 16 / 32 / 64: 5,644 / 5,581 / 5,617 / 5,641 us against
+// 6,097 (K = 16); the 130M shape has 96 head-pair sequences of 8 chunks, too
+// few workgroups at any K (K = 2 / 4 / 8: 71.6 / 77.7 / 103.4 us against
+// 66.8), and keeps the per-chunk path.
 int state_run_chunks(const Dims& d) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
