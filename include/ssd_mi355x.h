@@ -111,7 +111,10 @@ const char* ssd_status_str(int32_t status);
  * two-level recurrence between chunks applies (see ssd_chunk_state_runs) the
  * forward carves the same workspace as cs, dtc, T [B][H][nc][P][N],
  * Hr [B][H][nruns][P][N], lam [B][H][nc], rdec [B][H][nruns] instead, and the
- * size returned is the larger of the two layouts.
+ * size returned is the larger of the two layouts.  The run length (and so
+ * the size) is chosen for the device current at the call: a workspace sized
+ * on a device with fewer CUs than the one the forward runs on can be too
+ * small there (SSD_ERR_WORKSPACE, nothing launched).
  */
 size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
                                    int64_t headdim, int64_t dstate, int64_t ngroups,
