@@ -116,3 +116,54 @@ def test_decode_graph_replays_match_eager():
         say(f"[graph] decode replay {rep}")
         assert torch.equal(state, ref_state), rep
         assert all(torch.equal(a, b) for a, b in zip(ys, ref_ys)), rep
+
+
+def test_two_level_forward_graph_replays_match_eager():
+    """The forward where it runs the two-level form (chunk states over runs,
+    the chain over runs, the chunk scan forming the entering states; 32
+    heads, 128 chunks of 256 tokens: K = 2) captured with a caller-held
+    workspace and replayed with new inputs and eager work in between, bit for
+    bit against the same call made eagerly.  Inputs are drawn on the device
+    (only replay-against-eager equality is checked here; parity with the
+    oracle at these kernels is the forward and stage tests' job)."""
+    import mamba_ssd_scan_02_amd as ssd
+    batch, L, H, P, N, G, Q = 1, 32768, 32, 64, 128, 1, 256
+    K = ssd.forward_run_chunks(batch, L, H, P, N, G, Q, torch.bfloat16)
+    assert K > 0, "this shape should run the two-level form"
+    say(f"[graph] two-level forward, K = {K}")
+
+    def fresh(seed):
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        rn = lambda *s: torch.randn(*s, generator=gen, device="cuda")
+        return dict(
+            x=rn(batch, L, H, P).to(torch.bfloat16),
+            dt=torch.nn.functional.softplus(rn(batch, L, H) - 2.0),
+            A=-torch.exp(torch.rand(H, generator=gen, device="cuda") * 1.5),
+            B=(rn(batch, L, G, N) / N ** 0.5).to(torch.bfloat16),
+            C=(rn(batch, L, G, N) / N ** 0.5).to(torch.bfloat16),
+            D=rn(H),
+            init=rn(batch, H, P, N) * 0.3,
+        )
+
+    g = fresh(7)
+    y = torch.empty_like(g["x"])
+    fin = torch.empty((batch, H, P, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ssd.workspace_bytes(batch, L, H, P, N, G, Q, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        ssd.ssd_forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], Q, g["init"], y=y,
+                        final_state=fin, workspace=ws)
+
+    graph = _capture(run)
+    for rep, seed in enumerate((7, 8, 8, 9)):
+        new = fresh(seed)
+        _refill(g, new)
+        y_e, f_e = ssd.ssd_forward(new["x"], new["dt"], new["A"], new["B"], new["C"], new["D"], Q,
+                                   new["init"])
+        y.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep} (inputs seed {seed})")
+        assert torch.equal(y, y_e) and torch.equal(fin, f_e), rep
