@@ -299,3 +299,46 @@ def test_plain_c_caller(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "abi_smoke: ok" in out.stdout
+
+
+def test_two_level_stage_argument_errors(lib):
+    """The two-level stage calls accept only the shapes the forward runs them
+    at (bf16, P = 64, N = 128, chunk 256, an even head count per group) and
+    run lengths 1 .. 65536; every error returns before any launch."""
+    import mamba_ssd_scan_02_amd as ssd
+    import torch
+    P = ctypes.c_void_p
+    M = 1 << 24
+    a = [P((k + 1) * M) for k in range(12)]
+    ok = (1, 512, 4, 64, 128, 1, 256, 1)
+
+    def sr(dims=ok, K=2, ptrs=None):
+        q = ptrs or a[:9]
+        return lib.ssd_chunk_state_runs(*dims, K, *q, None)
+
+    assert sr(dims=(1, 512, 4, 64, 128, 1, 256, 0)) == UNSUP        # fp32
+    assert sr(dims=(1, 512, 4, 64, 128, 1, 128, 1)) == UNSUP        # chunk 128
+    assert sr(dims=(1, 512, 3, 64, 128, 1, 256, 1)) == UNSUP        # odd heads per group
+    assert sr(dims=(1, 512, 4, 32, 128, 1, 256, 1)) == UNSUP        # P = 32
+    assert sr(K=0) == SHAPE and sr(K=65537) == SHAPE
+    assert sr(ptrs=[a[0], None] + a[2:9]) == NULL
+    assert sr(ptrs=a[:6] + [P(a[6].value + 8)] + a[7:9]) == ALIGN   # T 8-byte aligned
+    rp = lambda K=2, T=a[0], Hr=a[3], fin=None: lib.ssd_run_passing(1, 512, 4, 64, 128, 256, 1, K, T,
+                                                                    a[1], None, Hr, fin, None)
+    assert rp(K=0) == SHAPE
+    assert rp(T=None) == NULL
+    assert rp(Hr=a[0]) == ALIAS                                     # Hr on T
+    cs = lambda K=2, y=a[10], T=a[5]: lib.ssd_chunk_scan_runs(*ok, K, a[0], a[1], a[2], a[3], a[4],
+                                                              T, a[6], a[7], None, y, None)
+    assert cs(K=0) == SHAPE
+    assert cs(T=None) == NULL
+    assert cs(y=a[6]) == ALIAS                                      # y on Hr
+    # the run length the forward uses: 0 where it keeps the per-chunk stages
+    assert ssd.forward_run_chunks(1, 512, 4, 64, 128, 1, 256, torch.bfloat16) == 0
+    assert ssd.forward_run_chunks(4, 8192, 80, 64, 128, 1, 256, torch.float32) == 0
+    assert ssd.forward_run_chunks(4, 8192, 80, 64, 128, 1, 128, torch.bfloat16) == 0
+    K = ssd.forward_run_chunks(4, 8192, 80, 64, 128, 1, 256, torch.bfloat16)
+    assert K in (2, 4, 8, 16)
+    # the workspace covers both layouts
+    n = lib.ssd_forward_workspace_bytes(1, 1, 2, 64, 128, 1, 256, 1)
+    assert n >= 2 * 256 * 4 * 2 + 2 * 64 * 128 * 2
