@@ -124,6 +124,21 @@ static void library_checks(void) {
     CHECK(ssd_chunk_scan(b, L, H, P, N, G, Q, f32, x, B, C, dt, A, NULL, D, y, NULL) == SSD_ERR_NULL);
     CHECK(ssd_chunk_scan(b, L, 3, P, N, 2, Q, f32, x, B, C, dt, A, ws, D, y, NULL) == SSD_ERR_SHAPE);
 
+    /* the two-level stage calls and the forward's run length (no launch: every
+       call below fails a check first) */
+    const int32_t bf = SSD_DTYPE_BF16;
+    CHECK(ssd_forward_run_chunks(b, L, H, P, N, G, Q, f32) == 0);
+    CHECK(ssd_forward_run_chunks(INT64_MAX, INT64_MAX, INT64_MAX, 64, 128, 1, 256, bf) == 0);
+    CHECK(ssd_forward_run_chunks(-1, -1, -1, -1, -1, -1, -1, bf) == 0);
+    CHECK(ssd_chunk_state_runs(b, L, H, P, N, G, Q, f32, 2, x, B, dt, A, (float*)ws, (float*)y, C, (float*)D, (float*)init, NULL) == SSD_ERR_UNSUPPORTED);
+    CHECK(ssd_chunk_state_runs(1, 512, 2, 64, 128, 1, 256, bf, 0, x, B, dt, A, (float*)ws, (float*)y, C, (float*)D, (float*)init, NULL) == SSD_ERR_SHAPE);
+    CHECK(ssd_chunk_state_runs(1, 512, 2, 64, 128, 1, 256, bf, INT64_MAX, x, B, dt, A, (float*)ws, (float*)y, C, (float*)D, (float*)init, NULL) == SSD_ERR_SHAPE);
+    CHECK(ssd_chunk_state_runs(1, 512, 2, 64, 128, 1, 256, bf, 2, x, NULL, dt, A, (float*)ws, (float*)y, C, (float*)D, (float*)init, NULL) == SSD_ERR_NULL);
+    CHECK(ssd_run_passing(1, 512, 2, 64, 128, 256, bf, 2, NULL, dt, init, y, fin, NULL) == SSD_ERR_NULL);
+    CHECK(ssd_run_passing(1, 512, 2, 64, 128, 256, bf, -5, ws, dt, init, y, fin, NULL) == SSD_ERR_SHAPE);
+    CHECK(ssd_chunk_scan_runs(1, 512, 2, 64, 128, 1, 256, bf, 2, x, B, C, dt, A, ws, y, (float*)D, NULL, NULL, NULL) == SSD_ERR_NULL);
+    CHECK(ssd_chunk_scan_runs(1, 512, 2, 64, 128, 1, 256, f32, 2, x, B, C, dt, A, ws, y, (float*)D, NULL, fin, NULL) == SSD_ERR_UNSUPPORTED);
+
     /* the block around the scan */
     CHECK(ssd_layer_in(0, L, H, P, N, G, 4, f32, x, dt, NULL, A, NULL, y, B, C, fin, NULL) == SSD_ERR_SHAPE);
     CHECK(ssd_layer_in(b, L, H, P, N, G, 4, f32, NULL, dt, NULL, A, NULL, y, B, C, fin, NULL) == SSD_ERR_NULL);
