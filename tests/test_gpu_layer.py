@@ -226,6 +226,8 @@ GATED_CASES = [
     ("short_q128", 1, 520, 2, 64, 128, 1, 128, "bf16"),
     ("short_q64", 1, 333, 2, 64, 128, 2, 64, "bf16"),
     ("generic_f32", 1, 300, 3, 16, 16, 1, 64, "f32"),
+    # the two-level form (runs of K = 2 chunks; the gate in the same store)
+    ("runs_two_level", 1, 32768, 32, 64, 128, 1, 256, "bf16"),
 ]
 
 
@@ -240,6 +242,8 @@ def test_forward_gated_matches_forward_then_gate(case):
 
     name, batch, L, H, P, N, G, Q, dtype = case
     say(f"[gated] {name}")
+    if name.startswith("runs"):
+        assert ssd.forward_run_chunks(batch, L, H, P, N, G, Q, torch.bfloat16) > 0
     inp = make_forward_inputs(_spec(batch, L, H, P, N, G, dtype, chunk=Q, init_var=0.1, seed=61))
     g = to_gpu(inp)
     x = g["x"]
