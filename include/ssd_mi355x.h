@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 7
+#define SSD_ABI_VERSION 8
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 

@@ -21,7 +21,7 @@ DTYPE_BF16 = 1
 
 # The SSD_ABI_VERSION this binding was written against; load() refuses a
 # library that reports another one (a stale build).
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _STATUS_OK = 0
 

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 7
+    assert lib.ssd_abi_version() == 8
     for s in range(8):
         assert lib.ssd_status_str(s)
     assert lib.ssd_status_str(99) == b"unknown status"
