@@ -575,8 +575,7 @@ __global__ __launch_bounds__(256, 3) void chunk_state_runs_kernel(
     const int r = br % nruns, b = br / nruns;
     const int c0 = r * K, c1 = min(c0 + K, nc);
     const bool keepx = (h0 % (H / G)) % keep_run < keep_k;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x;
     static_assert(sizeof(sm.bsr) >= P * N * 2 && sizeof(sm.xsr) >= (HG - 1) * P * N * 2,
                   "the ring holds the T tiles");
     SSD_LDS char* st[HG];
