@@ -330,8 +330,10 @@ struct RunState {
 
 // One wave of the paired kernel; ROLE 0 = lead, 1 = helper.  RUNS: the
 // carried state is formed from the two-level recurrence's T (passed as Hin)
-// and Hr (RunState) instead of read whole.
-template <int ROLE, bool RUNS>
+// and Hr (RunState) instead of read whole.  GATED: z is given and the store
+// writes y silu(z) (a template parameter, so that neither form carries the
+// other's branches through its loop over heads).
+template <int ROLE, bool RUNS, bool GATED>
 __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm,
                                            const bf16_t* __restrict__ Cm, const float* __restrict__ cs,
                                            const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
@@ -482,7 +484,7 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
         // that the staging below covers their latency
         const int tr = lane >> 3, tc = lane & 7;
         u32x4v zr[4];
-        if (z) {
+        if constexpr (GATED) {
             const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<bf16_t*>(z) + (((int64_t)b * L + tok0) * H + h0 + k) * P, (short)0, xrecord, 0x00020000);
 #pragma unroll
@@ -524,7 +526,7 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
         for (int m = 0; m < 4; ++m) {
             const int r = 8 * m + tr;
             u32x4v v = *reinterpret_cast<const SSD_LDS u32x4v*>(sb + (wave + 8 * m) * 1024 + stage_off(r, tc));
-            if (z) {
+            if constexpr (GATED) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y0 = bf16_bits_to_f32(v[e] & 0xffffu), y1 = bf16_bits_to_f32(v[e] >> 16);
@@ -674,7 +676,7 @@ __device__ __forceinline__ void paired_run(const bf16_t* __restrict__ x, const b
     wait_vmcnt<0>();
 }
 
-template <bool RUNS>
+template <bool RUNS, bool GATED>
 __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ cs, const float* __restrict__ dtc, const bf16_t* __restrict__ Hin,
@@ -695,9 +697,11 @@ __global__ __launch_bounds__(512, 1) void chunk_scan_paired_kernel(
     __builtin_assume(wave >= 0 && wave < 8);
     SSD_LDS char* const sm = (SSD_LDS char*)lds(smem);
     if (wave < 4)
-        paired_run<0, RUNS>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm, rs);
+        paired_run<0, RUNS, GATED>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane,
+                                   sm, rs);
     else
-        paired_run<1, RUNS>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane, sm, rs);
+        paired_run<1, RUNS, GATED>(x, Bm, Cm, cs, dtc, Hin, D, z, y, L, H, G, nc, b, c, g, h0, cnt, wave, lane,
+                                   sm, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1109,9 +1113,13 @@ hipError_t launch_chunk_scan(const Dims& d, int32_t dtype, const void* x, const 
         chunk_scan_runs(d, &hg, &nsplit);
         const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
         if (d.chunk == 256) {
-            chunk_scan_paired_kernel<false><<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, hb, D,
-                                                                        static_cast<const bf16_t*>(z), yb, L,
-                                                                        H, G, nc, hg, nsplit, RunState{});
+            const bf16_t* zb = static_cast<const bf16_t*>(z);
+            if (zb)
+                chunk_scan_paired_kernel<false, true><<<blocks, 512, 0, stream>>>(
+                    xb, bb, cb, cs, dtc, hb, D, zb, yb, L, H, G, nc, hg, nsplit, RunState{});
+            else
+                chunk_scan_paired_kernel<false, false><<<blocks, 512, 0, stream>>>(
+                    xb, bb, cb, cs, dtc, hb, D, nullptr, yb, L, H, G, nc, hg, nsplit, RunState{});
             return hipGetLastError();   // the gate, if any, is inside
         }
         if (d.chunk == 64) {
@@ -1144,10 +1152,18 @@ hipError_t launch_chunk_scan_runs(const Dims& d, int K, const void* x, const voi
     chunk_scan_runs(d, &hg, &nsplit);
     const unsigned blocks = (unsigned)(d.batch * nc * G * nsplit);
     const RunState rs{static_cast<const bf16_t*>(Hr), lam, K, (nc + K - 1) / K};
-    chunk_scan_paired_kernel<true><<<blocks, 512, 0, stream>>>(
-        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), cs, dtc,
-        static_cast<const bf16_t*>(T), D, static_cast<const bf16_t*>(z), static_cast<bf16_t*>(y), L, H, G, nc,
-        hg, nsplit, rs);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* bb = static_cast<const bf16_t*>(B);
+    const bf16_t* cb = static_cast<const bf16_t*>(C);
+    const bf16_t* tb = static_cast<const bf16_t*>(T);
+    const bf16_t* zb = static_cast<const bf16_t*>(z);
+    bf16_t* yb = static_cast<bf16_t*>(y);
+    if (zb)
+        chunk_scan_paired_kernel<true, true><<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, tb, D, zb, yb, L, H,
+                                                                         G, nc, hg, nsplit, rs);
+    else
+        chunk_scan_paired_kernel<true, false><<<blocks, 512, 0, stream>>>(xb, bb, cb, cs, dtc, tb, D, nullptr, yb,
+                                                                          L, H, G, nc, hg, nsplit, rs);
     return hipGetLastError();
 }
 
