@@ -602,6 +602,10 @@ def _short_kernel(name: str) -> str:
         return "chunk_state_runs"     # chunk states over runs (two-level path)
     if "run_passing_kernel" in name:
         return "run_passing"          # the chain over runs
+    if "chunk_scan_paired_kernel<true, true>" in name:
+        return "chunk_scan_runs_gated"   # the same with the block's gate in its store
+    if "chunk_scan_paired_kernel<false, true>" in name:
+        return "chunk_scan_gated"
     if "chunk_scan_paired_kernel<true" in name:
         return "chunk_scan_runs"      # chunk scan forming the entering states
     if "chunk_state" in name and ", true>" in name:
