@@ -57,3 +57,25 @@ def test_committed_summaries_name_their_kernels_and_commands():
         for key in ("command_fetch:", "command_write:", "calibration:", "hbm_bytes_per_dispatch:",
                     "algorithmic_bytes_per_dispatch:", "source_sha256_16:"):
             assert key in t, (p.name, key)
+
+
+def test_kernel_names_map_to_the_stage_they_run():
+    """Trace and counter summaries attribute each dispatch by its demangled
+    name; every kernel of the forward's two paths and their gated forms must
+    land under its own stage name."""
+    import bench
+    cases = {
+        "void ssd::chunk_scan_paired_kernel<true, false>(ssd::bf16_t const*, int)": "chunk_scan_runs",
+        "void ssd::chunk_scan_paired_kernel<true, true>(ssd::bf16_t const*, int)": "chunk_scan_runs_gated",
+        "void ssd::chunk_scan_paired_kernel<false, false>(ssd::bf16_t const*, int)": "chunk_scan",
+        "void ssd::chunk_scan_paired_kernel<false, true>(ssd::bf16_t const*, int)": "chunk_scan_gated",
+        "void ssd::chunk_state_runs_kernel<256, 2>(ssd::bf16_t const*)": "chunk_state_runs",
+        "void ssd::run_passing_kernel<ssd::bf16_t, 4, 4>(ssd::bf16_t const*)": "run_passing",
+        "void ssd::chunk_state_mfmah_kernel<256, 2, true>(ssd::bf16_t const*)": "chunk_state_cumsum",
+        "void ssd::chunk_state_mfmah_kernel<256, 2, false>(ssd::bf16_t const*)": "chunk_state",
+        "void ssd::state_passing_kernel<ssd::bf16_t, 4, 4, true>(ssd::bf16_t const*)": "state_passing",
+        "void ssd::state_walk_kernel<8>(ssd::bf16_t const*)": "state_scan",
+        "__amd_rocclr_copyBuffer": "copy",
+    }
+    for name, want in cases.items():
+        assert bench._short_kernel(name) == want, (name, bench._short_kernel(name))
