@@ -237,6 +237,28 @@ def test_final_state_may_alias_init():
     assert torch.equal(y_a, y_b) and torch.equal(f_a, st)
 
 
+def test_final_state_may_alias_init_two_level():
+    """The same on the two-level path (32 heads, 128 chunks: runs of two
+    chunks), where only the chain over runs reads the initial state and
+    writes the final one; inputs drawn on the device."""
+    import mamba_ssd_scan_02_amd as ssd
+    batch, L, H, P, N, G, Q = 1, 32768, 32, 64, 128, 1, 256
+    assert ssd.forward_run_chunks(batch, L, H, P, N, G, Q, torch.bfloat16) > 0
+    gen = torch.Generator(device="cuda").manual_seed(86)
+    rn = lambda *sh: torch.randn(*sh, generator=gen, device="cuda")
+    x = rn(batch, L, H, P).to(torch.bfloat16)
+    dt = torch.nn.functional.softplus(rn(batch, L, H) - 2.0)
+    A = -torch.exp(torch.rand(H, generator=gen, device="cuda") * 1.5)
+    Bm = (rn(batch, L, G, N) / N ** 0.5).to(torch.bfloat16)
+    Cm = (rn(batch, L, G, N) / N ** 0.5).to(torch.bfloat16)
+    D = rn(H)
+    init = rn(batch, H, P, N) * 0.3
+    y_a, f_a = ssd.ssd_forward(x, dt, A, Bm, Cm, D, Q, init)
+    st = init.clone()
+    y_b, f_b = ssd.ssd_forward(x, dt, A, Bm, Cm, D, Q, st, final_state=st)
+    assert torch.equal(y_a, y_b) and torch.equal(f_a, st)
+
+
 def test_bitwise_deterministic():
     from mamba_ssd_scan_02_amd.workloads import MAMBA2_130M
     inp = _spec_inputs(MAMBA2_130M.with_(batch=2, seqlen=1024, nheads=8, init_var=0.1, seed=86))
